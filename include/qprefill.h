@@ -1,0 +1,196 @@
+/*
+ * qprefill.h -- C ABI of the MI355X (gfx950) quantized prefill library.
+ *
+ * The operation: the batched prefill of a GGUF-quantized transformer runs a
+ * chunk of T prompt tokens through each projection as one product
+ * Y[T x N] = X[T x K] . W^T, where W (N output rows of K input weights) is
+ * held in a block-quantized GGUF type and is dequantized on the way in.
+ *   - "QK-norm models take the FP16 batched prefill" (aprender PR), "What
+ *     changes": chunked batched prefill in FP16 for models with a per-head
+ *     QK norm (FP8 fails parity on them).
+ *   - "Qwen3.5 batched prefill has no f32 dequant for IQ2_XXS, IQ3_S,
+ *     IQ3_XXS, Q2_K" (aprender issue), "Cause": every projection weight is
+ *     dequantized to f32 before the GEMM and the f16 copy is built from that
+ *     f32 value; an unsupported type is an InvalidParameter error, and the
+ *     engine fails closed instead of falling back to the CPU.  "Acceptance
+ *     (each row)": the dequant is bit-exact with the CPU oracle, including a
+ *     partial last block, and writes nothing outside its output.
+ *   - "CUDA prefill VRAM loans and SM75 Q4/native-IQ opt-ins" (Strata PR),
+ *     "Summary" and "Correctness and safety": routed experts run as a fused
+ *     prefill path whose routing ids, expert selection, route weights and
+ *     scatter order are those of the unfused path.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are device memory of the current HIP device;
+ *     (host) are host memory.  The caller owns every buffer.  The library
+ *     never allocates, frees or synchronizes; the caller-supplied workspace
+ *     is the only scratch memory.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and is
+ *     asynchronous: a QP_OK return means "validated and launched".
+ *   - Arguments are validated before anything is launched.  On any error
+ *     nothing is launched and no output is written.  There is no CPU
+ *     fallback for any operation.
+ *   - Block layouts (GGUF / ggml on-disk convention, little-endian fp16):
+ *       Q8_0  34 B per 32 weights  : d f16 @0, qs int8[32] @2;  w = d*q
+ *       Q4_K 144 B per 256 weights : d f16 @0, dmin f16 @2, 12 bytes of packed
+ *                                    6-bit (scale, min) for 8 sub-blocks of 32 @4,
+ *                                    qs u8[128] (4-bit quants) @16;  w = d*sc*q - dmin*m
+ *       Q6_K 210 B per 256 weights : ql u8[128] @0, qh u8[64] @128, scales int8[16] @192,
+ *                                    d f16 @208;  w = d*sc*(q - 32), q 6 bits
+ *       Q2_K  84 B per 256 weights : scales u8[16] (4-bit scale | 4-bit min << 4) @0,
+ *                                    qs u8[64] (2-bit quants) @16, d f16 @80, dmin f16 @82;
+ *                                    w = d*sc*q - dmin*m
+ *     A weight tensor of R rows x C columns is R rows of ceil(C/QK) whole
+ *     blocks, back to back (row stride = qp_row_bytes(qtype, C)).
+ *   - Type ids are the ggml type numbers.
+ */
+#ifndef QPREFILL_H
+#define QPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QP_OK = 0,
+  QP_ERR_INVALID_PARAMETER = 1,   /* bad size, stride, alignment, pointer or option */
+  QP_ERR_UNSUPPORTED_TYPE = 2,    /* qtype is not Q8_0, Q4_K, Q6_K or Q2_K */
+  QP_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the size query */
+  QP_ERR_DEVICE = 4               /* the HIP runtime reported an error at launch */
+} qp_status;
+
+typedef enum { QP_Q8_0 = 8, QP_Q2_K = 10, QP_Q4_K = 12, QP_Q6_K = 14 } qp_qtype;
+
+typedef enum { QP_F32 = 0, QP_F16 = 1 } qp_dtype;
+
+/* Weights per block: 32 (Q8_0) or 256 (K types); -1 for an unsupported type. */
+int64_t qp_block_size(int qtype);
+
+/* Bytes per block: 34, 144, 210, 84; -1 for an unsupported type. */
+int64_t qp_type_size(int qtype);
+
+/* Bytes of one row of `cols` weights: ceil(cols / QK) * type_size.
+ * -1 for an unsupported type or cols <= 0. */
+int64_t qp_row_bytes(int qtype, int64_t cols);
+
+/*
+ * Dequantize a rows x cols tensor to f32 ("Cause": the f32 dequant of every
+ * projection weight; "Acceptance (each row)": bit-exact, partial last block).
+ *   src (device): rows * qp_row_bytes(qtype, cols) bytes, 2-byte aligned.
+ *   dst (device): rows * cols floats, dense row-major: element (r, c) at
+ *                 dst[r * cols + c]; 4-byte aligned.  Only these elements
+ *                 are written: the unused quants of a partial last block are
+ *                 ignored.
+ * Values are computed in binary32, left to right, nearest-even:
+ *   Q8_0 d*q;  Q4_K, Q2_K (d*sc)*q - dmin*m;  Q6_K (d*sc)*(q-32).
+ * rows == 0 is a no-op.  Errors: QP_ERR_UNSUPPORTED_TYPE, or
+ * QP_ERR_INVALID_PARAMETER for rows < 0, cols <= 0, a NULL or misaligned
+ * pointer.
+ */
+qp_status qp_dequant_f32(int qtype, const void* src, int64_t rows, int64_t cols, float* dst,
+                         hipStream_t stream);
+
+/*
+ * Same as qp_dequant_f32, but each value is the binary16 (nearest-even,
+ * subnormals kept, overflow to +-inf) of the f32 dequant ("Cause": the f16
+ * copy is built from the f32 dequant).  dst (device): rows * cols binary16
+ * bit patterns, 2-byte aligned.
+ */
+qp_status qp_dequant_f16(int qtype, const void* src, int64_t rows, int64_t cols, uint16_t* dst,
+                         hipStream_t stream);
+
+/*
+ * Prefill projection ("What changes": batched prefill of a chunk of prompt
+ * tokens in FP16):  y[t*ldy + n] = sum_k x[t*ldx + k] * W[n, k]
+ *   w (device): the N x K weight tensor in `qtype`, 16-byte aligned.
+ *   x (device): T x K activations, row stride ldx elements, binary16
+ *               (x_dtype QP_F16) or f32 (QP_F32, rounded to binary16 on
+ *               load); 16-byte aligned with ldx * element size a multiple
+ *               of 16 bytes.
+ *   y (device): T x N f32 outputs, row stride ldy (>= n); 16-byte aligned.
+ * W is dequantized on load (nearest-even binary16 of the exact f32 value)
+ * and never stored; products run on FP16 MFMA with f32 accumulation.
+ * Requires k % 256 == 0.  t == 0 is a no-op.
+ * Errors: QP_ERR_UNSUPPORTED_TYPE; QP_ERR_INVALID_PARAMETER for sizes or
+ * strides out of range or misaligned pointers.
+ */
+qp_status qp_prefill_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype,
+                          int64_t t, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
+
+/*
+ * Prefill projection with the per-head RMSNorm of QK-norm models fused into
+ * the epilogue ("What changes": per-head QK norm):  with Y = X . W^T as in
+ * qp_prefill_gemm, for each token t and head h (columns h*head_dim ..
+ * h*head_dim + head_dim - 1):
+ *   y[t, h*hd + j] = Y[t, h*hd + j] / sqrt(mean_j Y[t, h*hd + j]^2 + eps)
+ *                    * gain[h * gain_head_stride + j]
+ *   gain (device): f32; gain_head_stride 0 shares one head_dim vector
+ *                  across heads, head_dim gives each head its own.
+ *   x (device): binary16 activations (as qp_prefill_gemm with QP_F16).
+ * Requires head_dim in {64, 128}, n % head_dim == 0, finite eps > 0.
+ */
+qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x,
+                                 int64_t t, int64_t ldx, int64_t head_dim, const float* gain,
+                                 int64_t gain_head_stride, float eps, float* y, int64_t ldy,
+                                 hipStream_t stream);
+
+/*
+ * Router of a routed-expert layer ("Correctness and safety": routing ids,
+ * expert selection and route weights):  for each token t,
+ * p = softmax(logits[t, :]) over n_experts; the top_k experts by logit,
+ * largest first, ties to the lower expert index; weight = p of each chosen
+ * expert (renorm != 0 divides the chosen weights by their sum).
+ *   logits (device): t x n_experts f32.   ids (device): t x top_k int32.
+ *   weights (device): t x top_k f32.
+ * Requires 1 <= top_k <= n_experts <= 1024.
+ */
+qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k,
+                            int renorm, int32_t* ids, float* weights, hipStream_t stream);
+
+/* Workspace bytes qp_grouped_expert_gemm needs for these sizes (0 on a bad size). */
+size_t qp_grouped_expert_workspace_bytes(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden,
+                                         int64_t inter);
+
+/*
+ * Routed expert FFN over per-expert token lists ("Summary": fused routed-
+ * expert prefill; "Correctness and safety": same selection, weights and
+ * scatter order):  for token t and slot s with expert e = ids[t, s]:
+ *   g = x[t] . Wg_e^T, u = x[t] . Wu_e^T           (inter values each)
+ *   h = SiLU(g) * u = g / (1 + exp(-g)) * u
+ *   out[t, :] = sum over s = 0..top_k-1, in slot order, of weights[t, s] * (h . Wd_e^T)
+ *   w_gate, w_up (device): n_experts tensors of inter x hidden in `qtype`,
+ *                          back to back (expert stride inter * row_bytes(hidden)).
+ *   w_down (device): n_experts tensors of hidden x inter (stride hidden * row_bytes(inter)).
+ *   x (device): t x hidden binary16, row stride hidden.
+ *   ids, weights (device): t x top_k int32 / f32.  A pair whose id is out of
+ *                          [0, n_experts) contributes nothing.
+ *   out (device): t x hidden f32, row stride hidden.
+ *   workspace (device): >= qp_grouped_expert_workspace_bytes(...), 256-byte
+ *                       aligned; its contents on entry do not matter.
+ * Token lists are built on the device (count, scan, stable fill by pair
+ * index), so the result is deterministic.  Requires hidden % 256 == 0 and
+ * inter % 256 == 0, 1 <= top_k <= n_experts.
+ */
+qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up, const void* w_down,
+                                 int64_t n_experts, int64_t hidden, int64_t inter, const uint16_t* x,
+                                 int64_t t, int64_t top_k, const int32_t* ids, const float* weights,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Static English name of a status ("QP_OK", ...). */
+const char* qp_status_string(qp_status s);
+
+/* Detail of the last error returned on the calling thread (host memory owned
+ * by the library, valid until the next call on this thread). */
+const char* qp_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPREFILL_H */

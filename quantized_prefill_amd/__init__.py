@@ -1,0 +1,183 @@
+"""Python binding of libqprefill (include/qprefill.h): argument marshalling only.
+
+Every step of the path runs in the HIP library; torch supplies device memory
+and the current stream.  If the library is not built, or a tensor is not on
+the GPU, the call raises -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqprefill.so")
+
+Q8_0, Q2_K, Q4_K, Q6_K = 8, 10, 12, 14
+F32, F16 = 0, 1
+
+STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_PARAMETER", 2: "QP_ERR_UNSUPPORTED_TYPE",
+          3: "QP_ERR_WORKSPACE_TOO_SMALL", 4: "QP_ERR_DEVICE"}
+
+# name -> (restype, argtypes) for every entry point of include/qprefill.h
+_VP, _I64, _INT, _F32C, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t
+SIGNATURES = {
+    "qp_block_size": (_I64, [_INT]),
+    "qp_type_size": (_I64, [_INT]),
+    "qp_row_bytes": (_I64, [_INT, _I64]),
+    "qp_dequant_f32": (_INT, [_INT, _VP, _I64, _I64, _VP, _VP]),
+    "qp_dequant_f16": (_INT, [_INT, _VP, _I64, _I64, _VP, _VP]),
+    "qp_prefill_gemm": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP]),
+    "qp_prefill_gemm_qknorm": (_INT, [_INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64, _F32C, _VP, _I64,
+                                      _VP]),
+    "qp_moe_route_topk": (_INT, [_VP, _I64, _I64, _I64, _INT, _VP, _VP, _VP]),
+    "qp_grouped_expert_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
+    "qp_grouped_expert_gemm": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP, _VP,
+                                      _SZ, _VP]),
+    "qp_status_string": (C.c_char_p, [_INT]),
+    "qp_last_error_detail": (C.c_char_p, []),
+}
+
+
+class QPError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libqprefill.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise QPError(status, lib().qp_last_error_detail().decode())
+
+
+def block_size(qtype: int) -> int:
+    return lib().qp_block_size(qtype)
+
+
+def type_size(qtype: int) -> int:
+    return lib().qp_type_size(qtype)
+
+
+def row_bytes(qtype: int, cols: int) -> int:
+    return lib().qp_row_bytes(qtype, cols)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def dequant_f32(qtype: int, w, rows: int, cols: int, out=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=w.device)
+    check(lib().qp_dequant_f32(qtype, _dev(w, "w"), rows, cols, _dev(out, "out"), _stream()))
+    return out
+
+
+def dequant_f16(qtype: int, w, rows: int, cols: int, out=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=w.device)
+    check(lib().qp_dequant_f16(qtype, _dev(w, "w"), rows, cols, _dev(out, "out"), _stream()))
+    return out
+
+
+def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None):
+    """y = x . W^T; x is [T, K] float16 or float32 (rows may be strided)."""
+    torch = _torch()
+    t = x.shape[0]
+    if x.dtype == torch.float16:
+        xd = F16
+    elif x.dtype == torch.float32:
+        xd = F32
+    else:
+        raise TypeError("x must be float16 or float32")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor with unit column stride")
+    if out is None:
+        out = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    check(lib().qp_prefill_gemm(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0), out.data_ptr(), out.stride(0),
+                                _stream()))
+    return out
+
+
+def prefill_gemm_qknorm(qtype: int, w, n: int, k: int, x, head_dim: int, gain, gain_head_stride: int = 0,
+                        eps: float = 1e-6, out=None):
+    torch = _torch()
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor with unit column stride")
+    t = x.shape[0]
+    if out is None:
+        out = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    check(lib().qp_prefill_gemm_qknorm(qtype, _dev(w, "w"), n, k, x.data_ptr(), t, x.stride(0), head_dim,
+                                       _dev(gain, "gain"), gain_head_stride, float(eps), out.data_ptr(),
+                                       out.stride(0), _stream()))
+    return out
+
+
+def moe_route_topk(logits, top_k: int, renorm: bool = False, ids=None, weights=None):
+    torch = _torch()
+    t, e = logits.shape
+    if ids is None:
+        ids = torch.empty((t, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((t, top_k), dtype=torch.float32, device=logits.device)
+    check(lib().qp_moe_route_topk(_dev(logits, "logits"), t, e, top_k, int(bool(renorm)), _dev(ids, "ids"),
+                                  _dev(weights, "weights"), _stream()))
+    return ids, weights
+
+
+def grouped_expert_workspace_bytes(t: int, top_k: int, n_experts: int, hidden: int, inter: int) -> int:
+    return lib().qp_grouped_expert_workspace_bytes(t, top_k, n_experts, hidden, inter)
+
+
+def grouped_expert_gemm(qtype: int, w_gate, w_up, w_down, n_experts: int, hidden: int, inter: int, x, ids, weights,
+                        out=None, workspace=None):
+    torch = _torch()
+    t, top_k = ids.shape
+    if out is None:
+        out = torch.empty((t, hidden), dtype=torch.float32, device=x.device)
+    nbytes = grouped_expert_workspace_bytes(t, top_k, n_experts, hidden, inter)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    check(lib().qp_grouped_expert_gemm(qtype, _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"),
+                                       n_experts, hidden, inter, _dev(x, "x"), t, top_k, _dev(ids, "ids"),
+                                       _dev(weights, "weights"), _dev(out, "out"), _dev(workspace, "workspace"),
+                                       workspace.numel(), _stream()))
+    return out

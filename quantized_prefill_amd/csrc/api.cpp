@@ -1,0 +1,195 @@
+// api.cpp -- the C ABI (include/qprefill.h): argument validation, launch,
+// status reporting.  Every check runs before anything is enqueued, so an
+// error leaves every output untouched; there is no CPU fallback ("Qwen3.5
+// batched prefill has no f32 dequant for IQ2_XXS, IQ3_S, IQ3_XXS, Q2_K",
+// sections "Cause" and title: an unsupported type is an InvalidParameter-style
+// error and the engine fails closed).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/qprefill.h"
+#include "qp_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+qp_status fail(qp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+qp_status ok() {
+  g_detail[0] = '\0';
+  return QP_OK;
+}
+
+qp_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported(int qtype) {
+  return qtype == QP_Q8_0 || qtype == QP_Q4_K || qtype == QP_Q6_K || qtype == QP_Q2_K;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every 32-bit index of the kernels in range
+
+}  // namespace
+
+extern "C" {
+
+int64_t qp_block_size(int qtype) {
+  switch (qtype) {
+    case QP_Q8_0: return 32;
+    case QP_Q4_K: case QP_Q6_K: case QP_Q2_K: return 256;
+    default: return -1;
+  }
+}
+
+int64_t qp_type_size(int qtype) {
+  switch (qtype) {
+    case QP_Q8_0: return 34;
+    case QP_Q4_K: return 144;
+    case QP_Q6_K: return 210;
+    case QP_Q2_K: return 84;
+    default: return -1;
+  }
+}
+
+int64_t qp_row_bytes(int qtype, int64_t cols) {
+  const int64_t qk = qp_block_size(qtype);
+  if (qk < 0 || cols <= 0) return -1;
+  return (cols + qk - 1) / qk * qp_type_size(qtype);
+}
+
+static qp_status dequant_common(int qtype, const void* src, int64_t rows, int64_t cols, void* dst, bool f16,
+                                hipStream_t stream) {
+  if (!supported(qtype)) return fail(QP_ERR_UNSUPPORTED_TYPE, "no dequant kernel for ggml type %d", qtype);
+  if (rows < 0 || cols <= 0 || rows > kMaxDim || cols > kMaxDim)
+    return fail(QP_ERR_INVALID_PARAMETER, "rows=%lld cols=%lld out of range", (long long)rows, (long long)cols);
+  if (rows == 0) return ok();
+  if (!src || !dst) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(src, 16)) return fail(QP_ERR_INVALID_PARAMETER, "src must be 16-byte aligned");
+  if (!aligned(dst, f16 ? 2 : 4)) return fail(QP_ERR_INVALID_PARAMETER, "dst misaligned");
+  const int64_t qk = qp_block_size(qtype);
+  const int64_t units = rows * ((cols + qk - 1) / qk) * (qk / 32);
+  if (units > ((int64_t)1 << 40)) return fail(QP_ERR_INVALID_PARAMETER, "tensor too large");
+  return from_hip(qp::launch_dequant(qtype, f16, src, rows, cols, dst, stream), "dequant launch");
+}
+
+qp_status qp_dequant_f32(int qtype, const void* src, int64_t rows, int64_t cols, float* dst, hipStream_t stream) {
+  return dequant_common(qtype, src, rows, cols, dst, false, stream);
+}
+
+qp_status qp_dequant_f16(int qtype, const void* src, int64_t rows, int64_t cols, uint16_t* dst,
+                         hipStream_t stream) {
+  return dequant_common(qtype, src, rows, cols, dst, true, stream);
+}
+
+static qp_status gemm_checks(int qtype, const void* w, int64_t n, int64_t k, const void* x, int64_t t, int64_t ldx,
+                             size_t xsize, const float* y, int64_t ldy) {
+  if (!supported(qtype)) return fail(QP_ERR_UNSUPPORTED_TYPE, "no prefill GEMM for ggml type %d", qtype);
+  if (n <= 0 || k <= 0 || t < 0 || n > kMaxDim || k > kMaxDim || t > kMaxDim)
+    return fail(QP_ERR_INVALID_PARAMETER, "n=%lld k=%lld t=%lld out of range", (long long)n, (long long)k,
+                (long long)t);
+  if (k % 256 != 0) return fail(QP_ERR_INVALID_PARAMETER, "k=%lld must be a multiple of 256", (long long)k);
+  if (ldx < k || ldy < n) return fail(QP_ERR_INVALID_PARAMETER, "ldx < k or ldy < n");
+  if ((ldx * (int64_t)xsize) % 16 != 0) return fail(QP_ERR_INVALID_PARAMETER, "ldx rows must be 16-byte multiples");
+  if (t == 0) return ok();
+  if (!w || !x || !y) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16))
+    return fail(QP_ERR_INVALID_PARAMETER, "w, x and y must be 16-byte aligned");
+  return ok();
+}
+
+qp_status qp_prefill_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype, int64_t t,
+                          int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+  if (x_dtype != QP_F16 && x_dtype != QP_F32) return fail(QP_ERR_INVALID_PARAMETER, "x_dtype must be QP_F16 or QP_F32");
+  qp_status st = gemm_checks(qtype, w, n, k, x, t, ldx, x_dtype == QP_F32 ? 4 : 2, y, ldy);
+  if (st != QP_OK || t == 0) return st;
+  return from_hip(qp::launch_gemm(qtype, w, n, k, x, x_dtype == QP_F32, t, ldx, y, ldy, stream), "gemm launch");
+}
+
+qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,
+                                 int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
+                                 float eps, float* y, int64_t ldy, hipStream_t stream) {
+  qp_status st = gemm_checks(qtype, w, n, k, x, t, ldx, 2, y, ldy);
+  if (st != QP_OK) return st;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(QP_ERR_INVALID_PARAMETER, "head_dim=%lld must be 64 or 128", (long long)head_dim);
+  if (n % head_dim != 0) return fail(QP_ERR_INVALID_PARAMETER, "n must be a multiple of head_dim");
+  if (!(eps > 0.f) || !isfinite(eps)) return fail(QP_ERR_INVALID_PARAMETER, "eps must be finite and > 0");
+  if (gain_head_stride < 0) return fail(QP_ERR_INVALID_PARAMETER, "gain_head_stride must be >= 0");
+  if (t == 0) return ok();
+  if (!gain) return fail(QP_ERR_INVALID_PARAMETER, "null gain");
+  return from_hip(qp::launch_gemm_qknorm(qtype, w, n, k, x, t, ldx, head_dim, gain, gain_head_stride, eps, y, ldy,
+                                         stream),
+                  "gemm_qknorm launch");
+}
+
+qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k, int renorm,
+                            int32_t* ids, float* weights, hipStream_t stream) {
+  if (t < 0 || t > kMaxDim || n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > n_experts)
+    return fail(QP_ERR_INVALID_PARAMETER, "t=%lld n_experts=%lld top_k=%lld out of range", (long long)t,
+                (long long)n_experts, (long long)top_k);
+  if (t == 0) return ok();
+  if (!logits || !ids || !weights) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
+    return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  return from_hip(qp::launch_route_topk(logits, t, n_experts, top_k, renorm, ids, weights, stream), "router launch");
+}
+
+size_t qp_grouped_expert_workspace_bytes(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden,
+                                         int64_t inter) {
+  qp::MoeWorkspace ws;
+  if (!qp::moe_workspace_layout(t, top_k, n_experts, hidden, inter, ws)) return 0;
+  return ws.total;
+}
+
+qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up, const void* w_down,
+                                 int64_t n_experts, int64_t hidden, int64_t inter, const uint16_t* x, int64_t t,
+                                 int64_t top_k, const int32_t* ids, const float* weights, float* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!supported(qtype)) return fail(QP_ERR_UNSUPPORTED_TYPE, "no grouped expert GEMM for ggml type %d", qtype);
+  if (n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > n_experts || t < 0 || hidden <= 0 || inter <= 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "sizes out of range");
+  if (hidden % 256 != 0 || inter % 256 != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "hidden and inter must be multiples of 256");
+  if (hidden > kMaxDim || inter > kMaxDim || t * top_k > ((int64_t)1 << 31) - 1)
+    return fail(QP_ERR_INVALID_PARAMETER, "sizes too large");
+  qp::MoeWorkspace ws;
+  qp::moe_workspace_layout(t, top_k, n_experts, hidden, inter, ws);
+  if (t == 0) return ok();
+  if (!w_gate || !w_up || !w_down || !x || !ids || !weights || !out || !workspace)
+    return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(x, 16) || !aligned(out, 16) ||
+      !aligned(ids, 4) || !aligned(weights, 4) || !aligned(workspace, 256))
+    return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  if (workspace_bytes < ws.total)
+    return fail(QP_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, ws.total);
+  return from_hip(qp::launch_grouped_expert(qtype, w_gate, w_up, w_down, n_experts, hidden, inter, x, t, top_k, ids,
+                                            weights, out, workspace, ws, stream),
+                  "grouped expert launch");
+}
+
+const char* qp_status_string(qp_status s) {
+  switch (s) {
+    case QP_OK: return "QP_OK";
+    case QP_ERR_INVALID_PARAMETER: return "QP_ERR_INVALID_PARAMETER";
+    case QP_ERR_UNSUPPORTED_TYPE: return "QP_ERR_UNSUPPORTED_TYPE";
+    case QP_ERR_WORKSPACE_TOO_SMALL: return "QP_ERR_WORKSPACE_TOO_SMALL";
+    case QP_ERR_DEVICE: return "QP_ERR_DEVICE";
+    default: return "QP_ERR_UNKNOWN";
+  }
+}
+
+const char* qp_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

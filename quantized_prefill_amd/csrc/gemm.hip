@@ -1,0 +1,636 @@
+// gemm.hip -- dequant-on-load FP16 MFMA projection for gfx950, its per-head
+// RMSNorm epilogue, and the two passes of the routed grouped-expert FFN.
+//
+//   Y[t, n] = sum_k X[t, k] * W[n, k]
+// ("QK-norm models take the FP16 batched prefill", section "What changes":
+// a chunk of prompt tokens runs through each projection as one FP16
+// product; the QK norm is per head.)
+//
+// Tiling: a workgroup of 256 threads (4 waves of 64) owns a 128 (tokens) x
+// 128 (output features) tile of Y and walks K in chunks of 64.  Per chunk:
+//   * X: 128 x 64 activations -> LDS as binary16 (f32 inputs are rounded to
+//     nearest-even on the way).
+//   * W: each thread decodes one 32-weight unit of one W row straight from the
+//     GGUF blocks in HBM (nearest-even binary16 of the exact f32 value) into
+//     LDS.  W is never materialised in HBM.
+//   * each wave multiplies its 64 x 64 sub-tile with v_mfma_f32_32x32x16_f16
+//     (2 x 2 tiles of 32 x 32, f32 accumulators), 4 k-steps of 16.
+// LDS is double-buffered: the global loads of chunk c+1 are issued before the
+// MFMAs of chunk c and decoded into the other buffer after them, with one
+// barrier per chunk.  LDS rows are padded to 72 halfs (144 B), which keeps the
+// 16-byte fragment reads of 32 consecutive rows free of bank conflicts.
+//
+// MFMA 32x32x16 operand layout (lane l, 8 halfs per lane): A row l%32 (B
+// column l%32), k = 8*(l/32) + e; result register a of lane l holds
+// D[8*(a/4) + 4*(l/32) + a%4][l%32].
+#include "qp_device.h"
+#include "qp_internal.h"
+
+namespace qp {
+
+constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
+
+struct GemmSmem {
+  _Float16 x[2][BM * LDK];
+  _Float16 w[2][BN * LDK];
+};
+
+enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4 };
+
+struct GemmParams {
+  const uint8_t* w;      // W (or the gate tensors of all experts)
+  const uint8_t* w2;     // up tensors of all experts (gate/up pass)
+  int64_t rb;            // bytes per W row
+  int64_t estride;       // bytes per expert tensor
+  int n;                 // W rows (output features)
+  int k;                 // reduction length (multiple of 256)
+  const void* x;         // activations (f16 or f32), or the f32 h rows (down pass)
+  int64_t ldx;
+  int t;                 // tokens (plain / qknorm)
+  float* y;
+  int64_t ldy;
+  const float* gain;
+  int64_t gstride;
+  int hd;
+  float eps;
+  // routed experts
+  const int* tiles;      // [max_tiles][2]: expert, first row of its list
+  const int* ntiles;
+  const int* offsets;    // first compact row of each expert
+  const int* counts;     // rows of each expert
+  const int* list;       // compact row -> pair index (token * top_k + slot)
+  int top_k;
+  uint32_t* rowmax;      // per compact row: bits of max |h|
+  float* hbuf;           // [pairs][inter]
+  float* dbuf;           // [pairs][hidden]
+  const float* weights;  // [pairs]
+};
+
+__device__ __forceinline__ float row_scale_from_max(uint32_t maxbits, bool inverse) {
+  // Power of two bringing the row's largest |h| into [2^14, 2^15): binary16
+  // then holds every value of the row without overflow.
+  if (maxbits == 0) return 1.f;
+  int be = (int)(maxbits >> 23);
+  int sh = 141 - be;
+  sh = sh < -100 ? -100 : (sh > 100 ? 100 : sh);
+  return __builtin_ldexpf(1.f, inverse ? -sh : sh);
+}
+
+template <int QT, int MODE>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
+  using F = Fmt<QT>;
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile coordinates -------------------------------------------------
+  int m_rows;        // valid rows of this tile
+  int base = 0;      // first compact row (routed passes)
+  int e = 0;         // expert
+  int n0;            // first output column
+  if constexpr (MODE == kGateUp || MODE == kDown) {
+    const int tile = blockIdx.x;
+    if (tile >= *p.ntiles) return;
+    e = p.tiles[2 * tile];
+    const int mstart = p.tiles[2 * tile + 1];
+    base = p.offsets[e] + mstart;
+    m_rows = min(BM, p.counts[e] - mstart);
+    n0 = blockIdx.y * (MODE == kGateUp ? BN / 2 : BN);
+  } else {
+    n0 = blockIdx.x * BN;
+    const int m0 = blockIdx.y * BM;
+    m_rows = min(BM, p.t - m0);
+    base = m0;
+  }
+
+  // ---- per-thread activation rows ---------------------------------------
+  // f16 rows: thread loads rows (tid >> 3) + 32 i, 16 bytes at column 8*(tid & 7)
+  // f32 rows: thread loads rows (tid >> 4) + 16 i, 16 bytes at column 4*(tid & 15)
+  constexpr bool XF32 = (MODE == kPlainF32 || MODE == kDown);
+  constexpr int XR = XF32 ? 8 : 4;
+  const char* xrow[XR];
+  float xscale[XR];
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    int r = XF32 ? (tid >> 4) + 16 * i : (tid >> 3) + 32 * i;
+    r = min(r, m_rows - 1);
+    xscale[i] = 1.f;
+    if constexpr (MODE == kGateUp) {
+      const int tok = p.list[base + r] / p.top_k;
+      xrow[i] = (const char*)((const _Float16*)p.x + (int64_t)tok * p.ldx);
+    } else if constexpr (MODE == kDown) {
+      xrow[i] = (const char*)(p.hbuf + (int64_t)(base + r) * p.k);
+      xscale[i] = row_scale_from_max(p.rowmax[base + r], false);
+    } else if constexpr (XF32) {
+      xrow[i] = (const char*)((const float*)p.x + (int64_t)(base + r) * p.ldx);
+    } else {
+      xrow[i] = (const char*)((const _Float16*)p.x + (int64_t)(base + r) * p.ldx);
+    }
+  }
+  const int xcol = XF32 ? 4 * (tid & 15) : 8 * (tid & 7);
+
+  // ---- per-thread W row ---------------------------------------------------
+  const int wn_t = tid >> 1, kh = tid & 1;
+  const uint8_t* wrow;
+  {
+    if constexpr (MODE == kGateUp) {
+      const int which = (wn_t >> 5) & 1;  // 0: gate, 1: up
+      int gr = n0 + 32 * (wn_t >> 6) + (wn_t & 31);
+      gr = min(gr, p.n - 1);
+      wrow = (which ? p.w2 : p.w) + (int64_t)e * p.estride + (int64_t)gr * p.rb;
+    } else {
+      int gr = min(n0 + wn_t, p.n - 1);
+      wrow = p.w + (int64_t)e * p.estride + (int64_t)gr * p.rb;
+    }
+  }
+
+  u32x4 xv[XF32 ? 8 : 4];
+  Raw<QT> wr;
+
+  auto issue_loads = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      if constexpr (XF32)
+        xv[i] = *(const u32x4*)((const float*)xrow[i] + 64 * c + xcol);
+      else
+        xv[i] = *(const u32x4*)((const _Float16*)xrow[i] + 64 * c + xcol);
+    }
+    const int ui = 2 * c + kh;  // 32-weight unit index within the row
+    wr.load(wrow + (int64_t)(ui / F::UNITS) * F::TS, (uint32_t)(ui % F::UNITS));
+  };
+
+  auto store_lds = [&](int buf) {
+    _Float16* xs = sm.x[buf];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      if constexpr (XF32) {
+        const int r = (tid >> 4) + 16 * i;
+        float4v f = __builtin_bit_cast(float4v, xv[i]);
+        const float s = xscale[i];
+        const uint32_t lo = pack_f16x2(f.x * s, f.y * s), hi = pack_f16x2(f.z * s, f.w * s);
+        *(uint2*)(xs + r * LDK + xcol) = make_uint2(lo, hi);
+      } else {
+        const int r = (tid >> 3) + 32 * i;
+        *(u32x4*)(xs + r * LDK + xcol) = xv[i];
+      }
+    }
+    UnitRaw ur;
+    wr.finish(ur);
+    uint32_t hw[16];
+    unit_to_f16<QT>(ur, hw);
+    _Float16* ws = sm.w[buf] + wn_t * LDK + 32 * kh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(u32x4*)(ws + 8 * q) = (u32x4){hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]};
+  };
+
+  float16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (float16v){};
+
+  const int nch = p.k / BK;
+  issue_loads(0);
+  store_lds(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) issue_loads(c + 1);
+    const _Float16* xs = sm.x[buf];
+    const _Float16* ws = sm.w[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 a[2], b[2];
+      const int koff = 16 * s + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *(const half8*)(xs + (64 * wm + 32 * i + (lane & 31)) * LDK + koff);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const half8*)(ws + (64 * wn + 32 * j + (lane & 31)) * LDK + koff);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (c + 1 < nch) store_lds(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogues ------------------------------------------------------------
+  // row (within the tile) and column (within the wave's 64) of acc[i][j][a]
+  auto row_of = [&](int i, int a) { return 64 * wm + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3); };
+
+  if constexpr (MODE == kPlainF16 || MODE == kPlainF32) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int r = row_of(i, a);
+          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a];
+        }
+      }
+  } else if constexpr (MODE == kQkNorm) {
+    // Sum of squares of each row over the wave's 64 columns, reduced across
+    // the 32 lanes that share a row; heads of 128 columns add the two waves
+    // of the tile through LDS.
+    float* red = (float*)&sm;  // [2 (wn)][BM] partial sums; LDS is free after the last barrier
+    float ss[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        float v = acc[i][0][a] * acc[i][0][a] + acc[i][1][a] * acc[i][1][a];
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
+        ss[i][a] = v;
+      }
+    if (p.hd == 128) {
+      if ((lane & 31) == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) red[wn * BM + row_of(i, a)] = ss[i][a];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int r = row_of(i, a);
+          ss[i][a] = red[r] + red[BM + r];
+        }
+    }
+    const float inv_hd = 1.f / (float)p.hd;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int r = row_of(i, a);
+        const float scale = 1.f / __builtin_sqrtf(ss[i][a] * inv_hd + p.eps);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          const int head = col / p.hd;
+          const float g = p.gain[(int64_t)head * p.gstride + (col - head * p.hd)];
+          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a] * scale * g;
+        }
+      }
+  } else if constexpr (MODE == kGateUp) {
+    // acc[i][0] = gate, acc[i][1] = up for output column n0 + 32 wn + lane%32
+    const int col = n0 + 32 * wn + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int r = row_of(i, a);
+        const float g = acc[i][0][a], u = acc[i][1][a];
+        const float h = g / (1.f + __expf(-g)) * u;
+        const bool ok = r < m_rows && col < p.n;
+        if (ok) p.hbuf[(int64_t)(base + r) * p.n + col] = h;
+        float mx = ok ? __builtin_fabsf(h) : 0.f;
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+        if ((lane & 31) == 0 && r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
+      }
+  } else {  // kDown
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int r = row_of(i, a);
+        if (r >= m_rows) continue;
+        const int pair = p.list[base + r];
+        const float f = row_scale_from_max(p.rowmax[base + r], true) * p.weights[pair];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          if (col < p.n) p.dbuf[(int64_t)pair * p.n + col] = acc[i][j][a] * f;
+        }
+      }
+  }
+}
+
+template <int MODE>
+static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStream_t s) {
+  switch (qtype) {
+    case kQ8_0: hipLaunchKernelGGL((gemm_kernel<kQ8_0, MODE>), grid, dim3(NT), 0, s, p); break;
+    case kQ4_K: hipLaunchKernelGGL((gemm_kernel<kQ4_K, MODE>), grid, dim3(NT), 0, s, p); break;
+    case kQ6_K: hipLaunchKernelGGL((gemm_kernel<kQ6_K, MODE>), grid, dim3(NT), 0, s, p); break;
+    case kQ2_K: hipLaunchKernelGGL((gemm_kernel<kQ2_K, MODE>), grid, dim3(NT), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static int64_t row_bytes_of(int qtype, int64_t cols) {
+  switch (qtype) {
+    case kQ8_0: return (cols + 31) / 32 * 34;
+    case kQ4_K: return (cols + 255) / 256 * 144;
+    case kQ6_K: return (cols + 255) / 256 * 210;
+    case kQ2_K: return (cols + 255) / 256 * 84;
+    default: return -1;
+  }
+}
+
+hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
+                       int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+  GemmParams p = {};
+  p.w = (const uint8_t*)w;
+  p.rb = row_bytes_of(qtype, k);
+  p.n = (int)n;
+  p.k = (int)k;
+  p.x = x;
+  p.ldx = ldx;
+  p.t = (int)t;
+  p.y = y;
+  p.ldy = ldy;
+  dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
+  return x_f32 ? launch_mode<kPlainF32>(qtype, grid, p, s) : launch_mode<kPlainF16>(qtype, grid, p, s);
+}
+
+hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,
+                              int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
+                              float eps, float* y, int64_t ldy, hipStream_t s) {
+  GemmParams p = {};
+  p.w = (const uint8_t*)w;
+  p.rb = row_bytes_of(qtype, k);
+  p.n = (int)n;
+  p.k = (int)k;
+  p.x = x;
+  p.ldx = ldx;
+  p.t = (int)t;
+  p.y = y;
+  p.ldy = ldy;
+  p.gain = gain;
+  p.gstride = gain_head_stride;
+  p.hd = (int)head_dim;
+  p.eps = eps;
+  dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
+  return launch_mode<kQkNorm>(qtype, grid, p, s);
+}
+
+// ---------------------------------------------------------------------------
+// Routed experts: router, token lists, combine.
+
+// One wave per token: softmax over the experts, top_k by logit (largest
+// first, ties to the lower index), weight = softmax probability.
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int t, int ne, int top_k,
+                                                         int renorm, int32_t* __restrict__ ids,
+                                                         float* __restrict__ weights) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= t) return;
+  constexpr int PER = 16;  // up to 1024 experts
+  float v[PER];
+  const float* lg = logits + (int64_t)tok * ne;
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < ne ? lg[e] : -__builtin_inff();
+    mx = __builtin_fmaxf(mx, v[i]);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < ne) sum += __expf(v[i] - mx);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
+  uint32_t taken = 0;
+  float chosen = 0.f;
+  float wsel[16];
+  int isel[16];
+  for (int s = 0; s < top_k; ++s) {
+    float bv = -__builtin_inff();
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      if (e < ne && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oi = __shfl_xor(bi, m, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const float w = __expf(bv - mx) / sum;
+    chosen += w;
+    if (s < 16) {
+      wsel[s] = w;
+      isel[s] = bi;
+    }
+    if (lane == 0 && s >= 16) {
+      ids[(int64_t)tok * top_k + s] = bi;
+      weights[(int64_t)tok * top_k + s] = w;
+    }
+  }
+  if (lane == 0) {
+    const float f = renorm ? 1.f / chosen : 1.f;
+    for (int s = 0; s < top_k && s < 16; ++s) {
+      ids[(int64_t)tok * top_k + s] = isel[s];
+      weights[(int64_t)tok * top_k + s] = wsel[s] * f;
+    }
+    if (renorm)
+      for (int s = 16; s < top_k; ++s) weights[(int64_t)tok * top_k + s] *= f;
+  }
+}
+
+hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t top_k, int renorm, int32_t* ids,
+                             float* weights, hipStream_t s) {
+  hipLaunchKernelGGL(route_topk_kernel, dim3((uint32_t)((t + 3) / 4)), dim3(256), 0, s, logits, (int)t, (int)e,
+                     (int)top_k, renorm, ids, weights);
+  return hipGetLastError();
+}
+
+// Count the pairs of each expert (one workgroup per expert) and clear the
+// row maxima of the h rows.
+__global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ ids, int npairs, int ne,
+                                                        int* __restrict__ counts, uint32_t* __restrict__ rowmax) {
+  __shared__ int red[4];
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int i = threadIdx.x; i < npairs; i += 256) c += ids[i] == e;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) c += __shfl_xor(c, m, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[e] = red[0] + red[1] + red[2] + red[3];
+  for (int i = e * 256 + threadIdx.x; i < npairs; i += ne * 256) rowmax[i] = 0u;
+}
+
+// Exclusive scans of the counts (compact row offsets) and of the tiles per
+// expert; writes the tile table and the number of tiles.  One workgroup of
+// 1024 threads (n_experts <= 1024).
+__global__ __launch_bounds__(1024) void moe_scan_kernel(const int* __restrict__ counts, int ne,
+                                                        int* __restrict__ offsets, int* __restrict__ tiles,
+                                                        int* __restrict__ ntiles) {
+  __shared__ int sc[1024], st[1024];
+  const int e = threadIdx.x;
+  const int c = e < ne ? counts[e] : 0;
+  const int nt = (c + BM - 1) / BM;
+  sc[e] = c;
+  st[e] = nt;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int a = e >= d ? sc[e - d] : 0, b = e >= d ? st[e - d] : 0;
+    __syncthreads();
+    sc[e] += a;
+    st[e] += b;
+    __syncthreads();
+  }
+  if (e < ne) {
+    offsets[e] = sc[e] - c;
+    const int t0 = st[e] - nt;
+    for (int k = 0; k < nt; ++k) {
+      tiles[2 * (t0 + k)] = e;
+      tiles[2 * (t0 + k) + 1] = k * BM;
+    }
+  }
+  if (e == 1023) *ntiles = st[1023];
+}
+
+// Stable compaction: compact row offsets[e] + r holds the r-th pair (in pair
+// order) routed to expert e.  One workgroup per expert.
+__global__ __launch_bounds__(256) void moe_fill_kernel(const int32_t* __restrict__ ids, int npairs,
+                                                       const int* __restrict__ offsets, int* __restrict__ list) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int running = offsets[e];
+  for (int start = 0; start < npairs; start += 256) {
+    const int i = start + threadIdx.x;
+    const bool match = i < npairs && ids[i] == e;
+    const uint64_t bal = __ballot(match);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int woff = 0;
+    for (int w = 0; w < wave; ++w) woff += wsum[w];
+    if (match) list[running + woff + before] = i;
+    running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+}
+
+// out[t, :] = sum over slots s (in order) of the weighted expert outputs of
+// pair t * top_k + s; pairs with an id outside [0, n_experts) add nothing.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ dbuf, const int32_t* __restrict__ ids,
+                                                          int t, int top_k, int ne, int hidden,
+                                                          float* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of out
+  const int64_t nq = (int64_t)t * hidden / 4;
+  if (q >= nq) return;
+  const int tok = (int)(q / (hidden / 4));
+  const int c4 = (int)(q - (int64_t)tok * (hidden / 4));
+  float4v acc = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < top_k; ++s) {
+    const int64_t pair = (int64_t)tok * top_k + s;
+    const int id = ids[pair];
+    if (id < 0 || id >= ne) continue;
+    const float4v v = *(const float4v*)(dbuf + pair * hidden + 4 * c4);
+    acc += v;
+  }
+  *(float4v*)(out + (int64_t)tok * hidden + 4 * c4) = acc;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden, int64_t inter,
+                          MoeWorkspace& ws) {
+  if (t < 0 || top_k <= 0 || n_experts <= 0 || hidden <= 0 || inter <= 0) return false;
+  const int64_t pairs = t * top_k;
+  ws.max_tiles = n_experts + (pairs + BM - 1) / BM;
+  size_t o = 0;
+  ws.counts = o;  o += align256(sizeof(int) * n_experts);
+  ws.offsets = o; o += align256(sizeof(int) * n_experts);
+  ws.ntiles = o;  o += align256(sizeof(int) * 4);
+  ws.tiles = o;   o += align256(sizeof(int) * 2 * ws.max_tiles);
+  ws.list = o;    o += align256(sizeof(int) * pairs);
+  ws.rowmax = o;  o += align256(sizeof(uint32_t) * pairs);
+  ws.hbuf = o;    o += align256(sizeof(float) * pairs * inter);
+  ws.dbuf = o;    o += align256(sizeof(float) * pairs * hidden);
+  ws.total = o;
+  return true;
+}
+
+hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up, const void* w_down,
+                                 int64_t n_experts, int64_t hidden, int64_t inter, const uint16_t* x, int64_t t,
+                                 int64_t top_k, const int32_t* ids, const float* weights, float* out,
+                                 void* workspace, const MoeWorkspace& ws, hipStream_t s) {
+  char* wsb = (char*)workspace;
+  int* counts = (int*)(wsb + ws.counts);
+  int* offsets = (int*)(wsb + ws.offsets);
+  int* ntiles = (int*)(wsb + ws.ntiles);
+  int* tiles = (int*)(wsb + ws.tiles);
+  int* list = (int*)(wsb + ws.list);
+  uint32_t* rowmax = (uint32_t*)(wsb + ws.rowmax);
+  float* hbuf = (float*)(wsb + ws.hbuf);
+  float* dbuf = (float*)(wsb + ws.dbuf);
+  const int npairs = (int)(t * top_k);
+  hipError_t err;
+
+  hipLaunchKernelGGL(moe_count_kernel, dim3((uint32_t)n_experts), dim3(256), 0, s, ids, npairs, (int)n_experts,
+                     counts, rowmax);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(moe_fill_kernel, dim3((uint32_t)n_experts), dim3(256), 0, s, ids, npairs, offsets, list);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  GemmParams p = {};
+  p.tiles = tiles;
+  p.ntiles = ntiles;
+  p.offsets = offsets;
+  p.counts = counts;
+  p.list = list;
+  p.top_k = (int)top_k;
+  p.rowmax = rowmax;
+  p.hbuf = hbuf;
+  p.dbuf = dbuf;
+  p.weights = weights;
+
+  // gate/up: A = gathered token rows, W tile = 64 gate rows + 64 up rows
+  p.w = (const uint8_t*)w_gate;
+  p.w2 = (const uint8_t*)w_up;
+  p.rb = row_bytes_of(qtype, hidden);
+  p.estride = p.rb * inter;
+  p.n = (int)inter;
+  p.k = (int)hidden;
+  p.x = x;
+  p.ldx = hidden;
+  dim3 g1((uint32_t)ws.max_tiles, (uint32_t)((inter + BN / 2 - 1) / (BN / 2)));
+  if ((err = launch_mode<kGateUp>(qtype, g1, p, s)) != hipSuccess) return err;
+
+  // down: A = h rows (scaled to binary16 per row), weighted scatter to dbuf
+  p.w = (const uint8_t*)w_down;
+  p.w2 = nullptr;
+  p.rb = row_bytes_of(qtype, inter);
+  p.estride = p.rb * hidden;
+  p.n = (int)hidden;
+  p.k = (int)inter;
+  p.x = nullptr;
+  dim3 g2((uint32_t)ws.max_tiles, (uint32_t)((hidden + BN - 1) / BN));
+  if ((err = launch_mode<kDown>(qtype, g2, p, s)) != hipSuccess) return err;
+
+  const int64_t nq = t * hidden / 4;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((uint32_t)((nq + 255) / 256)), dim3(256), 0, s, dbuf, ids, (int)t,
+                     (int)top_k, (int)n_experts, (int)hidden, out);
+  return hipGetLastError();
+}
+
+}  // namespace qp

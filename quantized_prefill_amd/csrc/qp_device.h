@@ -1,0 +1,276 @@
+// qp_device.h -- device helpers shared by the gfx950 kernels: vector types,
+// loads of 2-byte-aligned block fields, and per-type decoders of one "unit"
+// of 32 consecutive weights of a block.
+//
+// Block layouts are the GGUF / ggml on-disk convention (the pages name the
+// types -- "Qwen3.5 batched prefill has no f32 dequant for IQ2_XXS, IQ3_S,
+// IQ3_XXS, Q2_K", section "Cause" -- but not their bytes):
+//   Q8_0  34 B / 32  : d f16 @0, qs int8[32] @2                       w = d*q
+//   Q4_K 144 B / 256 : d @0, dmin @2, 12 packed 6-bit (sc, m) @4, qs[128] @16
+//                      w = (d*sc)*q - dmin*m, q the nibble of qs[32*(i/64) + i%32]
+//                      (low nibble for i%64 < 32), sub-block i/32
+//   Q6_K 210 B / 256 : ql[128] @0, qh[64] @128, int8 scales[16] @192, d @208
+//                      w = (d*sc[i/16])*(q-32), q = low4 | hi2 << 4
+//   Q2_K  84 B / 256 : scales[16] @0 (sc low nibble, m high), qs[64] @16, d @80, dmin @82
+//                      w = (d*sc)*q - dmin*m, q 2 bits of qs[32*(i/128) + i%32]
+//
+// A unit is weights 32u .. 32u+31 of a block (u = 0 for Q8_0, 0..7 otherwise):
+// one Q8_0 block, one Q4_K sub-block, or two 16-weight scale groups of Q6_K/Q2_K.
+// All products d*sc*q and dmin*m are exact in binary32 (at most 23 significant
+// bits), so (d*sc)*q - dmin*m rounds once, at the subtraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qp {
+
+constexpr int kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ6_K = 14;
+
+template <int QT> struct Fmt;
+template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, TS = 34, UNITS = 1; };
+template <> struct Fmt<kQ4_K> { static constexpr int QK = 256, TS = 144, UNITS = 8; };
+template <> struct Fmt<kQ6_K> { static constexpr int QK = 256, TS = 210, UNITS = 8; };
+template <> struct Fmt<kQ2_K> { static constexpr int QK = 256, TS = 84, UNITS = 8; };
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// nearest-even binary16 of two floats, packed low | high << 16
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  half2v h = __builtin_convertvector((float2v){lo, hi}, half2v);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// N dwords holding bytes [p, p + 4N) of a 2-byte-aligned address p.  Only
+// 4-byte-aligned dwords that overlap [p, p + 4N) are read, so no load leaves
+// the pages that hold those bytes.
+template <int N>
+__device__ __forceinline__ void load_dw_a2(const uint8_t* p, uint32_t (&out)[N]) {
+  const uintptr_t a = (uintptr_t)p;
+  const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
+  const uint32_t sh = (uint32_t)(a & 3);  // 0 or 2
+  uint32_t d[N + 1];
+#pragma unroll
+  for (int j = 0; j < N; ++j) d[j] = base[j];
+  d[N] = base[sh ? N : N - 1];
+#pragma unroll
+  for (int j = 0; j < N; ++j) out[j] = __builtin_amdgcn_alignbyte(d[j + 1], d[j], sh);
+}
+
+__device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
+  return *(const uint16_t*)p;
+}
+
+// byte i (0..11) of three dwords s0 | s1 << 32 | s2 << 64
+__device__ __forceinline__ uint32_t byte12(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t i) {
+  uint32_t w = i < 4 ? s0 : (i < 8 ? s1 : s2);
+  return (w >> (8 * (i & 3))) & 0xFFu;
+}
+
+// Q4_K 6-bit (scale, min) of sub-block j from the 12 packed scale bytes.
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t j,
+                                              uint32_t& sc, uint32_t& m) {
+  if (j < 4) {
+    sc = byte12(s0, s1, s2, j) & 63u;
+    m = byte12(s0, s1, s2, j + 4) & 63u;
+  } else {
+    const uint32_t b = byte12(s0, s1, s2, j + 4);
+    sc = (b & 15u) | ((byte12(s0, s1, s2, j - 4) >> 6) << 4);
+    m = (b >> 4) | ((byte12(s0, s1, s2, j) >> 6) << 4);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Raw fields of one unit: the quant bytes already shifted so that each byte
+// holds one weight's integer code, and the per-group float factors.
+//   code byte i (of 32) -> weight 32u + i
+//   value_i = A[i/16] * code_i - B[i/16]    (exact products, one rounding)
+// For Q8_0 the code is the signed byte; for Q6_K it is q = code - 32 with
+// A = d*sc and B = 32*d*sc; Q4_K / Q2_K use A = d*sc, B = dmin*m.
+
+struct UnitRaw {
+  uint32_t code[8];  // 32 one-byte codes
+  float a0, a1;      // multiplier for weights 0..15 / 16..31
+  float b0, b1;      // subtrahend (0 for Q8_0)
+  float sm0, sm1;    // Q4_K/Q2_K: dmin*m; Q6_K: d*sc; Q8_0: d (for the literal order)
+};
+
+// Raw<QT>: the bytes of one unit as loaded (load() issues only loads), and
+// finish() turning them into a UnitRaw.  Splitting the two lets a caller keep
+// the loads of the next unit in flight while it works on the current one.
+template <int QT> struct Raw;
+
+template <> struct Raw<kQ8_0> {
+  uint32_t d16, w[9], sh;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t) {
+    d16 = load_u16(blk);
+    const uintptr_t a = (uintptr_t)(blk + 2);
+    const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
+    sh = (uint32_t)(a & 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = base[j];
+    w[8] = base[sh ? 8 : 7];
+  }
+  __device__ __forceinline__ void finish(UnitRaw& r) const {
+    const float d = f16_to_f32(d16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.code[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], sh);
+    r.a0 = r.a1 = d;
+    r.b0 = r.b1 = 0.f;
+    r.sm0 = r.sm1 = d;
+  }
+};
+
+template <> struct Raw<kQ4_K> {
+  u32x4 hdr, q0, q1;
+  uint32_t u;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
+    u = u_;
+    hdr = *(const u32x4*)blk;  // 144-byte blocks keep 16-byte alignment
+    const u32x4* qs = (const u32x4*)(blk + 16 + 32 * (u_ >> 1));
+    q0 = qs[0];
+    q1 = qs[1];
+  }
+  __device__ __forceinline__ void finish(UnitRaw& r) const {
+    const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
+    uint32_t sc, m;
+    q4k_scale_min(hdr.y, hdr.z, hdr.w, u, sc, m);
+    const uint32_t sh = 4 * (u & 1);
+    const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.code[j] = (qq[j] >> sh) & 0x0F0F0F0Fu;
+    const float dsc = __fmul_rn(d, (float)sc);
+    const float dm = __fmul_rn(dmin, (float)m);
+    r.a0 = r.a1 = dsc;
+    r.b0 = r.b1 = dm;
+    r.sm0 = r.sm1 = dm;
+  }
+};
+
+template <> struct Raw<kQ6_K> {
+  uint32_t ql[9], qh[9], shl_a, shh_a, scp, d16, u;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
+    u = u_;
+    const uint32_t h = u_ >> 2, q4 = u_ & 3;
+    const uintptr_t al = (uintptr_t)(blk + 64 * h + 32 * (q4 & 1));
+    const uintptr_t ah = (uintptr_t)(blk + 128 + 32 * h);
+    const uint32_t* bl = (const uint32_t*)(al & ~(uintptr_t)3);
+    const uint32_t* bh = (const uint32_t*)(ah & ~(uintptr_t)3);
+    shl_a = (uint32_t)(al & 3);
+    shh_a = (uint32_t)(ah & 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ql[j] = bl[j];
+    ql[8] = bl[shl_a ? 8 : 7];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qh[j] = bh[j];
+    qh[8] = bh[shh_a ? 8 : 7];
+    scp = load_u16(blk + 192 + 2 * u_);
+    d16 = load_u16(blk + 208);
+  }
+  __device__ __forceinline__ void finish(UnitRaw& r) const {
+    const uint32_t q4 = u & 3;
+    const uint32_t shl = 4 * (q4 >> 1), shh = 2 * q4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t l = __builtin_amdgcn_alignbyte(ql[j + 1], ql[j], shl_a);
+      const uint32_t h = __builtin_amdgcn_alignbyte(qh[j + 1], qh[j], shh_a);
+      r.code[j] = ((l >> shl) & 0x0F0F0F0Fu) | (((h >> shh) & 0x03030303u) << 4);
+    }
+    const float d = f16_to_f32(d16);
+    const float a0 = __fmul_rn(d, (float)(int8_t)(scp & 0xFFu));
+    const float a1 = __fmul_rn(d, (float)(int8_t)(scp >> 8));
+    r.a0 = a0;
+    r.a1 = a1;
+    r.b0 = __fmul_rn(a0, 32.f);
+    r.b1 = __fmul_rn(a1, 32.f);
+    r.sm0 = a0;
+    r.sm1 = a1;
+  }
+};
+
+template <> struct Raw<kQ2_K> {
+  uint32_t qs[8], scp, dd, u;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
+    u = u_;
+    const uint32_t* q = (const uint32_t*)(blk + 16 + 32 * (u_ >> 2));  // 84-byte blocks keep 4-byte alignment
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qs[k] = q[k];
+    scp = load_u16(blk + 2 * u_);
+    dd = *(const uint32_t*)(blk + 80);
+  }
+  __device__ __forceinline__ void finish(UnitRaw& r) const {
+    const uint32_t sh = 2 * (u & 3);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.code[k] = (qs[k] >> sh) & 0x03030303u;
+    const float d = f16_to_f32(dd & 0xFFFFu), dmin = f16_to_f32(dd >> 16);
+    const uint32_t s0 = scp & 0xFFu, s1 = scp >> 8;
+    r.a0 = __fmul_rn(d, (float)(s0 & 15u));
+    r.a1 = __fmul_rn(d, (float)(s1 & 15u));
+    r.b0 = __fmul_rn(dmin, (float)(s0 >> 4));
+    r.b1 = __fmul_rn(dmin, (float)(s1 >> 4));
+    r.sm0 = r.b0;
+    r.sm1 = r.b1;
+  }
+};
+
+template <int QT> __device__ __forceinline__ void load_unit(const uint8_t* blk, uint32_t u, UnitRaw& r) {
+  Raw<QT> raw;
+  raw.load(blk, u);
+  raw.finish(r);
+}
+
+// Exact f32 value of weight i of the unit, in the literal left-to-right order
+// of the definition (used by the bit-exact dequant).
+template <int QT> __device__ __forceinline__ float unit_value_exact(const UnitRaw& r, int i) {
+  const uint32_t c = (r.code[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+  const bool hi = i >= 16;
+  if constexpr (QT == kQ8_0) {
+    return __fmul_rn(r.a0, (float)(int8_t)c);
+  } else if constexpr (QT == kQ6_K) {
+    // (d*sc) * (q - 32); the integer q converts exactly, keeping the sign of zero
+    const float q = (float)((int)c - 32);
+    return __fmul_rn(hi ? r.a1 : r.a0, q);
+  } else {
+    // (d*sc)*q - dmin*m
+    const float p = __fmul_rn(hi ? r.a1 : r.a0, (float)c);
+    return __fsub_rn(p, hi ? r.sm1 : r.sm0);
+  }
+}
+
+// The same value via one fused multiply-add (identical up to the sign of a
+// zero: the product is exact, so the fma rounds once, like the subtraction).
+// Q8_0 codes are biased by 128 (A*(code^0x80) - 128*A) to use the unsigned
+// byte converts.  Used where the result feeds a binary16 operand.
+template <int QT> __device__ __forceinline__ void unit_to_f16(const UnitRaw& r, uint32_t (&out)[16]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t c = r.code[j];
+    float a = j < 4 ? r.a0 : r.a1;
+    float b = j < 4 ? r.b0 : r.b1;
+    if constexpr (QT == kQ8_0) {
+      c ^= 0x80808080u;
+      b = __fmul_rn(a, 128.f);
+    }
+    const float v0 = __builtin_fmaf(a, (float)((c >> 0) & 0xFFu), -b);
+    const float v1 = __builtin_fmaf(a, (float)((c >> 8) & 0xFFu), -b);
+    const float v2 = __builtin_fmaf(a, (float)((c >> 16) & 0xFFu), -b);
+    const float v3 = __builtin_fmaf(a, (float)((c >> 24) & 0xFFu), -b);
+    out[2 * j] = pack_f16x2(v0, v1);
+    out[2 * j + 1] = pack_f16x2(v2, v3);
+  }
+}
+
+}  // namespace qp

@@ -1,0 +1,41 @@
+// qp_internal.h -- launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qp {
+
+hipError_t launch_dequant(int qtype, bool f16out, const void* src, int64_t rows, int64_t cols, void* dst,
+                          hipStream_t s);
+
+hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
+                       int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+
+hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,
+                              int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
+                              float eps, float* y, int64_t ldy, hipStream_t s);
+
+hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t top_k, int renorm, int32_t* ids,
+                             float* weights, hipStream_t s);
+
+// Workspace carve-up of the grouped expert GEMM (offsets in bytes, each
+// 256-byte aligned).
+struct MoeWorkspace {
+  size_t counts, offsets, ntiles, tiles, list, rowmax, hbuf, dbuf, total;
+  int64_t max_tiles;
+};
+bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden, int64_t inter,
+                          MoeWorkspace& ws);
+
+hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up, const void* w_down,
+                                 int64_t n_experts, int64_t hidden, int64_t inter, const uint16_t* x, int64_t t,
+                                 int64_t top_k, const int32_t* ids, const float* weights, float* out,
+                                 void* workspace, const MoeWorkspace& ws, hipStream_t s);
+
+// geometry of the GEMM tiles (the MoE layout and the ABI checks use them)
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+
+}  // namespace qp

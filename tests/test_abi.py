@@ -1,0 +1,96 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/qprefill.h declares, answers the size queries, and rejects bad
+arguments before launching anything (no call here reaches a kernel)."""
+import os
+import re
+
+import pytest
+
+import quantized_prefill_amd as qp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qprefill.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qp.LIB_PATH), reason="libqprefill.so not built")
+
+FAKE = 1 << 20  # a non-null, 256-byte aligned stand-in address; never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 12
+    L = qp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qp.SIGNATURES), "binding and header disagree"
+
+
+def test_geometry():
+    assert [qp.block_size(t) for t in (qp.Q8_0, qp.Q4_K, qp.Q6_K, qp.Q2_K)] == [32, 256, 256, 256]
+    assert [qp.type_size(t) for t in (qp.Q8_0, qp.Q4_K, qp.Q6_K, qp.Q2_K)] == [34, 144, 210, 84]
+    assert qp.row_bytes(qp.Q6_K, 4173) == 17 * 210
+    assert qp.row_bytes(qp.Q8_0, 33) == 2 * 34
+    assert qp.block_size(2) == -1 and qp.row_bytes(qp.Q4_K, 0) == -1
+
+
+def status_name(s):
+    return qp.lib().qp_status_string(s).decode()
+
+
+def test_status_strings():
+    assert [status_name(i) for i in range(5)] == [qp.STATUS[i] for i in range(5)]
+
+
+def test_dequant_rejections():
+    L = qp.lib()
+    assert L.qp_dequant_f32(2, FAKE, 4, 256, FAKE, None) == 2          # IQ4_NL-style id: unsupported
+    assert b"no dequant kernel" in L.qp_last_error_detail()
+    assert L.qp_dequant_f32(qp.Q4_K, FAKE, -1, 256, FAKE, None) == 1
+    assert L.qp_dequant_f32(qp.Q4_K, FAKE, 4, 0, FAKE, None) == 1
+    assert L.qp_dequant_f16(qp.Q4_K, None, 4, 256, FAKE, None) == 1
+    assert L.qp_dequant_f16(qp.Q4_K, FAKE + 2, 4, 256, FAKE, None) == 1  # src not 16-byte aligned
+    assert L.qp_dequant_f32(qp.Q4_K, FAKE, 4, 256, FAKE + 2, None) == 1  # dst not 4-byte aligned
+    assert L.qp_dequant_f32(qp.Q4_K, None, 0, 256, None, None) == 0      # rows == 0: nothing to do
+
+
+def test_gemm_rejections():
+    L = qp.lib()
+    g = L.qp_prefill_gemm
+    assert g(7, FAKE, 64, 256, FAKE, qp.F16, 8, 256, FAKE, 64, None) == 2
+    assert g(qp.Q8_0, FAKE, 64, 96, FAKE, qp.F16, 8, 96, FAKE, 64, None) == 1      # k % 256
+    assert g(qp.Q4_K, FAKE, 64, 256, FAKE, 3, 8, 256, FAKE, 64, None) == 1        # x dtype
+    assert g(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 8, 128, FAKE, 64, None) == 1   # ldx < k
+    assert g(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 8, 256, FAKE, 32, None) == 1   # ldy < n
+    assert g(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 8, 260, FAKE, 64, None) == 1   # ldx*2 % 16
+    assert g(qp.Q4_K, FAKE + 8, 64, 256, FAKE, qp.F16, 8, 256, FAKE, 64, None) == 1
+    assert g(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 0, 256, FAKE, 64, None) == 0   # t == 0
+    q = L.qp_prefill_gemm_qknorm
+    assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 96, FAKE, 0, 1e-6, FAKE, 256, None) == 1   # head_dim
+    assert q(qp.Q4_K, FAKE, 192, 256, FAKE, 8, 256, 128, FAKE, 0, 1e-6, FAKE, 192, None) == 1  # n % hd
+    assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, FAKE, 0, 0.0, FAKE, 256, None) == 1   # eps
+    assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, None, 0, 1e-6, FAKE, 256, None) == 1  # gain
+
+
+def test_moe_rejections():
+    L = qp.lib()
+    assert L.qp_moe_route_topk(FAKE, 4, 2000, 8, 0, FAKE, FAKE, None) == 1
+    assert L.qp_moe_route_topk(FAKE, 4, 128, 0, 0, FAKE, FAKE, None) == 1
+    ws = qp.grouped_expert_workspace_bytes(4096, 8, 128, 2048, 768)
+    assert ws > 4096 * 8 * (2048 + 768) * 4
+    assert qp.grouped_expert_workspace_bytes(4096, 0, 128, 2048, 768) == 0
+    f = L.qp_grouped_expert_gemm
+    args = [qp.Q4_K, FAKE, FAKE, FAKE, 128, 2048, 768, FAKE, 4096, 8, FAKE, FAKE, FAKE, FAKE]
+    assert f(*args, ws - 1, None) == 3
+    assert b"workspace" in L.qp_last_error_detail()
+    bad = list(args)
+    bad[6] = 700  # inter not a multiple of 256
+    assert f(*bad, ws, None) == 1
+    bad = list(args)
+    bad[0] = 3
+    assert f(*bad, ws, None) == 2

@@ -1,0 +1,152 @@
+"""Prefill projection and its QK-norm epilogue on the GPU against the binary64
+oracle: normwise relative error <= 1e-3 and per-token-row cosine >= 0.9999."""
+import numpy as np
+import pytest
+
+import synth
+import quantized_prefill_amd as qp
+from gpu_helpers import assert_close, act_f16, sample_tokens, say, to_dev, weights
+from synth import Q8_0, Q4_K, Q6_K, Q2_K
+
+pytestmark = pytest.mark.gpu
+
+QTYPES = [Q8_0, Q4_K, Q6_K, Q2_K]
+
+
+def run_gemm(qtype, raw, n, k, x: np.ndarray):
+    import torch
+    assert raw.size == n * synth.row_bytes(qtype, k)
+    assert x.shape[1] == k
+    w = to_dev(raw)
+    if x.dtype == np.uint16:
+        xt = to_dev(x).view(torch.float16)
+    else:
+        xt = to_dev(x)
+    y = qp.prefill_gemm(qtype, w, n, k, xt)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# small and ragged: T and N not multiples of the 128 x 128 tile, one token,
+# one output row, several K chunks
+SMALL = [(1, 1, 256), (1, 130, 512), (7, 64, 256), (129, 129, 768), (200, 300, 1024), (64, 257, 256),
+         (300, 96, 512)]
+
+
+@pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
+@pytest.mark.parametrize("t,n,k", SMALL)
+def test_small_shapes(orc, qtype, t, n, k):
+    say(f"gemm {synth.NAMES[qtype]} t={t} n={n} k={k}")
+    raw = weights(qtype, n, k, 8000 + n + k)
+    x = act_f16(t, k, 8100 + t + k)
+    y = run_gemm(qtype, raw, n, k, x)
+    ref = orc.prefill_gemm(qtype, raw, n, k, x)
+    assert_close(y, ref, f"{synth.NAMES[qtype]} {t}x{n}x{k}")
+
+
+def test_f32_activations(orc):
+    """f32 X (rounded to binary16 on load), the 64 x 1024 x 1024 Q8_0 projection."""
+    raw = weights(Q8_0, 1024, 1024, synth.seed_for(0, 0))
+    x = synth.activations_f32(64, 1024, synth.seed_for(0, 1))
+    y = run_gemm(Q8_0, raw, 1024, 1024, x)
+    ref = orc.prefill_gemm(Q8_0, raw, 1024, 1024, x)
+    assert_close(y, ref, "q8_0 64x1024x1024 f32 x")
+
+
+def test_strided_io(orc):
+    """X and Y with row strides larger than K and N."""
+    import torch
+    t, n, k = 100, 192, 512
+    raw = weights(Q4_K, n, k, 8200)
+    x = act_f16(t, k, 8201)
+    xpad = np.zeros((t, k + 64), np.uint16)
+    xpad[:, :k] = x
+    xt = to_dev(xpad).view(torch.float16)[:, :k]
+    ybig = torch.full((t, n + 32), float("nan"), device="cuda")
+    yv = ybig[:, :n]
+    qp.check(qp.lib().qp_prefill_gemm(Q4_K, to_dev(raw).data_ptr(), n, k, xt.data_ptr(), qp.F16, t, k + 64,
+                                      yv.data_ptr(), n + 32, None))
+    torch.cuda.synchronize()
+    yb = ybig.cpu().numpy()
+    assert np.all(np.isnan(yb[:, n:])), "wrote outside the n output columns"
+    assert_close(yb[:, :n], orc.prefill_gemm(Q4_K, raw, n, k, x), "strided")
+
+
+def test_identity_and_determinism(orc):
+    """X = I selects W^T; two runs give identical bits."""
+    k = n = 256
+    raw = weights(Q6_K, n, k, 8300)
+    x = np.zeros((k, k), np.uint16)
+    x[np.arange(k), np.arange(k)] = 0x3C00
+    y = run_gemm(Q6_K, raw, n, k, x)
+    w16 = orc.dequant_f16_bits(Q6_K, raw, n, k).view(np.float16).astype(np.float32)
+    assert np.array_equal(y, w16.T), "identity X must return the binary16 weights exactly"
+    y2 = run_gemm(Q6_K, raw, n, k, x)
+    assert np.array_equal(y, y2)
+
+
+def _projection_cases():
+    cases = []
+    for i, (name, n, k) in enumerate(synth.PROJ_1_7B):
+        cases.append((f"1.7b_{name}_Q4_K", Q4_K, n, k, 512, synth.seed_for(1, i), synth.seed_for(1, 500 + k // 256)))
+    for qt in (Q6_K, Q2_K):
+        for i, (name, n, k) in enumerate(synth.PROJ_8B):
+            cases.append((f"8b_{name}_{synth.NAMES[qt]}", qt, n, k, 2048, synth.seed_for(2, 10 * qt + i),
+                          synth.seed_for(2, 500 + k // 256)))
+    return cases
+
+
+@pytest.mark.parametrize("name,qtype,n,k,t,wseed,xseed", _projection_cases(), ids=[c[0] for c in _projection_cases()])
+def test_workload_projections(orc, name, qtype, n, k, t, wseed, xseed):
+    """Full-size projections in the launch configuration the bench times;
+    the oracle computes a spread of token rows."""
+    say(f"gemm workload {name} t={t} n={n} k={k}")
+    raw = weights(qtype, n, k, wseed)
+    x = act_f16(t, k, xseed)
+    y = run_gemm(qtype, raw, n, k, x)
+    tok = sample_tokens(t, 12, 9000 + n)
+    ref = orc.prefill_gemm(qtype, raw, n, k, x, tokens=tok)
+    assert_close(y[tok], ref, name)
+    weights.cache_clear()
+
+
+def run_qknorm(qtype, raw, n, k, x, hd, gain, gstride, eps):
+    import torch
+    w = to_dev(raw)
+    xt = to_dev(x).view(torch.float16)
+    y = qp.prefill_gemm_qknorm(qtype, w, n, k, xt, hd, to_dev(gain), gstride, eps)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
+def test_qknorm_small(orc, qtype, hd):
+    t, n, k = 77, 384, 512
+    raw = weights(qtype, n, k, 8400 + hd)
+    x = act_f16(t, k, 8401)
+    for gstride, gn in ((0, hd), (hd, n)):
+        gain = synth.gains(gn, 8402 + gstride)
+        y = run_qknorm(qtype, raw, n, k, x, hd, gain, gstride, 1e-6)
+        ref = orc.prefill_gemm_qknorm(qtype, raw, n, k, x, hd, gain, gstride, 1e-6)
+        assert_close(y, ref, f"qknorm {synth.NAMES[qtype]} hd={hd} stride={gstride}")
+
+
+def test_qknorm_workload(orc):
+    """Qwen3-8B attention shapes at T = 8192: Q (Q4_K 4096 -> 32 heads) and
+    K (Q6_K 4096 -> 8 heads), per-head RMSNorm with eps 1e-6."""
+    t, hidden, hd = 8192, 4096, 128
+    x = act_f16(t, hidden, synth.seed_for(3, 0))
+    tok = sample_tokens(t, 12, 9100)
+    for name, qtype, n, wseed, gseed in (("q", Q4_K, 4096, synth.seed_for(3, 1), synth.seed_for(3, 3)),
+                                         ("k", Q6_K, 1024, synth.seed_for(3, 2), synth.seed_for(3, 4))):
+        say(f"qknorm workload {name} n={n}")
+        raw = weights(qtype, n, hidden, wseed)
+        gain = synth.gains(hd, gseed)
+        y = run_qknorm(qtype, raw, n, hidden, x, hd, gain, 0, 1e-6)
+        ref = orc.prefill_gemm_qknorm(qtype, raw, n, hidden, x, hd, gain, 0, 1e-6, tokens=tok)
+        assert_close(y[tok], ref, f"qknorm {name}")
+        # every head of every token is unit-RMS up to the gains (property at full size)
+        hn = (y / np.tile(gain, n // hd)).reshape(t, n // hd, hd)
+        ms = (hn.astype(np.float64) ** 2).mean(axis=2)
+        assert np.allclose(ms, 1.0, atol=2e-3), f"head mean squares off: {ms.min()} {ms.max()}"
