@@ -1,0 +1,326 @@
+"""Benchmark of the quantized prefill path on one MI355X.
+
+One step is one pass of the path over one Qwen3-8B-shaped layer at T = 2048
+prompt tokens, in both Q6_K and Q2_K: the f32 and f16 dequant of every
+projection weight (q, k, v, o, gate, up, down), then every projection
+Y = X . W^T with W dequantized on load (q and k through the per-head QK-norm
+epilogue).  Inputs are seeded synthetic tensors resident in HBM before timing
+starts.  `value` is the projection TFLOP/s (sum of algorithmic flops over the
+sum of the projection launches' HIP-event durations); the dequant GB/s is
+reported beside it.  After the timed region the remaining workloads -- the
+Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the fused
+QK-norm projections at T = 8192 and the routed 128-expert FFN -- are timed
+and reported under "rows".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill projection TFLOP/s (FP16 MFMA %peak) + dequant GB/s, 8B shapes T=2048"
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+WORKLOAD = "q6_k_q2_k_qwen3_8b_t2048"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "qp_device.h"):
+        with open(os.path.join(ROOT, "quantized_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per projection launch from the committed counter runs, if
+    they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP-event pairs around launches on torch's current stream."""
+
+    def __init__(self):
+        self.pending = []   # (category, start, end)
+        self.total = {}
+        self.count = {}
+
+    def run(self, cat, fn):
+        import torch
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pending.append((cat, s, e))
+
+    def collect(self):
+        for cat, s, e in self.pending:
+            self.total[cat] = self.total.get(cat, 0.0) + s.elapsed_time(e)
+            self.count[cat] = self.count.get(cat, 0) + 1
+        self.pending = []
+
+    def reset(self):
+        self.pending, self.total, self.count = [], {}, {}
+
+
+def build_8b(torch, synth, qp):
+    """Weights (both types), activations and outputs of the 8B layer."""
+    t, hidden = 2048, 4096
+    dev = torch.device("cuda")
+    xs = {}
+    for k in sorted({k for _, _, k in synth.PROJ_8B}):
+        xs[k] = torch.from_numpy(synth.activations_f16(t, k, synth.seed_for(2, 500 + k // 256))).to(dev).view(
+            torch.float16)
+    projs = []
+    for qt in (synth.Q6_K, synth.Q2_K):
+        for i, (name, n, k) in enumerate(synth.PROJ_8B):
+            raw = synth.quant_weights(qt, n, k, synth.seed_for(2, 10 * qt + i))
+            projs.append(dict(name=name, qtype=qt, n=n, k=k, w=torch.from_numpy(raw).to(dev),
+                              y=torch.empty((t, n), dtype=torch.float32, device=dev)))
+    gains = {name: torch.from_numpy(synth.gains(128, synth.seed_for(2, 600 + j))).to(dev)
+             for j, name in enumerate(("q", "k"))}
+    maxw = max(p["n"] * p["k"] for p in projs)
+    d32 = torch.empty(maxw, dtype=torch.float32, device=dev)
+    d16 = torch.empty(maxw, dtype=torch.float16, device=dev)
+    return dict(t=t, hidden=hidden, xs=xs, projs=projs, gains=gains, d32=d32, d16=d16)
+
+
+def step_8b(L, qp, timer):
+    for p in L["projs"]:
+        n, k = p["n"], p["k"]
+        timer.run("dequant_f32", lambda p=p: qp.dequant_f32(p["qtype"], p["w"], n, k, out=L["d32"][:n * k].view(n, k)))
+        timer.run("dequant_f16", lambda p=p: qp.dequant_f16(p["qtype"], p["w"], n, k, out=L["d16"][:n * k].view(n, k)))
+    for p in L["projs"]:
+        x = L["xs"][p["k"]]
+        if p["name"] in ("q", "k"):
+            timer.run("gemm", lambda p=p, x=x: qp.prefill_gemm_qknorm(p["qtype"], p["w"], p["n"], p["k"], x, 128,
+                                                                       L["gains"][p["name"]], 0, 1e-6, out=p["y"]))
+        else:
+            timer.run("gemm", lambda p=p, x=x: qp.prefill_gemm(p["qtype"], p["w"], p["n"], p["k"], x, out=p["y"]))
+
+
+def gemm_flops_8b(L):
+    return sum(2.0 * L["t"] * p["n"] * p["k"] for p in L["projs"])
+
+
+def dequant_bytes_8b(L, synth):
+    tot = 0.0
+    for p in L["projs"]:
+        read = p["n"] * synth.row_bytes(p["qtype"], p["k"])
+        tot += 2 * read + p["n"] * p["k"] * (4 + 2)
+    return tot
+
+
+def time_fn(torch, fn, iters):
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters  # ms
+
+
+def other_rows(torch, synth, qp, iters):
+    """The other workloads, each timed on its own after the main region."""
+    dev = torch.device("cuda")
+    rows = {}
+
+    def d(a):
+        return torch.from_numpy(a).to(dev)
+
+    # Q8_0 1024 x 1024, T = 64, f32 activations
+    w = d(synth.quant_weights(synth.Q8_0, 1024, 1024, synth.seed_for(0, 0)))
+    x = d(synth.activations_f32(64, 1024, synth.seed_for(0, 1)))
+    y = torch.empty((64, 1024), device=dev)
+    ms = time_fn(torch, lambda: qp.prefill_gemm(synth.Q8_0, w, 1024, 1024, x, out=y), iters)
+    o32 = torch.empty((1024, 1024), device=dev)
+    msd = time_fn(torch, lambda: qp.dequant_f32(synth.Q8_0, w, 1024, 1024, out=o32), iters)
+    rows["q8_0_1024_t64"] = dict(gemm_tflops=2 * 64 * 1024 * 1024 / ms / 1e9, gemm_us=ms * 1e3,
+                                 dequant_f32_gbps=(1024 * 1088 + 1024 * 1024 * 4) / msd / 1e6)
+    # Q4_K, Qwen3-1.7B layer at T = 512
+    flops, tms, dbytes, dms = 0.0, 0.0, 0.0, 0.0
+    for i, (name, n, k) in enumerate(synth.PROJ_1_7B):
+        w = d(synth.quant_weights(synth.Q4_K, n, k, synth.seed_for(1, i)))
+        x = d(synth.activations_f16(512, k, synth.seed_for(1, 500 + k // 256))).view(torch.float16)
+        y = torch.empty((512, n), device=dev)
+        tms += time_fn(torch, lambda: qp.prefill_gemm(synth.Q4_K, w, n, k, x, out=y), iters)
+        flops += 2.0 * 512 * n * k
+        o32 = torch.empty((n, k), device=dev)
+        dms += time_fn(torch, lambda: qp.dequant_f32(synth.Q4_K, w, n, k, out=o32), iters)
+        dbytes += n * synth.row_bytes(synth.Q4_K, k) + 4.0 * n * k
+    rows["q4_k_qwen3_1p7b_t512"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
+                                        dequant_f32_gbps=dbytes / dms / 1e6)
+    # fused QK norm, T = 8192
+    t = 8192
+    x = d(synth.activations_f16(t, 4096, synth.seed_for(3, 0))).view(torch.float16)
+    flops, tms = 0.0, 0.0
+    for qt, n, ws, gs in ((synth.Q4_K, 4096, synth.seed_for(3, 1), synth.seed_for(3, 3)),
+                          (synth.Q6_K, 1024, synth.seed_for(3, 2), synth.seed_for(3, 4))):
+        w = d(synth.quant_weights(qt, n, 4096, ws))
+        g = d(synth.gains(128, gs))
+        y = torch.empty((t, n), device=dev)
+        tms += time_fn(torch, lambda: qp.prefill_gemm_qknorm(qt, w, n, 4096, x, 128, g, 0, 1e-6, out=y), iters)
+        flops += 2.0 * t * n * 4096
+    rows["qknorm_qwen3_8b_t8192"] = dict(tflops=flops / tms / 1e9, us=tms * 1e3)
+    del x, y
+    # routed experts: 128 experts, top-8, T = 4096, router included
+    t, ne, k, hidden, inter = 4096, 128, 8, 2048, 768
+    wg = d(synth.quant_weights(synth.Q4_K, ne * inter, hidden, synth.seed_for(4, 2)))
+    wu = d(synth.quant_weights(synth.Q4_K, ne * inter, hidden, synth.seed_for(4, 3)))
+    wd = d(synth.quant_weights(synth.Q4_K, ne * hidden, inter, synth.seed_for(4, 4)))
+    x = d(synth.activations_f16(t, hidden, synth.seed_for(4, 0))).view(torch.float16)
+    lg = d(synth.router_logits(t, ne, synth.seed_for(4, 1)))
+    ids = torch.empty((t, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((t, k), dtype=torch.float32, device=dev)
+    out = torch.empty((t, hidden), device=dev)
+    ws = torch.empty(qp.grouped_expert_workspace_bytes(t, k, ne, hidden, inter), dtype=torch.uint8, device=dev)
+
+    def moe():
+        qp.moe_route_topk(lg, k, False, ids=ids, weights=wts)
+        qp.grouped_expert_gemm(synth.Q4_K, wg, wu, wd, ne, hidden, inter, x, ids, wts, out=out, workspace=ws)
+
+    ms = time_fn(torch, moe, iters)
+    flops = 2.0 * t * k * 3 * hidden * inter
+    rows["moe_e128_top8_t4096"] = dict(tflops=flops / ms / 1e9, us=ms * 1e3)
+    return rows
+
+
+def cpu_baseline(synth, budget_s: float):
+    """The oracle (binary64 GEMM over its own exact dequant) on the host cores,
+    on a bounded sample of the same workload: the first few token rows of
+    each 8B projection, growing until about budget_s seconds of CPU work."""
+    import oracle
+    orc = oracle.get()
+    projs = []
+    for qt in (synth.Q6_K, synth.Q2_K):
+        for i, (name, n, k) in enumerate(synth.PROJ_8B):
+            projs.append((qt, n, k, synth.quant_weights(qt, n, k, synth.seed_for(2, 10 * qt + i))))
+    xs = {k: synth.activations_f16(1, k, synth.seed_for(2, 500 + k // 256)) for k in {p[2] for p in projs}}
+    def run(ntok):
+        flops = 0.0
+        t0 = time.perf_counter()
+        for qt, n, k, raw in projs:
+            orc.prefill_gemm(qt, raw, n, k, xs[k][:ntok])
+            flops += 2.0 * ntok * n * k
+        return flops, time.perf_counter() - t0
+
+    flops, dt = run(1)
+    ntok = int(max(1, min(64, budget_s / max(dt, 1e-3))))
+    if ntok > 1:
+        xs = {k: synth.activations_f16(ntok, k, synth.seed_for(2, 500 + k // 256)) for k in xs}
+        flops, dt = run(ntok)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=orc.num_threads(), kind="oracle",
+                sample=f"first {ntok} token rows of each of the 14 Qwen3-8B projections (Q6_K and Q2_K), "
+                       f"binary64 dot products over the oracle's f32 dequant; {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import quantized_prefill_amd as qp
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(2)
+    qp.lib()
+    torch.cuda.set_device(0)
+    print("bench: generating the 8B-layer inputs", file=sys.stderr, flush=True)
+    L = build_8b(torch, synth, qp)
+    torch.cuda.synchronize()
+    timer = Timer()
+    for _ in range(args.warmup):
+        step_8b(L, qp, timer)
+    torch.cuda.synchronize()
+    timer.reset()
+    print("bench: timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_8b(L, qp, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect()
+
+    gemm_ms = timer.total["gemm"] / args.steps
+    deq_ms = (timer.total["dequant_f32"] + timer.total["dequant_f16"]) / args.steps
+    flops = gemm_flops_8b(L)
+    tflops = flops / gemm_ms / 1e9
+    dq_gbps = dequant_bytes_8b(L, synth) / deq_ms / 1e6
+    nlaunch = len(L["projs"])
+    traffic = recorded_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "t": L["t"], "hidden": 4096, "intermediate": 12288, "qtypes": ["Q6_K", "Q2_K"],
+                   "projections": 14},
+        "mfma_frac": round(tflops / PEAK_F16_TFLOPS, 4),
+        "gemm_ms_per_step": round(gemm_ms, 4),
+        "dequant_gbps": round(dq_gbps, 1),
+        "dequant_hbm_frac": round(dq_gbps / PEAK_HBM_GBPS, 4),
+        "dequant_ms_per_step": round(deq_ms, 4),
+        "roofline": {
+            "kernel": "gemm_kernel (all 14 projection launches)",
+            "bound": "mfma",
+            "achieved": round(flops / nlaunch / (gemm_ms / nlaunch) / 1e9, 2),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    del L
+    torch.cuda.empty_cache()
+    if not args.no_rows:
+        print("bench: other workloads", file=sys.stderr, flush=True)
+        res["rows"] = {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in other_rows(torch, synth, qp, 10).items()}
+    if not args.no_cpu:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(synth, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

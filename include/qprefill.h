@@ -81,7 +81,7 @@ int64_t qp_row_bytes(int qtype, int64_t cols);
 /*
  * Dequantize a rows x cols tensor to f32 ("Cause": the f32 dequant of every
  * projection weight; "Acceptance (each row)": bit-exact, partial last block).
- *   src (device): rows * qp_row_bytes(qtype, cols) bytes, 2-byte aligned.
+ *   src (device): rows * qp_row_bytes(qtype, cols) bytes, 16-byte aligned.
  *   dst (device): rows * cols floats, dense row-major: element (r, c) at
  *                 dst[r * cols + c]; 4-byte aligned.  Only these elements
  *                 are written: the unused quants of a partial last block are
@@ -147,7 +147,7 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
  * expert (renorm != 0 divides the chosen weights by their sum).
  *   logits (device): t x n_experts f32.   ids (device): t x top_k int32.
  *   weights (device): t x top_k f32.
- * Requires 1 <= top_k <= n_experts <= 1024.
+ * Requires 1 <= top_k <= min(n_experts, 64) and n_experts <= 1024.
  */
 qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k,
                             int renorm, int32_t* ids, float* weights, hipStream_t stream);

@@ -136,7 +136,7 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
 
 qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k, int renorm,
                             int32_t* ids, float* weights, hipStream_t stream) {
-  if (t < 0 || t > kMaxDim || n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > n_experts)
+  if (t < 0 || t > kMaxDim || n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > n_experts || top_k > 64)
     return fail(QP_ERR_INVALID_PARAMETER, "t=%lld n_experts=%lld top_k=%lld out of range", (long long)t,
                 (long long)n_experts, (long long)top_k);
   if (t == 0) return ok();

@@ -45,7 +45,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 8; ++j) o4[j] = (float4v){v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
     } else {
-      for (int i = 0; i < valid; ++i) o[i] = v[i];
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (i < valid) o[i] = v[i];
     }
   } else {
     uint16_t* o = (uint16_t*)dst_ + off;
@@ -56,7 +58,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
         o4[j] = (u32x4){pack_f16x2(v[8 * j], v[8 * j + 1]), pack_f16x2(v[8 * j + 2], v[8 * j + 3]),
                         pack_f16x2(v[8 * j + 4], v[8 * j + 5]), pack_f16x2(v[8 * j + 6], v[8 * j + 7])};
     } else {
-      for (int i = 0; i < valid; ++i) o[i] = f32_to_f16_bits(v[i]);
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (i < valid) o[i] = f32_to_f16_bits(v[i]);
     }
   }
 }

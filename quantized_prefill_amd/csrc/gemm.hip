@@ -378,14 +378,16 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
 // Routed experts: router, token lists, combine.
 
 // One wave per token: softmax over the experts, top_k by logit (largest
-// first, ties to the lower index), weight = softmax probability.
+// first, ties to the lower index), weight = softmax probability.  Lane s
+// keeps the s-th choice (top_k <= 64), so no register array is indexed at
+// run time.
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int t, int ne, int top_k,
                                                          int renorm, int32_t* __restrict__ ids,
                                                          float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tok >= t) return;
-  constexpr int PER = 16;  // up to 1024 experts
+  constexpr int PER = 16;  // up to 1024 experts, expert lane + 64 i in slot i
   float v[PER];
   const float* lg = logits + (int64_t)tok * ne;
   float mx = -__builtin_inff();
@@ -403,10 +405,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     if (lane + 64 * i < ne) sum += __expf(v[i] - mx);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
-  uint32_t taken = 0;
-  float chosen = 0.f;
-  float wsel[16];
-  int isel[16];
+  uint32_t taken = 0;  // bit i: slot i of this lane already chosen
+  float chosen = 0.f, my_w = 0.f;
+  int my_id = 0;
   for (int s = 0; s < top_k; ++s) {
     float bv = -__builtin_inff();
     int bi = 0x7FFFFFFF;
@@ -430,23 +431,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     const float w = __expf(bv - mx) / sum;
     chosen += w;
-    if (s < 16) {
-      wsel[s] = w;
-      isel[s] = bi;
-    }
-    if (lane == 0 && s >= 16) {
-      ids[(int64_t)tok * top_k + s] = bi;
-      weights[(int64_t)tok * top_k + s] = w;
+    if (lane == s) {
+      my_w = w;
+      my_id = bi;
     }
   }
-  if (lane == 0) {
+  if (lane < top_k) {
     const float f = renorm ? 1.f / chosen : 1.f;
-    for (int s = 0; s < top_k && s < 16; ++s) {
-      ids[(int64_t)tok * top_k + s] = isel[s];
-      weights[(int64_t)tok * top_k + s] = wsel[s] * f;
-    }
-    if (renorm)
-      for (int s = 16; s < top_k; ++s) weights[(int64_t)tok * top_k + s] *= f;
+    ids[(int64_t)tok * top_k + lane] = my_id;
+    weights[(int64_t)tok * top_k + lane] = my_w * f;
   }
 }
 
