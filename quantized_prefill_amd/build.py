@@ -33,7 +33,8 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB)
     objs = []
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    include = os.path.join(os.path.dirname(HERE), "include")
+    common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", include,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + list(extra or [])
     procs = []
     for src in sources():

@@ -8,7 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/qprefill.h"
+#include "qprefill.h"
 #include "qp_internal.h"
 
 namespace {

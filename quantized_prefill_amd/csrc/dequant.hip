@@ -4,12 +4,21 @@
 // dequant, the f16 copy built from the f32 value, a partial last block
 // handled, nothing written outside the output).
 //
-// One thread decodes one unit (32 consecutive weights of a block).  Rows of
-// the tensor are whole blocks back to back, so block g of the flat block
-// sequence is block g % nb of row g / nb.  Adjacent lanes take adjacent
-// units, so a wave's block fields come from a few cache lines and its 16-byte
-// stores cover a contiguous run of the output.  HBM-bound: per weight the
-// kernel reads type_size/QK bytes and writes 4 (f32) or 2 (f16) bytes.
+// HBM-bound: per weight the kernel reads type_size/QK bytes and writes 4
+// (f32) or 2 (f16) bytes, so the design is about the write stream.
+//
+// Dense tensors (cols a multiple of QK, the case of every model projection):
+// the output is the flat sequence of block values, so each lane owns V
+// consecutive outputs (V = 4 floats or 8 halfs, one 16-byte store) and one
+// store instruction of a wave writes 1 KB of contiguous output.  Each lane
+// reads only the few bytes of its V weights (quants, scale, d), which the
+// wave's lanes fetch from the same one or two blocks.  A wave handles G such
+// groups, issuing all loads before the first store.
+//
+// Partial last blocks (cols % QK != 0): one thread decodes one unit (32
+// consecutive weights of a block).  Rows of the tensor are whole blocks back
+// to back, so block g of the flat block sequence is block g % nb of row
+// g / nb; only the cols valid weights of each row are stored.
 #include "qp_device.h"
 #include "qp_internal.h"
 
@@ -65,9 +74,49 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
+template <int QT, bool F16OUT, int G>
+__global__ __launch_bounds__(256) void dequant_flat_kernel(const uint8_t* __restrict__ src, uint64_t total,
+                                                           void* __restrict__ dst_) {
+  using F = Fmt<QT>;
+  constexpr int V = F16OUT ? 8 : 4;
+  constexpr uint64_t GW = 64 * V;  // weights per wave group
+  const uint64_t wave = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63;
+  Span<QT, V> sp[G];
+  uint64_t w0[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    w0[g] = (wave * G + g) * GW + (uint64_t)lane * V;
+    if (w0[g] < total) sp[g].load(src + (w0[g] / F::QK) * F::TS, (uint32_t)(w0[g] % F::QK));
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (w0[g] >= total) continue;
+    float v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = sp[g].value(i);
+    if constexpr (!F16OUT) {
+      __builtin_nontemporal_store((float4v){v[0], v[1], v[2], v[3]}, (float4v*)((float*)dst_ + w0[g]));
+    } else {
+      __builtin_nontemporal_store((u32x4){pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                                          pack_f16x2(v[6], v[7])},
+                                  (u32x4*)((uint16_t*)dst_ + w0[g]));
+    }
+  }
+}
+
 template <int QT, bool F16OUT>
 static hipError_t launch_dequant_t(const void* src, int64_t rows, int64_t cols, void* dst, hipStream_t s) {
   using F = Fmt<QT>;
+  if (cols % F::QK == 0 && ((uintptr_t)dst & 15) == 0) {
+    constexpr int G = 4;
+    const uint64_t total = (uint64_t)rows * cols;
+    const uint64_t gw = F16OUT ? 512 : 256;
+    const uint64_t waves = ((total + gw - 1) / gw + G - 1) / G;
+    hipLaunchKernelGGL((dequant_flat_kernel<QT, F16OUT, G>), dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0, s,
+                       (const uint8_t*)src, total, dst);
+    return hipGetLastError();
+  }
   const uint32_t nb = (uint32_t)((cols + F::QK - 1) / F::QK);
   const uint64_t units = (uint64_t)rows * nb * F::UNITS;
   const uint64_t grid = (units + 255) / 256;

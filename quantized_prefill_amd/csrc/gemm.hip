@@ -6,8 +6,13 @@
 // a chunk of prompt tokens runs through each projection as one FP16
 // product; the QK norm is per head.)
 //
-// Tiling: a workgroup of 256 threads (4 waves of 64) owns a 128 (tokens) x
-// 128 (output features) tile of Y and walks K in chunks of 64.  Per chunk:
+// This file holds the 128-token tile kernel (small token counts, the routed
+// expert passes, f32 activations), the router and the routed-expert list
+// kernels; gemm_tall.hip holds the 256-token tile kernel used for large
+// prefill chunks.
+//
+// Tiling here: a workgroup of 256 threads (4 waves of 64) owns a 128 (tokens)
+// x 128 (output features) tile of Y and walks K in chunks of 64.  Per chunk:
 //   * X: 128 x 64 activations -> LDS as binary16 (f32 inputs are rounded to
 //     nearest-even on the way).
 //   * W: each thread decodes one 32-weight unit of one W row straight from the
@@ -23,58 +28,14 @@
 // MFMA 32x32x16 operand layout (lane l, 8 halfs per lane): A row l%32 (B
 // column l%32), k = 8*(l/32) + e; result register a of lane l holds
 // D[8*(a/4) + 4*(l/32) + a%4][l%32].
-#include "qp_device.h"
-#include "qp_internal.h"
+#include "gemm_common.h"
 
 namespace qp {
-
-constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
 
 struct GemmSmem {
   _Float16 x[2][BM * LDK];
   _Float16 w[2][BN * LDK];
 };
-
-enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4 };
-
-struct GemmParams {
-  const uint8_t* w;      // W (or the gate tensors of all experts)
-  const uint8_t* w2;     // up tensors of all experts (gate/up pass)
-  int64_t rb;            // bytes per W row
-  int64_t estride;       // bytes per expert tensor
-  int n;                 // W rows (output features)
-  int k;                 // reduction length (multiple of 256)
-  const void* x;         // activations (f16 or f32), or the f32 h rows (down pass)
-  int64_t ldx;
-  int t;                 // tokens (plain / qknorm)
-  float* y;
-  int64_t ldy;
-  const float* gain;
-  int64_t gstride;
-  int hd;
-  float eps;
-  // routed experts
-  const int* tiles;      // [max_tiles][2]: expert, first row of its list
-  const int* ntiles;
-  const int* offsets;    // first compact row of each expert
-  const int* counts;     // rows of each expert
-  const int* list;       // compact row -> pair index (token * top_k + slot)
-  int top_k;
-  uint32_t* rowmax;      // per compact row: bits of max |h|
-  float* hbuf;           // [pairs][inter]
-  float* dbuf;           // [pairs][hidden]
-  const float* weights;  // [pairs]
-};
-
-__device__ __forceinline__ float row_scale_from_max(uint32_t maxbits, bool inverse) {
-  // Power of two bringing the row's largest |h| into [2^14, 2^15): binary16
-  // then holds every value of the row without overflow.
-  if (maxbits == 0) return 1.f;
-  int be = (int)(maxbits >> 23);
-  int sh = 141 - be;
-  sh = sh < -100 ? -100 : (sh > 100 ? 100 : sh);
-  return __builtin_ldexpf(1.f, inverse ? -sh : sh);
-}
 
 template <int QT, int MODE>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
@@ -218,101 +179,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogues ------------------------------------------------------------
-  // row (within the tile) and column (within the wave's 64) of acc[i][j][a]
-  auto row_of = [&](int i, int a) { return 64 * wm + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3); };
-
-  if constexpr (MODE == kPlainF16 || MODE == kPlainF32) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int r = row_of(i, a);
-          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a];
-        }
-      }
-  } else if constexpr (MODE == kQkNorm) {
-    // Sum of squares of each row over the wave's 64 columns, reduced across
-    // the 32 lanes that share a row; heads of 128 columns add the two waves
-    // of the tile through LDS.
-    float* red = (float*)&sm;  // [2 (wn)][BM] partial sums; LDS is free after the last barrier
-    float ss[2][16];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        float v = acc[i][0][a] * acc[i][0][a] + acc[i][1][a] * acc[i][1][a];
-#pragma unroll
-        for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
-        ss[i][a] = v;
-      }
-    if (p.hd == 128) {
-      if ((lane & 31) == 0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int a = 0; a < 16; ++a) red[wn * BM + row_of(i, a)] = ss[i][a];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int r = row_of(i, a);
-          ss[i][a] = red[r] + red[BM + r];
-        }
-    }
-    const float inv_hd = 1.f / (float)p.hd;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int r = row_of(i, a);
-        const float scale = 1.f / __builtin_sqrtf(ss[i][a] * inv_hd + p.eps);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-          const int head = col / p.hd;
-          const float g = p.gain[(int64_t)head * p.gstride + (col - head * p.hd)];
-          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a] * scale * g;
-        }
-      }
-  } else if constexpr (MODE == kGateUp) {
-    // acc[i][0] = gate, acc[i][1] = up for output column n0 + 32 wn + lane%32
-    const int col = n0 + 32 * wn + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int r = row_of(i, a);
-        const float g = acc[i][0][a], u = acc[i][1][a];
-        const float h = g / (1.f + __expf(-g)) * u;
-        const bool ok = r < m_rows && col < p.n;
-        if (ok) p.hbuf[(int64_t)(base + r) * p.n + col] = h;
-        float mx = ok ? __builtin_fabsf(h) : 0.f;
-#pragma unroll
-        for (int m = 1; m < 32; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
-        if ((lane & 31) == 0 && r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
-      }
-  } else {  // kDown
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int r = row_of(i, a);
-        if (r >= m_rows) continue;
-        const int pair = p.list[base + r];
-        const float f = row_scale_from_max(p.rowmax[base + r], true) * p.weights[pair];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-          if (col < p.n) p.dbuf[(int64_t)pair * p.n + col] = acc[i][j][a] * f;
-        }
-      }
-  }
+  gemm_epilogue<MODE, 2>(p, acc, base, m_rows, n0, wm, wn, lane, (float*)&sm);
 }
 
 template <int MODE>
@@ -327,14 +194,11 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
   return hipGetLastError();
 }
 
-static int64_t row_bytes_of(int qtype, int64_t cols) {
-  switch (qtype) {
-    case kQ8_0: return (cols + 31) / 32 * 34;
-    case kQ4_K: return (cols + 255) / 256 * 144;
-    case kQ6_K: return (cols + 255) / 256 * 210;
-    case kQ2_K: return (cols + 255) / 256 * 84;
-    default: return -1;
-  }
+// Token-tile height: 256 halves the decode work per flop and is used when the
+// launch still fills the 256 CUs with one 256-token tile each.
+static bool use_tall_tiles(int64_t n, int64_t t) {
+  const int64_t tiles = ((n + BN - 1) / BN) * ((t + 255) / 256);
+  return t >= 512 && tiles >= 256;
 }
 
 hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
@@ -349,6 +213,10 @@ hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const voi
   p.t = (int)t;
   p.y = y;
   p.ldy = ldy;
+  if (!x_f32 && use_tall_tiles(n, t)) {
+    dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
+    return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
+  }
   dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
   return x_f32 ? launch_mode<kPlainF32>(qtype, grid, p, s) : launch_mode<kPlainF16>(qtype, grid, p, s);
 }
@@ -370,6 +238,10 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   p.gstride = gain_head_stride;
   p.hd = (int)head_dim;
   p.eps = eps;
+  if (use_tall_tiles(n, t)) {
+    dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
+    return launch_gemm_tall(qtype, kQkNorm, grid, p, s);
+  }
   dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
   return launch_mode<kQkNorm>(qtype, grid, p, s);
 }

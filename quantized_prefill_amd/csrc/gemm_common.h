@@ -1,0 +1,167 @@
+// gemm_common.h -- definitions shared by the projection kernels: tile
+// constants, launch parameters, and the epilogues that turn the f32
+// accumulators into outputs (plain store, per-head RMSNorm, SiLU(gate)*up,
+// route-weighted expert output).
+//
+// MFMA 32x32x16 result layout: register a of lane l holds
+// D[8*(a/4) + 4*(l/32) + a%4][l%32] of a 32 x 32 tile.
+#pragma once
+
+#include "qp_device.h"
+#include "qp_internal.h"
+
+namespace qp {
+
+constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
+
+enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4 };
+
+struct GemmParams {
+  const uint8_t* w;      // W (or the gate tensors of all experts)
+  const uint8_t* w2;     // up tensors of all experts (gate/up pass)
+  int64_t rb;            // bytes per W row
+  int64_t estride;       // bytes per expert tensor
+  int n;                 // W rows (output features)
+  int k;                 // reduction length (multiple of 256)
+  const void* x;         // activations (f16 or f32), or the f32 h rows (down pass)
+  int64_t ldx;
+  int t;                 // tokens (plain / qknorm)
+  float* y;
+  int64_t ldy;
+  const float* gain;
+  int64_t gstride;
+  int hd;
+  float eps;
+  // routed experts
+  const int* tiles;      // [max_tiles][2]: expert, first row of its list
+  const int* ntiles;
+  const int* offsets;    // first compact row of each expert
+  const int* counts;     // rows of each expert
+  const int* list;       // compact row -> pair index (token * top_k + slot)
+  int top_k;
+  uint32_t* rowmax;      // per compact row: bits of max |h|
+  float* hbuf;           // [pairs][inter]
+  float* dbuf;           // [pairs][hidden]
+  const float* weights;  // [pairs]
+};
+
+// Power of two bringing a row's largest |h| into [2^14, 2^15): binary16 then
+// holds every value of the row without overflow (inverse: its reciprocal).
+__device__ __forceinline__ float row_scale_from_max(uint32_t maxbits, bool inverse) {
+  if (maxbits == 0) return 1.f;
+  int be = (int)(maxbits >> 23);
+  int sh = 141 - be;
+  sh = sh < -100 ? -100 : (sh > 100 ? 100 : sh);
+  return __builtin_ldexpf(1.f, inverse ? -sh : sh);
+}
+
+// Epilogue of a tile whose waves form 2 x 2, each owning WM rows x 64
+// columns (MI = WM / 32 MFMA tiles along M, 2 along N).  `base` is the first
+// output row (token, or compact row of the routed passes), m_rows the valid
+// rows, n0 the first output column.  `red` is LDS scratch of 2 * 2 * WM
+// floats, free once the main loop's last barrier has passed.
+// `active` false: a wave holding no tile (the producer waves of the
+// specialised kernel) only takes part in the epilogue's barriers.
+template <int MODE, int MI>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
+                                              int n0, int wm, int wn, int lane, float* red, bool active = true) {
+  constexpr int WM = 32 * MI;
+  if (!active) {
+    if constexpr (MODE == kQkNorm) __syncthreads();
+    return;
+  }
+  auto row_of = [&](int i, int a) { return WM * wm + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3); };
+
+  if constexpr (MODE == kPlainF16 || MODE == kPlainF32) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int r = row_of(i, a);
+          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a];
+        }
+      }
+  } else if constexpr (MODE == kQkNorm) {
+    // Sum of squares of each row over the wave's 64 columns, reduced across
+    // the 32 lanes that share a row, parked in LDS; after one barrier a head
+    // of 64 columns reads its wave's sum, a head of 128 adds the two waves'.
+    constexpr int TM = 2 * WM;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        float v = acc[i][0][a] * acc[i][0][a] + acc[i][1][a] * acc[i][1][a];
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
+        if ((lane & 31) == 0) red[wn * TM + row_of(i, a)] = v;
+      }
+    __syncthreads();
+    const float inv_hd = 1.f / (float)p.hd;
+    const bool pair_heads = p.hd == 128;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int r = row_of(i, a);
+        const float ss = pair_heads ? red[r] + red[TM + r] : red[wn * TM + r];
+        const float scale = 1.f / __builtin_sqrtf(ss * inv_hd + p.eps);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          const int head = col / p.hd;
+          const float g = p.gain[(int64_t)head * p.gstride + (col - head * p.hd)];
+          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a] * scale * g;
+        }
+      }
+  } else if constexpr (MODE == kGateUp) {
+    // acc[i][0] = gate, acc[i][1] = up for output column n0 + 32 wn + lane%32
+    const int col = n0 + 32 * wn + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int r = row_of(i, a);
+        const float g = acc[i][0][a], u = acc[i][1][a];
+        const float h = g / (1.f + __expf(-g)) * u;
+        const bool ok = r < m_rows && col < p.n;
+        if (ok) p.hbuf[(int64_t)(base + r) * p.n + col] = h;
+        float mx = ok ? __builtin_fabsf(h) : 0.f;
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+        if ((lane & 31) == 0 && r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
+      }
+  } else {  // kDown
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int r = row_of(i, a);
+        if (r >= m_rows) continue;
+        const int pair = p.list[base + r];
+        const float f = row_scale_from_max(p.rowmax[base + r], true) * p.weights[pair];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          if (col < p.n) p.dbuf[(int64_t)pair * p.n + col] = acc[i][j][a] * f;
+        }
+      }
+  }
+}
+
+static inline int64_t row_bytes_of(int qtype, int64_t cols) {
+  switch (qtype) {
+    case kQ8_0: return (cols + 31) / 32 * 34;
+    case kQ4_K: return (cols + 255) / 256 * 144;
+    case kQ6_K: return (cols + 255) / 256 * 210;
+    case kQ2_K: return (cols + 255) / 256 * 84;
+    default: return -1;
+  }
+}
+
+// The 256-token tile kernel (gemm_tall.hip) for the plain f16 and QK-norm modes.
+hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p, hipStream_t s);
+
+}  // namespace qp

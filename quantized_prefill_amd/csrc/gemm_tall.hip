@@ -1,0 +1,317 @@
+// gemm_tall.hip -- the 256-token tile of the dequant-on-load projection
+//   Y[t, n] = sum_k X[t, k] * W[n, k]
+// ("QK-norm models take the FP16 batched prefill", section "What changes":
+// chunked batched prefill in FP16; the QK norm is per head).
+//
+// Why a separate kernel: the weight bytes of a 128-row tile are few
+// (0.3-1 byte per weight) but each GGUF row lives in its own place in HBM.
+// Loading them lane-per-row puts 32 rows into every load instruction, which
+// keeps the vector address unit busy far longer than the MFMAs of a tile.
+// Here the workgroup copies whole superblock columns of its 128 weight rows
+// with contiguous loads (one row per wave instruction, one dword per lane)
+// into an LDS staging area, one unit of K ahead, and decodes from LDS.  The
+// 256-token height halves the decode work per flop compared with 128.
+//
+// Workgroup: 512 threads = 8 waves.  Four consumer waves (2 x 2, each 128
+// tokens x 64 features, 4 x 2 MFMA tiles of 32 x 32, v_mfma_f32_32x32x16_f16
+// with f32 accumulation) only read fragments and multiply; four producer waves
+// only stage weight bytes and decode them.  Each SIMD runs one wave of each
+// role, so decode arithmetic issues beside the MFMAs.  K advances in chunks of
+// 64; per chunk:
+//   * activations 256 x 64 (binary16) go straight from global memory into an
+//     LDS ring of three buffers (16-byte direct loads issued by the consumer
+//     waves two chunks ahead);
+//   * each producer thread decodes one 32-weight unit of one weight row from
+//     the LDS staging copy into the binary16 weight tile (nearest-even of the
+//     exact f32 value);
+//   * 32 MFMAs per consumer wave.
+// LDS tiles keep rows of 64 halfs (128 B) as 8 pieces of 16 B; piece p of row
+// r sits in slot p ^ (r & 7), so 16-byte fragment reads of 8 consecutive rows
+// hit 8 different bank groups.  The staging copy keeps RSD dwords per row with
+// RSD odd (dword reads of 32 rows at one offset are conflict-free).
+#include "gemm_common.h"
+
+namespace qp {
+
+constexpr int TBM = 256;           // tokens per tile
+constexpr int TMI = TBM / 2 / 32;  // MFMA tiles per wave along M
+
+// Staging unit of K per type: weights (KW), bytes per row (UB), LDS dwords
+// per row (RSD >= (UB + 2 + 3) / 4, odd).
+template <int QT> struct StageUnit;
+template <> struct StageUnit<kQ4_K> { static constexpr int KW = 256, UB = 144, RSD = 37; };
+template <> struct StageUnit<kQ6_K> { static constexpr int KW = 256, UB = 210, RSD = 53; };
+template <> struct StageUnit<kQ2_K> { static constexpr int KW = 256, UB = 84, RSD = 21; };
+template <> struct StageUnit<kQ8_0> { static constexpr int KW = 128, UB = 136, RSD = 35; };
+
+constexpr int XBUF = 3;  // activation ring depth
+static_assert(BN * 21 >= 4 * TBM / 2 * 2 / 2, "staging area holds the epilogue reduction scratch");
+
+template <int QT>
+struct TallSmem {
+  _Float16 x[XBUF][TBM * BK];
+  _Float16 w[2][BN * BK];
+  uint32_t raw[BN * StageUnit<QT>::RSD];
+};
+
+// LDS offset (halfs) of 16-byte piece `piece` of tile row `row`
+__device__ __forceinline__ int swz(int row, int piece) { return (row * 8 + (piece ^ (row & 7))) * 8; }
+
+// 8 dwords holding block bytes [f0, f0 + 32) of a staged row whose block
+// starts `delta` (0 or 2) bytes into its first dword.
+__device__ __forceinline__ void staged32(const uint32_t* row, uint32_t delta, uint32_t f0, uint32_t (&out)[8]) {
+  const uint32_t b = delta + f0, k0 = b >> 2, s = b & 3;
+  uint32_t d[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) d[i] = row[k0 + i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], s);
+}
+
+// the 16-bit field at block byte f (f even) of a staged row
+__device__ __forceinline__ uint32_t staged16(const uint32_t* row, uint32_t delta, uint32_t f) {
+  const uint32_t b = delta + f;
+  return (row[b >> 2] >> (8 * (b & 3))) & 0xFFFFu;
+}
+
+// Decode 32-weight unit `ui` of a staged unit (a Q8_0 unit is 4 blocks; the
+// K types' is one superblock) into the UnitRaw form of qp_device.h.
+template <int QT> __device__ __forceinline__ void staged_unit(const uint32_t* row, uint32_t delta, uint32_t ui,
+                                                             UnitRaw& r);
+
+template <> __device__ __forceinline__ void staged_unit<kQ8_0>(const uint32_t* row, uint32_t delta, uint32_t ui,
+                                                              UnitRaw& r) {
+  const uint32_t f = 34 * ui;
+  const float d = f16_to_f32(staged16(row, delta, f));
+  staged32(row, delta, f + 2, r.code);
+  r.a0 = r.a1 = d;
+  r.b0 = r.b1 = 0.f;
+  r.sm0 = r.sm1 = d;
+}
+
+template <> __device__ __forceinline__ void staged_unit<kQ4_K>(const uint32_t* row, uint32_t, uint32_t u, UnitRaw& r) {
+  const uint32_t h0 = row[0], s0 = row[1], s1 = row[2], s2 = row[3];  // 144-byte blocks: delta is 0
+  const float d = f16_to_f32(h0 & 0xFFFFu), dmin = f16_to_f32(h0 >> 16);
+  uint32_t sc, m;
+  q4k_scale_min(s0, s1, s2, u, sc, m);
+  const uint32_t* qs = row + 4 + 8 * (u >> 1);
+  const uint32_t sh = 4 * (u & 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.code[j] = (qs[j] >> sh) & 0x0F0F0F0Fu;
+  const float dsc = __fmul_rn(d, (float)sc);
+  const float dm = __fmul_rn(dmin, (float)m);
+  r.a0 = r.a1 = dsc;
+  r.b0 = r.b1 = dm;
+  r.sm0 = r.sm1 = dm;
+}
+
+template <> __device__ __forceinline__ void staged_unit<kQ6_K>(const uint32_t* row, uint32_t delta, uint32_t u,
+                                                              UnitRaw& r) {
+  const uint32_t h = u >> 2, q4 = u & 3;
+  uint32_t ql[8], qh[8];
+  staged32(row, delta, 64 * h + 32 * (q4 & 1), ql);
+  staged32(row, delta, 128 + 32 * h, qh);
+  const uint32_t scp = staged16(row, delta, 192 + 2 * u);
+  const float d = f16_to_f32(staged16(row, delta, 208));
+  const uint32_t shl = 4 * (q4 >> 1), shh = 2 * q4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.code[j] = ((ql[j] >> shl) & 0x0F0F0F0Fu) | (((qh[j] >> shh) & 0x03030303u) << 4);
+  const float a0 = __fmul_rn(d, (float)(int8_t)(scp & 0xFFu));
+  const float a1 = __fmul_rn(d, (float)(int8_t)(scp >> 8));
+  r.a0 = a0;
+  r.a1 = a1;
+  r.b0 = __fmul_rn(a0, 32.f);
+  r.b1 = __fmul_rn(a1, 32.f);
+  r.sm0 = a0;
+  r.sm1 = a1;
+}
+
+template <> __device__ __forceinline__ void staged_unit<kQ2_K>(const uint32_t* row, uint32_t, uint32_t u, UnitRaw& r) {
+  const uint32_t* qs = row + 4 + 8 * (u >> 2);  // 84-byte blocks: delta is 0
+  const uint32_t sh = 2 * (u & 3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r.code[k] = (qs[k] >> sh) & 0x03030303u;
+  const uint32_t scp = (row[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+  const uint32_t dd = row[20];
+  const float d = f16_to_f32(dd & 0xFFFFu), dmin = f16_to_f32(dd >> 16);
+  const uint32_t s0 = scp & 0xFFu, s1 = scp >> 8;
+  r.a0 = __fmul_rn(d, (float)(s0 & 15u));
+  r.a1 = __fmul_rn(d, (float)(s1 & 15u));
+  r.b0 = __fmul_rn(dmin, (float)(s0 >> 4));
+  r.b1 = __fmul_rn(dmin, (float)(s1 >> 4));
+  r.sm0 = r.b0;
+  r.sm1 = r.b1;
+}
+
+template <int QT, int MODE>
+__global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
+  using SU = StageUnit<QT>;
+  constexpr int RSD = SU::RSD, CPU = SU::KW / BK;  // chunks per staging unit
+  __shared__ __attribute__((aligned(16))) TallSmem<QT> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Roles: waves of even bit parity {0, 3, 5, 6} multiply, {1, 2, 4, 7}
+  // produce.  Whether a SIMD takes waves {i, i + 4} or {2i, 2i + 1} of the
+  // workgroup, each SIMD then runs one of each.
+  const bool producer = (__builtin_popcount(wave) & 1) != 0;
+  const int role_idx = wave >> 1;  // 0..3 within each role
+  const int n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * TBM;
+  const int m_rows = min(TBM, p.t - m0);
+  const int nch = p.k / BK;
+  const int nunits = p.k / SU::KW;
+
+  float16v acc[TMI][2];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (float16v){};
+  const int wm = role_idx >> 1, wn = role_idx & 1;
+
+  if (!producer) {
+    // ---- consumer waves -------------------------------------------------
+    // Activation copy: this wave's 8 load instructions cover tile rows
+    // 64 cw + 8 q .. + 7; lane l lands in slot l & 7 of row (l >> 3), which
+    // holds piece (l & 7) ^ (l >> 3).
+    const int cw = role_idx;
+    const _Float16* xsrc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 64 * cw + 8 * q + (lane >> 3);
+      const int piece = (lane & 7) ^ (lane >> 3);
+      xsrc[q] = (const _Float16*)p.x + (int64_t)(m0 + min(row, m_rows - 1)) * p.ldx + 8 * piece;
+    }
+    auto load_x = [&](int c) {
+      c = c < nch ? c : nch - 1;
+      _Float16* dst = sm.x[c % XBUF] + 64 * cw * BK;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + 64 * c),
+                                         (__attribute__((address_space(3))) void*)(dst + 8 * q * BK), 16, 0, 0);
+    };
+    auto frags = [&](const _Float16* xs, const _Float16* ws, int s, half8 (&a)[TMI], half8 (&b)[2]) {
+      const int piece = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) a[i] = *(const half8*)(xs + swz(128 * wm + 32 * i + (lane & 31), piece));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const half8*)(ws + swz(64 * wn + 32 * j + (lane & 31), piece));
+    };
+    auto mfmas = [&](const half8 (&a)[TMI], const half8 (&b)[2]) {
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
+    load_x(0);
+    load_x(1);
+    __syncthreads();                                   // staging of the first unit
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // chunk 0 landed, chunk 1 may be in flight
+    __syncthreads();                                   // first chunk decoded
+    constexpr int NF = TMI + 2, NM = 2 * TMI;
+    for (int c = 0; c < nch; ++c) {
+      load_x(c + 2);
+      const _Float16* xs = sm.x[c % XBUF];
+      const _Float16* ws = sm.w[c & 1];
+      half8 a0[TMI], b0[2], a1[TMI], b1[2];
+      frags(xs, ws, 0, a0, b0);
+      frags(xs, ws, 1, a1, b1);
+      mfmas(a0, b0);
+      frags(xs, ws, 2, a0, b0);
+      mfmas(a1, b1);
+      frags(xs, ws, 3, a1, b1);
+      mfmas(a0, b0);
+      mfmas(a1, b1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);       // activation loads of chunk c + 2
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF, 0);  // steps 0, 1 fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);      // step 0 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);      // step 2 reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);      // step 1 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);      // step 3 reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);  // steps 2, 3 MFMAs
+      if ((c + 1) % CPU == 0 && c + 1 < nch) __syncthreads();  // next unit staged
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");         // chunk c + 1 landed
+      __syncthreads();                                          // next chunk decoded
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
+  } else {
+    // ---- producer waves: stage and decode the next chunk ----------------
+    const int pw = role_idx;        // 0..3
+    const int pt = pw * 64 + lane;  // 0..255
+    // staging copy: producer wave pw copies rows pw + 4 r (r < 32), lane = dword of the row
+    uint32_t stg[BN / 4];
+    auto stage_load = [&](int u) {
+      u = u < nunits ? u : nunits - 1;
+#pragma unroll
+      for (int r = 0; r < BN / 4; ++r) {
+        const int n = pw + 4 * r;
+        const uint8_t* blk = p.w + (int64_t)min(n0 + n, p.n - 1) * p.rb + (int64_t)u * SU::UB;
+        const uintptr_t a = (uintptr_t)blk;
+        const uint32_t cnt = (uint32_t)(((a & 3) + SU::UB + 3) >> 2);
+        const uint32_t* src = (const uint32_t*)(a & ~(uintptr_t)3);
+        uint32_t v = 0u;
+        if ((uint32_t)lane < cnt) v = src[lane];
+        stg[r] = v;
+      }
+    };
+    auto stage_store = [&]() {
+      if (lane < RSD) {
+#pragma unroll
+        for (int r = 0; r < BN / 4; ++r) sm.raw[(pw + 4 * r) * RSD + lane] = stg[r];
+      }
+    };
+    // decode: producer thread owns weight row pt >> 1 of the tile, 32-weight half kh
+    const int wn_t = pt >> 1, kh = pt & 1;
+    const uint8_t* wrow = p.w + (int64_t)min(n0 + wn_t, p.n - 1) * p.rb;
+    auto decode = [&](int c, int buf) {
+      const int u = c / CPU;
+      const uint32_t delta = (uint32_t)(((uintptr_t)wrow + (uintptr_t)u * SU::UB) & 3);
+      UnitRaw ur;
+      staged_unit<QT>(sm.raw + wn_t * RSD, delta, (uint32_t)(2 * (c % CPU) + kh), ur);
+      uint32_t hw[16];
+      unit_to_f16<QT>(ur, hw);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(u32x4*)(sm.w[buf] + swz(wn_t, 4 * kh + q)) = (u32x4){hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]};
+    };
+
+    stage_load(0);
+    stage_store();
+    __syncthreads();  // staging of the first unit
+    decode(0, 0);
+    stage_load(1);
+    __syncthreads();  // first chunk decoded
+    for (int c = 0; c < nch; ++c) {
+      if ((c + 1) % CPU == 0 && c + 1 < nch) {
+        stage_store();    // every producer finished decoding the previous unit
+        __syncthreads();  // next unit staged
+        stage_load((c + 1) / CPU + 1);
+      }
+      if (c + 1 < nch) decode(c + 1, (c + 1) & 1);
+      __syncthreads();  // next chunk decoded
+    }
+  }
+
+  // reduction scratch in the staging area: no asynchronous copy writes there
+  gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw, !producer);
+}
+
+hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p, hipStream_t s) {
+#define QP_TALL(QT)                                                                          \
+  if (mode == kQkNorm)                                                                       \
+    hipLaunchKernelGGL((gemm_tall_kernel<QT, kQkNorm>), grid, dim3(2 * NT), 0, s, p);        \
+  else                                                                                       \
+    hipLaunchKernelGGL((gemm_tall_kernel<QT, kPlainF16>), grid, dim3(2 * NT), 0, s, p);
+  switch (qtype) {
+    case kQ8_0: QP_TALL(kQ8_0) break;
+    case kQ4_K: QP_TALL(kQ4_K) break;
+    case kQ6_K: QP_TALL(kQ6_K) break;
+    case kQ2_K: QP_TALL(kQ2_K) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QP_TALL
+  return hipGetLastError();
+}
+
+}  // namespace qp

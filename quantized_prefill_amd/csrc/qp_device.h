@@ -74,6 +74,17 @@ __device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
   return *(const uint16_t*)p;
 }
 
+// 4 dwords from a 4-byte-aligned address, as one 16-byte load (multi-dword
+// global loads need only dword alignment)
+__device__ __forceinline__ void load_x4(const uint32_t* p, uint32_t* out) {
+  u32x4 v;
+  __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 16);
+  out[0] = v.x;
+  out[1] = v.y;
+  out[2] = v.z;
+  out[3] = v.w;
+}
+
 // byte i (0..11) of three dwords s0 | s1 << 32 | s2 << 64
 __device__ __forceinline__ uint32_t byte12(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t i) {
   uint32_t w = i < 4 ? s0 : (i < 8 ? s1 : s2);
@@ -120,8 +131,8 @@ template <> struct Raw<kQ8_0> {
     const uintptr_t a = (uintptr_t)(blk + 2);
     const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
     sh = (uint32_t)(a & 3);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = base[j];
+    load_x4(base, w);
+    load_x4(base + 4, w + 4);
     w[8] = base[sh ? 8 : 7];
   }
   __device__ __forceinline__ void finish(UnitRaw& r) const {
@@ -171,11 +182,11 @@ template <> struct Raw<kQ6_K> {
     const uint32_t* bh = (const uint32_t*)(ah & ~(uintptr_t)3);
     shl_a = (uint32_t)(al & 3);
     shh_a = (uint32_t)(ah & 3);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ql[j] = bl[j];
+    load_x4(bl, ql);
+    load_x4(bl + 4, ql + 4);
     ql[8] = bl[shl_a ? 8 : 7];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qh[j] = bh[j];
+    load_x4(bh, qh);
+    load_x4(bh + 4, qh + 4);
     qh[8] = bh[shh_a ? 8 : 7];
     scp = load_u16(blk + 192 + 2 * u_);
     d16 = load_u16(blk + 208);
@@ -206,8 +217,8 @@ template <> struct Raw<kQ2_K> {
   __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
     u = u_;
     const uint32_t* q = (const uint32_t*)(blk + 16 + 32 * (u_ >> 2));  // 84-byte blocks keep 4-byte alignment
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qs[k] = q[k];
+    load_x4(q, qs);
+    load_x4(q + 4, qs + 4);
     scp = load_u16(blk + 2 * u_);
     dd = *(const uint32_t*)(blk + 80);
   }
@@ -231,6 +242,107 @@ template <int QT> __device__ __forceinline__ void load_unit(const uint8_t* blk, 
   raw.load(blk, u);
   raw.finish(r);
 }
+
+// Span<QT, V>: V consecutive weights (V = 4 or 8, i0 % V == 0) of one block,
+// loaded with a handful of coalescible loads (load) and turned into their
+// exact f32 values in the literal order of the definition (value).  Used by
+// the streaming dequant, whose lanes each own V consecutive outputs.
+template <int QT, int V> struct Span;
+
+template <int V> struct Span<kQ8_0, V> {
+  static constexpr int N = V / 4;
+  uint32_t d16, w[N + 1], sh;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
+    d16 = load_u16(blk);
+    const uintptr_t a = (uintptr_t)(blk + 2 + i0);
+    const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
+    sh = (uint32_t)(a & 3);
+#pragma unroll
+    for (int j = 0; j < N; ++j) w[j] = base[j];
+    w[N] = base[sh ? N : N - 1];
+  }
+  __device__ __forceinline__ float value(int i) const {
+    const uint32_t dw = __builtin_amdgcn_alignbyte(w[i / 4 + 1], w[i / 4], sh);
+    return __fmul_rn(f16_to_f32(d16), (float)(int8_t)((dw >> (8 * (i & 3))) & 0xFFu));
+  }
+};
+
+template <int V> struct Span<kQ4_K, V> {
+  static constexpr int N = V / 4;
+  u32x4 hdr;
+  uint32_t q[N], j;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
+    hdr = *(const u32x4*)blk;
+    j = i0 / 32;
+    const uint32_t* qs = (const uint32_t*)(blk + 16 + 32 * (i0 / 64) + (i0 % 32));
+#pragma unroll
+    for (int k = 0; k < N; ++k) q[k] = qs[k];
+  }
+  __device__ __forceinline__ float value(int i) const {
+    uint32_t sc, m;
+    q4k_scale_min(hdr.y, hdr.z, hdr.w, j, sc, m);
+    const uint32_t code = (q[i / 4] >> (8 * (i & 3) + 4 * (j & 1))) & 15u;
+    const float dsc = __fmul_rn(f16_to_f32(hdr.x & 0xFFFFu), (float)sc);
+    const float dm = __fmul_rn(f16_to_f32(hdr.x >> 16), (float)m);
+    return __fsub_rn(__fmul_rn(dsc, (float)code), dm);
+  }
+};
+
+template <int V> struct Span<kQ6_K, V> {
+  static constexpr int N = V / 4;
+  uint32_t ql[N + 1], qh[N + 1], sl, sh_, scw, d16, shl, shh;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
+    const uint32_t h = i0 / 128, r = i0 % 128, c = r / 32, l = r % 32;
+    const uintptr_t al = (uintptr_t)(blk + 64 * h + 32 * (c & 1) + l);
+    const uintptr_t ah = (uintptr_t)(blk + 128 + 32 * h + l);
+    const uint32_t* bl = (const uint32_t*)(al & ~(uintptr_t)3);
+    const uint32_t* bh = (const uint32_t*)(ah & ~(uintptr_t)3);
+    sl = (uint32_t)(al & 3);
+    sh_ = (uint32_t)(ah & 3);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      ql[k] = bl[k];
+      qh[k] = bh[k];
+    }
+    ql[N] = bl[sl ? N : N - 1];
+    qh[N] = bh[sh_ ? N : N - 1];
+    const uintptr_t as = (uintptr_t)(blk + 192 + i0 / 16);
+    scw = (*(const uint32_t*)(as & ~(uintptr_t)3)) >> (8 * (uint32_t)(as & 3));
+    d16 = load_u16(blk + 208);
+    shl = 4 * (c >> 1);
+    shh = 2 * c;
+  }
+  __device__ __forceinline__ float value(int i) const {
+    const uint32_t lw = __builtin_amdgcn_alignbyte(ql[i / 4 + 1], ql[i / 4], sl);
+    const uint32_t hw = __builtin_amdgcn_alignbyte(qh[i / 4 + 1], qh[i / 4], sh_);
+    const uint32_t b = 8 * (i & 3);
+    const int q = (int)((((lw >> b) >> shl) & 15u) | ((((hw >> b) >> shh) & 3u) << 4)) - 32;
+    const float dsc = __fmul_rn(f16_to_f32(d16), (float)(int8_t)(scw & 0xFFu));
+    return __fmul_rn(dsc, (float)q);
+  }
+};
+
+template <int V> struct Span<kQ2_K, V> {
+  static constexpr int N = V / 4;
+  uint32_t q[N], scw, dd, shq;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
+    const uint32_t h = i0 / 128, j = (i0 % 128) / 32, l = i0 % 32;
+    const uint32_t* qs = (const uint32_t*)(blk + 16 + 32 * h + l);
+#pragma unroll
+    for (int k = 0; k < N; ++k) q[k] = qs[k];
+    const uint32_t so = i0 / 16;
+    scw = (*(const uint32_t*)(blk + (so & ~3u))) >> (8 * (so & 3u));
+    dd = *(const uint32_t*)(blk + 80);
+    shq = 2 * j;
+  }
+  __device__ __forceinline__ float value(int i) const {
+    const uint32_t code = (q[i / 4] >> (8 * (i & 3) + shq)) & 3u;
+    const uint32_t s = scw & 0xFFu;
+    const float dsc = __fmul_rn(f16_to_f32(dd & 0xFFFFu), (float)(s & 15u));
+    const float dm = __fmul_rn(f16_to_f32(dd >> 16), (float)(s >> 4));
+    return __fsub_rn(__fmul_rn(dsc, (float)code), dm);
+  }
+};
 
 // Exact f32 value of weight i of the unit, in the literal left-to-right order
 // of the definition (used by the bit-exact dequant).

@@ -5,7 +5,8 @@ Run-time indexed register access (s_set_gpr_idx / v_movrel) is banned
 outright: a private array indexed by a loop counter was once lowered to an
 indexed register write hoisted above its bounds guard, which overwrote a store
 address and faulted the GPU.  Kernels keep every register array at
-compile-time indices instead."""
+compile-time indices instead.  Packed f32 arithmetic is kept out of the
+device code too (the build disables the packed-fp32-ops target feature)."""
 import glob
 import os
 import re
@@ -32,12 +33,16 @@ def test_device_code_has_no_indexed_registers_or_scratch(src, tmp_path):
     text = asm.read_text()
     kernel = None
     bad = []
+    packed = []
     for line in text.splitlines():
         m = re.match(r"^(_Z\w+):", line)
         if m:
             kernel = m.group(1)
         if re.search(r"\bs_set_gpr_idx_on\b|\bv_movrel", line):
             bad.append((kernel, line.strip()))
+        if re.search(r"\bv_pk_(fma|mul|add)_f32\b", line):
+            packed.append((kernel, line.strip()))
     assert not bad, f"run-time indexed register access: {bad[:4]}"
+    assert not packed, f"packed f32 arithmetic in device code: {packed[:4]}"
     scratch = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
     assert scratch and all(int(s) == 0 for s in scratch), f"private scratch in use: {scratch}"
