@@ -28,28 +28,54 @@ METRIC = "prefill projection TFLOP/s (FP16 MFMA %peak) + dequant GB/s, 8B shapes
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 WORKLOAD = "q6_k_q2_k_qwen3_8b_t2048"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tall_q6k_qwen3_8b_t2048.txt")
+# The kernel the roofline object describes: the 256-token-tile projection
+# kernel for Q6_K weights without the norm epilogue.  In the 8B layer at
+# T = 2048 it runs the o, gate, up and down projections (v has too few
+# output tiles for the tall tile and goes to the 128 x 128 kernel).
+DOMINANT = "gemm_tall_kernel<14, 0> (Q6_K, f16 X, plain f32 Y)"
+DOMINANT_PROJS = ("o", "gate", "up", "down")
+KERNEL_SOURCES = ("gemm_tall.hip", "gemm_common.h", "qp_device.h", "qp_internal.h")
 
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "qp_device.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "quantized_prefill_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic():
-    """HBM bytes per projection launch from the committed counter runs, if
-    they were taken on the current kernel source; else None."""
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary ("key: value" lines), if its counters were taken on the current
+    kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
-            rec = json.load(fh)
-    except (OSError, ValueError):
+            rec = dict(l.split(":", 1) for l in fh.read().splitlines() if ":" in l and not l.startswith("#"))
+    except OSError:
         return None
+    rec = {k.strip(): v.strip() for k, v in rec.items()}
     if rec.get("source_digest") != kernel_source_digest():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 256 MiB, three times: the byte
+    counters read on it give the scale from counter units to bytes."""
+    import torch
+    n = 256 * 1024 * 1024 // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 3}), flush=True)
 
 
 class Timer:
@@ -92,6 +118,7 @@ def build_8b(torch, synth, qp):
         for i, (name, n, k) in enumerate(synth.PROJ_8B):
             raw = synth.quant_weights(qt, n, k, synth.seed_for(2, 10 * qt + i))
             projs.append(dict(name=name, qtype=qt, n=n, k=k, w=torch.from_numpy(raw).to(dev),
+                              dom=qt == synth.Q6_K and name in DOMINANT_PROJS,
                               y=torch.empty((t, n), dtype=torch.float32, device=dev)))
     gains = {name: torch.from_numpy(synth.gains(128, synth.seed_for(2, 600 + j))).to(dev)
              for j, name in enumerate(("q", "k"))}
@@ -112,7 +139,8 @@ def step_8b(L, qp, timer):
             timer.run("gemm", lambda p=p, x=x: qp.prefill_gemm_qknorm(p["qtype"], p["w"], p["n"], p["k"], x, 128,
                                                                        L["gains"][p["name"]], 0, 1e-6, out=p["y"]))
         else:
-            timer.run("gemm", lambda p=p, x=x: qp.prefill_gemm(p["qtype"], p["w"], p["n"], p["k"], x, out=p["y"]))
+            cat = "gemm_dom" if p["dom"] else "gemm"
+            timer.run(cat, lambda p=p, x=x: qp.prefill_gemm(p["qtype"], p["w"], p["n"], p["k"], x, out=p["y"]))
 
 
 def gemm_flops_8b(L):
@@ -225,7 +253,7 @@ def cpu_baseline(synth, budget_s: float):
         return flops, time.perf_counter() - t0
 
     flops, dt = run(1)
-    ntok = int(max(1, min(64, budget_s / max(dt, 1e-3))))
+    ntok = int(max(1, min(512, budget_s / max(dt, 1e-3))))
     if ntok > 1:
         xs = {k: synth.activations_f16(ntok, k, synth.seed_for(2, 500 + k // 256)) for k in xs}
         flops, dt = run(ntok)
@@ -242,6 +270,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 256 MiB copy that calibrates the byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -255,8 +285,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU", file=sys.stderr)
         sys.exit(2)
-    qp.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    qp.lib()
     print("bench: generating the 8B-layer inputs", file=sys.stderr, flush=True)
     L = build_8b(torch, synth, qp)
     torch.cuda.synchronize()
@@ -274,12 +307,13 @@ def main():
     wall = time.perf_counter() - t0
     timer.collect()
 
-    gemm_ms = timer.total["gemm"] / args.steps
+    dom_ms = timer.total["gemm_dom"] / timer.count["gemm_dom"]   # average launch
+    dom_flops = sum(2.0 * L["t"] * p["n"] * p["k"] for p in L["projs"] if p["dom"]) / len(DOMINANT_PROJS)
+    gemm_ms = (timer.total["gemm"] + timer.total["gemm_dom"]) / args.steps
     deq_ms = (timer.total["dequant_f32"] + timer.total["dequant_f16"]) / args.steps
     flops = gemm_flops_8b(L)
     tflops = flops / gemm_ms / 1e9
     dq_gbps = dequant_bytes_8b(L, synth) / deq_ms / 1e6
-    nlaunch = len(L["projs"])
     traffic = recorded_traffic()
     res = {
         "metric": METRIC,
@@ -302,13 +336,15 @@ def main():
         "dequant_hbm_frac": round(dq_gbps / PEAK_HBM_GBPS, 4),
         "dequant_ms_per_step": round(deq_ms, 4),
         "roofline": {
-            "kernel": "gemm_kernel (all 14 projection launches)",
+            "kernel": DOMINANT,
             "bound": "mfma",
-            "achieved": round(flops / nlaunch / (gemm_ms / nlaunch) / 1e9, 2),
+            "achieved": round(dom_flops / dom_ms / 1e9, 2),
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+            "frac": round(dom_flops / dom_ms / 1e9 / PEAK_F16_TFLOPS, 4),
             "traffic": traffic,
+            "flops_per_launch": dom_flops,
+            "avg_launch_us": round(dom_ms * 1e3, 2),
         },
     }
     del L

@@ -150,3 +150,44 @@ def test_qknorm_workload(orc):
         hn = (y / np.tile(gain, n // hd)).reshape(t, n // hd, hd)
         ms = (hn.astype(np.float64) ** 2).mean(axis=2)
         assert np.allclose(ms, 1.0, atol=2e-3), f"head mean squares off: {ms.min()} {ms.max()}"
+
+
+# Shapes that take the 256-token tile (at least 512 tokens and at least 256
+# output tiles) with T and N not multiples of the tile, in padded strides.
+TALL = [(777, 8269, 512), (513, 11009, 256)]
+
+
+@pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
+@pytest.mark.parametrize("t,n,k", TALL)
+def test_tall_tile_ragged(orc, qtype, t, n, k):
+    import torch
+    say(f"gemm tall {synth.NAMES[qtype]} t={t} n={n} k={k}")
+    raw = weights(qtype, n, k, 8500 + t)
+    x = act_f16(t, k, 8501 + t)
+    ldx, ldy = k + 64, (n + 7) // 4 * 4 + 4
+    xpad = np.zeros((t, ldx), np.uint16)
+    xpad[:, :k] = x
+    xt = to_dev(xpad).view(torch.float16)
+    ybig = torch.full((t, ldy), float("nan"), device="cuda")
+    qp.check(qp.lib().qp_prefill_gemm(qtype, to_dev(raw).data_ptr(), n, k, xt.data_ptr(), qp.F16, t, ldx,
+                                      ybig.data_ptr(), ldy, None))
+    torch.cuda.synchronize()
+    yb = ybig.cpu().numpy()
+    assert np.all(np.isnan(yb[:, n:])), "wrote outside the n output columns"
+    assert_close(yb[:, :n], orc.prefill_gemm(qtype, raw, n, k, x), f"tall {synth.NAMES[qtype]} {t}x{n}x{k}")
+
+
+@pytest.mark.parametrize("hd,n", [(128, 8192), (64, 8256)])
+@pytest.mark.parametrize("qtype", [Q4_K, Q6_K], ids=["Q4_K", "Q6_K"])
+def test_qknorm_tall_tile_ragged(orc, qtype, hd, n):
+    """QK-norm epilogue on the 256-token tile: ragged T; for head_dim 64 the
+    last column tile holds a single head."""
+    t, k = 777, 512
+    say(f"qknorm tall {synth.NAMES[qtype]} t={t} n={n} hd={hd}")
+    raw = weights(qtype, n, k, 8600 + hd)
+    x = act_f16(t, k, 8601)
+    for gstride, gn in ((0, hd), (hd, n)):
+        gain = synth.gains(gn, 8602 + gstride)
+        y = run_qknorm(qtype, raw, n, k, x, hd, gain, gstride, 1e-6)
+        ref = orc.prefill_gemm_qknorm(qtype, raw, n, k, x, hd, gain, gstride, 1e-6)
+        assert_close(y, ref, f"qknorm tall {synth.NAMES[qtype]} hd={hd} stride={gstride}")
