@@ -19,16 +19,24 @@
 // role, so decode arithmetic issues beside the MFMAs.  K advances in chunks of
 // 64; per chunk:
 //   * activations 256 x 64 (binary16) go straight from global memory into an
-//     LDS ring of three buffers (16-byte direct loads issued by the consumer
-//     waves two chunks ahead);
+//     LDS ring (16-byte direct loads issued by the consumer waves one or two
+//     chunks ahead, as deep as the LDS left over by the staging area allows);
 //   * each producer thread decodes one 32-weight unit of one weight row from
 //     the LDS staging copy into the binary16 weight tile (nearest-even of the
 //     exact f32 value);
 //   * 32 MFMAs per consumer wave.
+// The staging area holds two units: while one is decoded, the producers fill
+// the other with direct global-to-LDS dword loads issued over the first two
+// chunks of the unit, and wait for them only at the barrier before the unit
+// is needed, so no chunk pays for a whole unit's load latency.
 // LDS tiles keep rows of 64 halfs (128 B) as 8 pieces of 16 B; piece p of row
-// r sits in slot p ^ (r & 7), so 16-byte fragment reads of 8 consecutive rows
-// hit 8 different bank groups.  The staging copy keeps RSD dwords per row with
-// RSD odd (dword reads of 32 rows at one offset are conflict-free).
+// r sits in slot p ^ ((r >> 1) & 7).  The LDS serves a 16-byte read for 16
+// lanes per cycle from 64 banks (256 B), i.e. two 128-byte rows: with this
+// slot order the 16 consecutive rows of a fragment read fall in 16 different
+// 16-byte bank groups (a plain p ^ (r & 7) would put rows r and r + 8 in the
+// same group and halve the read rate).  The staging copy keeps RSD dwords per
+// row with RSD odd, so dword reads of the 32 rows of a wave at one offset hit
+// distinct banks.
 #include "gemm_common.h"
 
 namespace qp {
@@ -44,18 +52,31 @@ template <> struct StageUnit<kQ6_K> { static constexpr int KW = 256, UB = 210, R
 template <> struct StageUnit<kQ2_K> { static constexpr int KW = 256, UB = 84, RSD = 21; };
 template <> struct StageUnit<kQ8_0> { static constexpr int KW = 128, UB = 136, RSD = 35; };
 
-constexpr int XBUF = 3;  // activation ring depth
+constexpr int kLdsBytes = 160 * 1024;
+// Activation ring depth: three buffers where the LDS allows, else two.
+template <int QT>
+constexpr int xbuf_of() {
+  return 3 * TBM * BK * 2 + 2 * BN * BK * 2 + 2 * BN * StageUnit<QT>::RSD * 4 <= kLdsBytes ? 3 : 2;
+}
 static_assert(BN * 21 >= 4 * TBM / 2 * 2 / 2, "staging area holds the epilogue reduction scratch");
 
 template <int QT>
 struct TallSmem {
-  _Float16 x[XBUF][TBM * BK];
+  _Float16 x[xbuf_of<QT>()][TBM * BK];
   _Float16 w[2][BN * BK];
-  uint32_t raw[BN * StageUnit<QT>::RSD];
+  uint32_t raw[2][BN * StageUnit<QT>::RSD];
 };
 
+// Workgroup barrier that waits for this wave's LDS reads and writes only.
+// __syncthreads() also orders global memory, which makes the compiler drain
+// every outstanding global load first, the direct-to-LDS copies included;
+// the main loops keep those in flight across barriers and wait for them
+// explicitly (s_waitcnt vmcnt) where their data is needed.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // LDS offset (halfs) of 16-byte piece `piece` of tile row `row`
-__device__ __forceinline__ int swz(int row, int piece) { return (row * 8 + (piece ^ (row & 7))) * 8; }
+__device__ __forceinline__ int swz_of(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int piece) { return (row * 8 + (piece ^ swz_of(row))) * 8; }
 
 // 8 dwords holding block bytes [f0, f0 + 32) of a staged row whose block
 // starts `delta` (0 or 2) bytes into its first dword.
@@ -147,6 +168,10 @@ template <int QT, int MODE>
 __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
   using SU = StageUnit<QT>;
   constexpr int RSD = SU::RSD, CPU = SU::KW / BK;  // chunks per staging unit
+  constexpr int XB = xbuf_of<QT>();
+  constexpr int NPART = CPU / 2;                    // staging is issued over the unit's first NPART chunks
+  constexpr int RPP = BN / 4 / NPART;               // rows per producer wave per part
+  static_assert(sizeof(TallSmem<QT>) <= kLdsBytes, "LDS budget");
   __shared__ __attribute__((aligned(16))) TallSmem<QT> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,23 +197,30 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
   if (!producer) {
     // ---- consumer waves -------------------------------------------------
     // Activation copy: this wave's 8 load instructions cover tile rows
-    // 64 cw + 8 q .. + 7; lane l lands in slot l & 7 of row (l >> 3), which
-    // holds piece (l & 7) ^ (l >> 3).
+    // 64 cw + 8 q .. + 7; lane l lands in slot l & 7 of row 64 cw + 8 q + (l >> 3),
+    // which holds the piece that slot order puts there.
     const int cw = role_idx;
     const _Float16* xsrc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = 64 * cw + 8 * q + (lane >> 3);
-      const int piece = (lane & 7) ^ (lane >> 3);
+      const int piece = (lane & 7) ^ swz_of(row);
       xsrc[q] = (const _Float16*)p.x + (int64_t)(m0 + min(row, m_rows - 1)) * p.ldx + 8 * piece;
     }
-    auto load_x = [&](int c) {
+    auto load_x = [&](int c) __attribute__((always_inline)) {
       c = c < nch ? c : nch - 1;
-      _Float16* dst = sm.x[c % XBUF] + 64 * cw * BK;
+      _Float16* dst = sm.x[c % XB] + 64 * cw * BK;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + 64 * c),
                                          (__attribute__((address_space(3))) void*)(dst + 8 * q * BK), 16, 0, 0);
+    };
+    // wait until the loads of every chunk but the newest XB - 2 have landed
+    auto wait_x = [&]() __attribute__((always_inline)) {
+      if constexpr (XB == 3)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
     auto frags = [&](const _Float16* xs, const _Float16* ws, int s, half8 (&a)[TMI], half8 (&b)[2]) {
       const int piece = 2 * s + (lane >> 5);
@@ -204,15 +236,15 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     };
-    load_x(0);
-    load_x(1);
-    __syncthreads();                                   // staging of the first unit
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // chunk 0 landed, chunk 1 may be in flight
-    __syncthreads();                                   // first chunk decoded
+#pragma unroll
+    for (int c = 0; c < XB - 1; ++c) load_x(c);
+    lds_barrier();  // first unit staged
+    wait_x();         // chunk 0 landed
+    lds_barrier();  // first chunk decoded
     constexpr int NF = TMI + 2, NM = 2 * TMI;
     for (int c = 0; c < nch; ++c) {
-      load_x(c + 2);
-      const _Float16* xs = sm.x[c % XBUF];
+      load_x(c + XB - 1);
+      const _Float16* xs = sm.x[c % XB];
       const _Float16* ws = sm.w[c & 1];
       half8 a0[TMI], b0[2], a1[TMI], b1[2];
       frags(xs, ws, 0, a0, b0);
@@ -223,78 +255,108 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
       frags(xs, ws, 3, a1, b1);
       mfmas(a0, b0);
       mfmas(a1, b1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);       // activation loads of chunk c + 2
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);       // activation loads of a later chunk
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF, 0);  // steps 0, 1 fragment reads
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);      // step 0 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);      // step 2 reads
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);      // step 1 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);      // step 3 reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);  // steps 2, 3 MFMAs
-      if ((c + 1) % CPU == 0 && c + 1 < nch) __syncthreads();  // next unit staged
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");         // chunk c + 1 landed
-      __syncthreads();                                          // next chunk decoded
+      __builtin_amdgcn_sched_barrier(0);                        // the waits below stay after every MFMA
+      wait_x();         // chunk c + 1 landed
+      lds_barrier();  // next chunk decoded
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
   } else {
-    // ---- producer waves: stage and decode the next chunk ----------------
-    const int pw = role_idx;        // 0..3
-    const int pt = pw * 64 + lane;  // 0..255
-    // staging copy: producer wave pw copies rows pw + 4 r (r < 32), lane = dword of the row
-    uint32_t stg[BN / 4];
-    auto stage_load = [&](int u) {
-      u = u < nunits ? u : nunits - 1;
+    // ---- producer waves: stage and decode ---------------------------------
+    const int pw = role_idx;  // 0..3
+    // Staging: part `part` of unit u is rows pw + 4 r, r in [part RPP, (part + 1) RPP),
+    // of this wave; one direct load per row puts dword `lane` of the row's unit
+    // bytes (from the dword holding its first byte) at dword `lane` of the row's
+    // slot.  Lanes past the unit's last dword load nothing.
+    // A full tile (every row inside the tensor) stages from one wave-uniform
+    // address stepping 4 rows: rows 4 apart start at the same offset within a
+    // dword (4 row strides are a multiple of 4 bytes), so the lanes and the
+    // dword count are the same for all of them and the per-row cost is a few
+    // scalar adds (the scalar unit is shared by the CU's four SIMDs).
+    const bool full_tile = n0 + BN <= p.n;
+    auto stage_part = [&](int u, int part) __attribute__((always_inline)) {
+      uint32_t* dst = sm.raw[u & 1];
+      const int64_t uoff = (int64_t)u * SU::UB;
+      if (full_tile) {
+        const uint8_t* first = p.w + (int64_t)(n0 + pw + 4 * part * RPP) * p.rb + uoff;
+        const uint32_t a = (uint32_t)((uintptr_t)first & 3);
+        const uint32_t cnt = (a + SU::UB + 3) >> 2;
+        const uint8_t* base = first - a;
+        const int64_t step = 4 * p.rb;
+        if ((uint32_t)lane < cnt) {
 #pragma unroll
-      for (int r = 0; r < BN / 4; ++r) {
-        const int n = pw + 4 * r;
-        const uint8_t* blk = p.w + (int64_t)min(n0 + n, p.n - 1) * p.rb + (int64_t)u * SU::UB;
-        const uintptr_t a = (uintptr_t)blk;
-        const uint32_t cnt = (uint32_t)(((a & 3) + SU::UB + 3) >> 2);
-        const uint32_t* src = (const uint32_t*)(a & ~(uintptr_t)3);
-        uint32_t v = 0u;
-        if ((uint32_t)lane < cnt) v = src[lane];
-        stg[r] = v;
+          for (int r = part * RPP; r < (part + 1) * RPP; ++r, base += step)
+            __builtin_amdgcn_global_load_lds((const void*)((const uint32_t*)base + lane),
+                                             (__attribute__((address_space(3))) void*)(dst + (pw + 4 * r) * RSD), 4,
+                                             0, 0);
+        }
+        return;
       }
-    };
-    auto stage_store = [&]() {
-      if (lane < RSD) {
+      const uint8_t* last = p.w + (int64_t)(p.n - 1) * p.rb + uoff;  // rows past the tensor repeat its last row
+      const uint8_t* rp = p.w + (int64_t)(n0 + pw + 4 * part * RPP) * p.rb + uoff;
+      const int64_t step = 4 * p.rb;
 #pragma unroll
-        for (int r = 0; r < BN / 4; ++r) sm.raw[(pw + 4 * r) * RSD + lane] = stg[r];
+      for (int r = part * RPP; r < (part + 1) * RPP; ++r, rp += step) {
+        const int n = pw + 4 * r;
+        const uint8_t* blk = n0 + n < p.n ? rp : last;
+        const uint32_t cnt = (uint32_t)((((uintptr_t)blk & 3) + SU::UB + 3) >> 2);
+        if ((uint32_t)lane < cnt)
+          __builtin_amdgcn_global_load_lds((const void*)(dword_floor(blk) + lane),
+                                           (__attribute__((address_space(3))) void*)(dst + n * RSD), 4, 0, 0);
       }
     };
     // decode: producer thread owns weight row pt >> 1 of the tile, 32-weight half kh
+    const int pt = pw * 64 + lane;  // 0..255
     const int wn_t = pt >> 1, kh = pt & 1;
     const uint8_t* wrow = p.w + (int64_t)min(n0 + wn_t, p.n - 1) * p.rb;
-    auto decode = [&](int c, int buf) {
+    auto decode = [&](int c, int buf) __attribute__((always_inline)) {
       const int u = c / CPU;
       const uint32_t delta = (uint32_t)(((uintptr_t)wrow + (uintptr_t)u * SU::UB) & 3);
       UnitRaw ur;
-      staged_unit<QT>(sm.raw + wn_t * RSD, delta, (uint32_t)(2 * (c % CPU) + kh), ur);
+      staged_unit<QT>(sm.raw[u & 1] + wn_t * RSD, delta, (uint32_t)(2 * (c % CPU) + kh), ur);
       uint32_t hw[16];
       unit_to_f16<QT>(ur, hw);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *(u32x4*)(sm.w[buf] + swz(wn_t, 4 * kh + q)) = (u32x4){hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]};
     };
+    // Unit u + 1 is staged while chunks of unit u are decoded: part ph after
+    // the decode of the unit's chunk ph (ph < NPART; by then the activation
+    // loads issued at the start of the chunk are mostly served), complete at
+    // its last chunk.  Its buffer last held unit u - 1, whose final decode
+    // preceded the previous barrier.
+    auto stage_next = [&](int c) __attribute__((always_inline)) {
+      const int u = c / CPU, ph = c % CPU;
+      if (ph < NPART && u + 1 < nunits) stage_part(u + 1, ph);
+    };
 
-    stage_load(0);
-    stage_store();
-    __syncthreads();  // staging of the first unit
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) stage_part(0, part);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // first unit staged
     decode(0, 0);
-    stage_load(1);
-    __syncthreads();  // first chunk decoded
+    stage_next(0);
+    lds_barrier();  // first chunk decoded
     for (int c = 0; c < nch; ++c) {
-      if ((c + 1) % CPU == 0 && c + 1 < nch) {
-        stage_store();    // every producer finished decoding the previous unit
-        __syncthreads();  // next unit staged
-        stage_load((c + 1) / CPU + 1);
+      const int nc = c + 1;
+      if (nc < nch) {
+        decode(nc, nc & 1);
+        stage_next(nc);
+        if (nc % CPU == CPU - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next unit staged
       }
-      if (c + 1 < nch) decode(c + 1, (c + 1) & 1);
-      __syncthreads();  // next chunk decoded
+      lds_barrier();  // next chunk decoded
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // reduction scratch in the staging area: no asynchronous copy writes there
-  gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw, !producer);
+  gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
 }
 
 hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p, hipStream_t s) {

@@ -54,13 +54,22 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// The dword that holds byte p, found by pointer arithmetic: an integer round
+// trip would lose the global address space the compiler infers for kernel
+// arguments and turn every load into a flat load, which also counts against
+// the LDS wait counter.
+__device__ __forceinline__ const uint32_t* dword_floor(const uint8_t* p) {
+  return (const uint32_t*)(p - ((uintptr_t)p & 3));
+}
+
 // N dwords holding bytes [p, p + 4N) of a 2-byte-aligned address p.  Only
 // 4-byte-aligned dwords that overlap [p, p + 4N) are read, so no load leaves
 // the pages that hold those bytes.
 template <int N>
 __device__ __forceinline__ void load_dw_a2(const uint8_t* p, uint32_t (&out)[N]) {
-  const uintptr_t a = (uintptr_t)p;
-  const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
+  const uint8_t* a_p = p;
+  const uintptr_t a = (uintptr_t)a_p;
+  const uint32_t* base = dword_floor(a_p);
   const uint32_t sh = (uint32_t)(a & 3);  // 0 or 2
   uint32_t d[N + 1];
 #pragma unroll
@@ -128,8 +137,9 @@ template <> struct Raw<kQ8_0> {
   uint32_t d16, w[9], sh;
   __device__ __forceinline__ void load(const uint8_t* blk, uint32_t) {
     d16 = load_u16(blk);
-    const uintptr_t a = (uintptr_t)(blk + 2);
-    const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
+    const uint8_t* a_p = blk + 2;
+    const uintptr_t a = (uintptr_t)a_p;
+    const uint32_t* base = dword_floor(a_p);
     sh = (uint32_t)(a & 3);
     load_x4(base, w);
     load_x4(base + 4, w + 4);
@@ -176,10 +186,12 @@ template <> struct Raw<kQ6_K> {
   __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
     u = u_;
     const uint32_t h = u_ >> 2, q4 = u_ & 3;
-    const uintptr_t al = (uintptr_t)(blk + 64 * h + 32 * (q4 & 1));
-    const uintptr_t ah = (uintptr_t)(blk + 128 + 32 * h);
-    const uint32_t* bl = (const uint32_t*)(al & ~(uintptr_t)3);
-    const uint32_t* bh = (const uint32_t*)(ah & ~(uintptr_t)3);
+    const uint8_t* al_p = blk + 64 * h + 32 * (q4 & 1);
+    const uintptr_t al = (uintptr_t)al_p;
+    const uint8_t* ah_p = blk + 128 + 32 * h;
+    const uintptr_t ah = (uintptr_t)ah_p;
+    const uint32_t* bl = dword_floor(al_p);
+    const uint32_t* bh = dword_floor(ah_p);
     shl_a = (uint32_t)(al & 3);
     shh_a = (uint32_t)(ah & 3);
     load_x4(bl, ql);
@@ -254,8 +266,9 @@ template <int V> struct Span<kQ8_0, V> {
   uint32_t d16, w[N + 1], sh;
   __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
     d16 = load_u16(blk);
-    const uintptr_t a = (uintptr_t)(blk + 2 + i0);
-    const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
+    const uint8_t* a_p = blk + 2 + i0;
+    const uintptr_t a = (uintptr_t)a_p;
+    const uint32_t* base = dword_floor(a_p);
     sh = (uint32_t)(a & 3);
 #pragma unroll
     for (int j = 0; j < N; ++j) w[j] = base[j];
@@ -293,10 +306,12 @@ template <int V> struct Span<kQ6_K, V> {
   uint32_t ql[N + 1], qh[N + 1], sl, sh_, scw, d16, shl, shh;
   __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
     const uint32_t h = i0 / 128, r = i0 % 128, c = r / 32, l = r % 32;
-    const uintptr_t al = (uintptr_t)(blk + 64 * h + 32 * (c & 1) + l);
-    const uintptr_t ah = (uintptr_t)(blk + 128 + 32 * h + l);
-    const uint32_t* bl = (const uint32_t*)(al & ~(uintptr_t)3);
-    const uint32_t* bh = (const uint32_t*)(ah & ~(uintptr_t)3);
+    const uint8_t* al_p = blk + 64 * h + 32 * (c & 1) + l;
+    const uintptr_t al = (uintptr_t)al_p;
+    const uint8_t* ah_p = blk + 128 + 32 * h + l;
+    const uintptr_t ah = (uintptr_t)ah_p;
+    const uint32_t* bl = dword_floor(al_p);
+    const uint32_t* bh = dword_floor(ah_p);
     sl = (uint32_t)(al & 3);
     sh_ = (uint32_t)(ah & 3);
 #pragma unroll
@@ -306,8 +321,9 @@ template <int V> struct Span<kQ6_K, V> {
     }
     ql[N] = bl[sl ? N : N - 1];
     qh[N] = bh[sh_ ? N : N - 1];
-    const uintptr_t as = (uintptr_t)(blk + 192 + i0 / 16);
-    scw = (*(const uint32_t*)(as & ~(uintptr_t)3)) >> (8 * (uint32_t)(as & 3));
+    const uint8_t* as_p = blk + 192 + i0 / 16;
+    const uintptr_t as = (uintptr_t)as_p;
+    scw = (*dword_floor(as_p)) >> (8 * (uint32_t)(as & 3));
     d16 = load_u16(blk + 208);
     shl = 4 * (c >> 1);
     shh = 2 * c;

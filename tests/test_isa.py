@@ -6,7 +6,10 @@ outright: a private array indexed by a loop counter was once lowered to an
 indexed register write hoisted above its bounds guard, which overwrote a store
 address and faulted the GPU.  Kernels keep every register array at
 compile-time indices instead.  Packed f32 arithmetic is kept out of the
-device code too (the build disables the packed-fp32-ops target feature)."""
+device code too (the build disables the packed-fp32-ops target feature).
+Global memory is read and written with global (or buffer) instructions, never
+flat ones: a flat load also counts against the LDS wait counter, so every LDS
+wait after it waits for HBM as well."""
 import glob
 import os
 import re
@@ -34,6 +37,7 @@ def test_device_code_has_no_indexed_registers_or_scratch(src, tmp_path):
     kernel = None
     bad = []
     packed = []
+    flat = []
     for line in text.splitlines():
         m = re.match(r"^(_Z\w+):", line)
         if m:
@@ -42,7 +46,10 @@ def test_device_code_has_no_indexed_registers_or_scratch(src, tmp_path):
             bad.append((kernel, line.strip()))
         if re.search(r"\bv_pk_(fma|mul|add)_f32\b", line):
             packed.append((kernel, line.strip()))
+        if re.search(r"\bflat_(load|store|atomic)", line):
+            flat.append((kernel, line.strip()))
     assert not bad, f"run-time indexed register access: {bad[:4]}"
     assert not packed, f"packed f32 arithmetic in device code: {packed[:4]}"
+    assert not flat, f"flat memory instructions in device code: {flat[:4]}"
     scratch = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
     assert scratch and all(int(s) == 0 for s in scratch), f"private scratch in use: {scratch}"
