@@ -311,9 +311,12 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
                                            (__attribute__((address_space(3))) void*)(dst + n * RSD), 4, 0, 0);
       }
     };
-    // decode: producer thread owns weight row pt >> 1 of the tile, 32-weight half kh
+    // decode: producer thread owns weight row pt & 127 of the tile, 32-weight
+    // half kh = pt >> 7, so the 64 lanes of a wave read 64 different staged
+    // rows at one offset, which an odd row pitch spreads over all 64 banks
+    // (two lanes per row would read 8 dwords apart, and some row pairs collide).
     const int pt = pw * 64 + lane;  // 0..255
-    const int wn_t = pt >> 1, kh = pt & 1;
+    const int wn_t = pt & 127, kh = pt >> 7;
     const uint8_t* wrow = p.w + (int64_t)min(n0 + wn_t, p.n - 1) * p.rb;
     auto decode = [&](int c, int buf) __attribute__((always_inline)) {
       const int u = c / CPU;
