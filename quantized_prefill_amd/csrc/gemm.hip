@@ -195,10 +195,11 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
 }
 
 // Token-tile height: 256 halves the decode work per flop and is used when the
-// launch still fills the 256 CUs with one 256-token tile each.
-static bool use_tall_tiles(int64_t n, int64_t t) {
+// launch still fills the 256 CUs with one 256-token tile each.  The tall
+// kernel addresses a tile's activation rows with 32-bit byte offsets.
+static bool use_tall_tiles(int64_t n, int64_t t, int64_t ldx) {
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + 255) / 256);
-  return t >= 512 && tiles >= 256;
+  return t >= 512 && tiles >= 256 && 256 * ldx * 2 < ((int64_t)1 << 31);
 }
 
 hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
@@ -213,7 +214,7 @@ hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const voi
   p.t = (int)t;
   p.y = y;
   p.ldy = ldy;
-  if (!x_f32 && use_tall_tiles(n, t)) {
+  if (!x_f32 && use_tall_tiles(n, t, ldx)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
   }
@@ -238,7 +239,7 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   p.gstride = gain_head_stride;
   p.hd = (int)head_dim;
   p.eps = eps;
-  if (use_tall_tiles(n, t)) {
+  if (use_tall_tiles(n, t, ldx)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kQkNorm, grid, p, s);
   }

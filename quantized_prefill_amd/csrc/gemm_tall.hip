@@ -72,7 +72,12 @@ struct TallSmem {
 // every outstanding global load first, the direct-to-LDS copies included;
 // the main loops keep those in flight across barriers and wait for them
 // explicitly (s_waitcnt vmcnt) where their data is needed.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The explicit wait is the builtin, so the compiler's own wait placement
+// knows that every LDS read issued before the barrier has returned.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // LDS offset (halfs) of 16-byte piece `piece` of tile row `row`
 __device__ __forceinline__ int swz_of(int row) { return (row >> 1) & 7; }
@@ -200,19 +205,20 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
     // 64 cw + 8 q .. + 7; lane l lands in slot l & 7 of row 64 cw + 8 q + (l >> 3),
     // which holds the piece that slot order puts there.
     const int cw = role_idx;
-    const _Float16* xsrc[8];
+    const _Float16* xtile = (const _Float16*)p.x + (int64_t)m0 * p.ldx;  // tile row 0
+    uint32_t xoff[8];  // halfs from xtile (a tile spans under 2^30 halfs)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = 64 * cw + 8 * q + (lane >> 3);
       const int piece = (lane & 7) ^ swz_of(row);
-      xsrc[q] = (const _Float16*)p.x + (int64_t)(m0 + min(row, m_rows - 1)) * p.ldx + 8 * piece;
+      xoff[q] = (uint32_t)(min(row, m_rows - 1) * p.ldx + 8 * piece);
     }
     auto load_x = [&](int c) __attribute__((always_inline)) {
       c = c < nch ? c : nch - 1;
       _Float16* dst = sm.x[c % XB] + 64 * cw * BK;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + 64 * c),
+        __builtin_amdgcn_global_load_lds((const void*)(xtile + (xoff[q] + 64 * c)),
                                          (__attribute__((address_space(3))) void*)(dst + 8 * q * BK), 16, 0, 0);
     };
     // wait until the loads of every chunk but the newest XB - 2 have landed
@@ -242,29 +248,46 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
     wait_x();         // chunk 0 landed
     lds_barrier();  // first chunk decoded
     constexpr int NF = TMI + 2, NM = 2 * TMI;
+    // Rotated loop: the barrier that hands over chunk c + 1 sits after the
+    // last fragment reads of chunk c, and the reads of chunk c + 1's steps 0
+    // and 1 go out right after it, between the MFMAs of chunk c's steps 2 and
+    // 3, so the matrix unit does not wait for LDS at the start of a chunk.
+    // Buffers stay safe: the next writes to chunk c's X and W slots are issued
+    // after that barrier, which every wave passes only once all of its reads
+    // of chunk c have returned.  (After the last chunk the reads fetch unused
+    // values from in-bounds LDS.)
+    half8 a0[TMI], b0[2], a1[TMI], b1[2];  // steps 0 and 1 of the current chunk
+    frags(sm.x[0], sm.w[0], 0, a0, b0);
+    frags(sm.x[0], sm.w[0], 1, a1, b1);
     for (int c = 0; c < nch; ++c) {
       load_x(c + XB - 1);
       const _Float16* xs = sm.x[c % XB];
       const _Float16* ws = sm.w[c & 1];
-      half8 a0[TMI], b0[2], a1[TMI], b1[2];
-      frags(xs, ws, 0, a0, b0);
-      frags(xs, ws, 1, a1, b1);
+      half8 a2[TMI], b2[2], a3[TMI], b3[2];
       mfmas(a0, b0);
-      frags(xs, ws, 2, a0, b0);
+      frags(xs, ws, 2, a2, b2);
       mfmas(a1, b1);
-      frags(xs, ws, 3, a1, b1);
-      mfmas(a0, b0);
-      mfmas(a1, b1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);       // activation loads of a later chunk
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF, 0);  // steps 0, 1 fragment reads
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);      // step 0 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);      // step 2 reads
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);      // step 1 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);      // step 3 reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);  // steps 2, 3 MFMAs
-      __builtin_amdgcn_sched_barrier(0);                        // the waits below stay after every MFMA
+      frags(xs, ws, 3, a3, b3);
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);   // activation loads of a later chunk
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 0 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // step 2 reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 1 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // step 3 reads
+      __builtin_amdgcn_sched_barrier(0);
       wait_x();         // chunk c + 1 landed
-      lds_barrier();  // next chunk decoded
+      lds_barrier();    // chunk c + 1 decoded; this wave's reads of chunk c are done
+      __builtin_amdgcn_sched_barrier(0);
+      const _Float16* xn = sm.x[(c + 1) % XB];
+      const _Float16* wnx = sm.w[(c + 1) & 1];
+      frags(xn, wnx, 0, a0, b0);
+      mfmas(a2, b2);
+      frags(xn, wnx, 1, a1, b1);
+      mfmas(a3, b3);
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // next chunk's step 0 reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 2 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // next chunk's step 1 reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 3 MFMAs
+      __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
   } else {

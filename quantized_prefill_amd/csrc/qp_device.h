@@ -382,7 +382,32 @@ template <int QT> __device__ __forceinline__ float unit_value_exact(const UnitRa
 // zero: the product is exact, so the fma rounds once, like the subtraction).
 // Q8_0 codes are biased by 128 (A*(code^0x80) - 128*A) to use the unsigned
 // byte converts.  Used where the result feeds a binary16 operand.
+//
+// Q6_K and Q8_0 (no min) take a shorter route: a byte permute turns two codes
+// c into the binary16 numbers 1024 + c (exponent 10, c in the mantissa), and
+// a mixed-precision fma A * (1024 + c) - (1024 + bias) * A = A * (c - bias)
+// writes each binary16 result straight into its half of the output word.
+// Every term is exact in f32 ((1024 + bias) * A has at most 24 significant
+// bits), so the fma's only rounding is the one to binary16.
 template <int QT> __device__ __forceinline__ void unit_to_f16(const UnitRaw& r, uint32_t (&out)[16]) {
+  if constexpr (QT == kQ6_K || QT == kQ8_0) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    constexpr float kBias = QT == kQ6_K ? 32.f : 128.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t c = r.code[j];
+      if constexpr (QT == kQ8_0) c ^= 0x80808080u;  // int8 q -> q + 128
+      const float a = j < 4 ? r.a0 : r.a1;
+      const float cc = -__fmul_rn(a, 1024.f + kBias);
+      const h2 x01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, c, 0x07010700u));
+      const h2 x23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, c, 0x07030702u));
+      const h2 r01 = {(_Float16)__builtin_fmaf(a, (float)x01[0], cc), (_Float16)__builtin_fmaf(a, (float)x01[1], cc)};
+      const h2 r23 = {(_Float16)__builtin_fmaf(a, (float)x23[0], cc), (_Float16)__builtin_fmaf(a, (float)x23[1], cc)};
+      out[2 * j] = __builtin_bit_cast(uint32_t, r01);
+      out[2 * j + 1] = __builtin_bit_cast(uint32_t, r23);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t c = r.code[j];
