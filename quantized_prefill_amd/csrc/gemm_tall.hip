@@ -37,6 +37,8 @@
 // same group and halve the read rate).  The staging copy keeps RSD dwords per
 // row with RSD odd, so dword reads of the 32 rows of a wave at one offset hit
 // distinct banks.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace qp {
@@ -174,8 +176,10 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
   using SU = StageUnit<QT>;
   constexpr int RSD = SU::RSD, CPU = SU::KW / BK;  // chunks per staging unit
   constexpr int XB = xbuf_of<QT>();
-  constexpr int NPART = CPU / 2;                    // staging is issued over the unit's first NPART chunks
-  constexpr int RPP = BN / 4 / NPART;               // rows per producer wave per part
+  // staging of the next unit is issued over the first NPART chunks of a unit
+  // (all but its last chunk, at most three), each part a slice of the 32 rows
+  // of a producer wave
+  constexpr int NPART = CPU >= 4 ? 3 : 1;
   static_assert(sizeof(TallSmem<QT>) <= kLdsBytes, "LDS budget");
   __shared__ __attribute__((aligned(16))) TallSmem<QT> sm;
   const int tid = threadIdx.x;
@@ -293,28 +297,29 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
   } else {
     // ---- producer waves: stage and decode ---------------------------------
     const int pw = role_idx;  // 0..3
-    // Staging: part `part` of unit u is rows pw + 4 r, r in [part RPP, (part + 1) RPP),
-    // of this wave; one direct load per row puts dword `lane` of the row's unit
-    // bytes (from the dword holding its first byte) at dword `lane` of the row's
-    // slot.  Lanes past the unit's last dword load nothing.
+    // Staging: rows pw + 4 r, r in [R0, R1), of unit u; one direct load per
+    // row puts dword `lane` of the row's unit bytes (from the dword holding its
+    // first byte) at dword `lane` of the row's slot.  Lanes past the unit's
+    // last dword load nothing.
     // A full tile (every row inside the tensor) stages from one wave-uniform
     // address stepping 4 rows: rows 4 apart start at the same offset within a
     // dword (4 row strides are a multiple of 4 bytes), so the lanes and the
     // dword count are the same for all of them and the per-row cost is a few
     // scalar adds (the scalar unit is shared by the CU's four SIMDs).
     const bool full_tile = n0 + BN <= p.n;
-    auto stage_part = [&](int u, int part) __attribute__((always_inline)) {
+    auto stage_rows = [&](int u, auto r0c, auto r1c) __attribute__((always_inline)) {
+      constexpr int R0 = decltype(r0c)::value, R1 = decltype(r1c)::value;
       uint32_t* dst = sm.raw[u & 1];
       const int64_t uoff = (int64_t)u * SU::UB;
+      const int64_t step = 4 * p.rb;
       if (full_tile) {
-        const uint8_t* first = p.w + (int64_t)(n0 + pw + 4 * part * RPP) * p.rb + uoff;
+        const uint8_t* first = p.w + (int64_t)(n0 + pw + 4 * R0) * p.rb + uoff;
         const uint32_t a = (uint32_t)((uintptr_t)first & 3);
         const uint32_t cnt = (a + SU::UB + 3) >> 2;
         const uint8_t* base = first - a;
-        const int64_t step = 4 * p.rb;
         if ((uint32_t)lane < cnt) {
 #pragma unroll
-          for (int r = part * RPP; r < (part + 1) * RPP; ++r, base += step)
+          for (int r = R0; r < R1; ++r, base += step)
             __builtin_amdgcn_global_load_lds((const void*)((const uint32_t*)base + lane),
                                              (__attribute__((address_space(3))) void*)(dst + (pw + 4 * r) * RSD), 4,
                                              0, 0);
@@ -322,10 +327,9 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
         return;
       }
       const uint8_t* last = p.w + (int64_t)(p.n - 1) * p.rb + uoff;  // rows past the tensor repeat its last row
-      const uint8_t* rp = p.w + (int64_t)(n0 + pw + 4 * part * RPP) * p.rb + uoff;
-      const int64_t step = 4 * p.rb;
+      const uint8_t* rp = p.w + (int64_t)(n0 + pw + 4 * R0) * p.rb + uoff;
 #pragma unroll
-      for (int r = part * RPP; r < (part + 1) * RPP; ++r, rp += step) {
+      for (int r = R0; r < R1; ++r, rp += step) {
         const int n = pw + 4 * r;
         const uint8_t* blk = n0 + n < p.n ? rp : last;
         const uint32_t cnt = (uint32_t)((((uintptr_t)blk & 3) + SU::UB + 3) >> 2);
@@ -334,6 +338,10 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
                                            (__attribute__((address_space(3))) void*)(dst + n * RSD), 4, 0, 0);
       }
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, BN / 4 * 1 / NPART>;
+    using I2 = std::integral_constant<int, BN / 4 * 2 / NPART>;
+    using IE = std::integral_constant<int, BN / 4>;
     // decode: producer thread owns weight row pt & 127 of the tile, 32-weight
     // half kh = pt >> 7, so the 64 lanes of a wave read 64 different staged
     // rows at one offset, which an odd row pitch spreads over all 64 banks
@@ -359,11 +367,21 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
     // preceded the previous barrier.
     auto stage_next = [&](int c) __attribute__((always_inline)) {
       const int u = c / CPU, ph = c % CPU;
-      if (ph < NPART && u + 1 < nunits) stage_part(u + 1, ph);
+      if (u + 1 >= nunits) return;
+      if constexpr (NPART == 1) {
+        if (ph == 0) stage_rows(u + 1, I0{}, IE{});
+      } else {
+        static_assert(NPART == 3, "three staging parts");
+        if (ph == 0)
+          stage_rows(u + 1, I0{}, I1{});
+        else if (ph == 1)
+          stage_rows(u + 1, I1{}, I2{});
+        else if (ph == 2)
+          stage_rows(u + 1, I2{}, IE{});
+      }
     };
 
-#pragma unroll
-    for (int part = 0; part < NPART; ++part) stage_part(0, part);
+    stage_rows(0, I0{}, IE{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();  // first unit staged
     decode(0, 0);
