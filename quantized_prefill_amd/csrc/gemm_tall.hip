@@ -217,15 +217,17 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
       const int piece = (lane & 7) ^ swz_of(row);
       xoff[q] = (uint32_t)(min(row, m_rows - 1) * p.ldx + 8 * piece);
     }
-    auto load_x = [&](int c) __attribute__((always_inline)) {
+    // load q (of 8) of this wave's share of chunk c (past the end: the last chunk again)
+    auto load_xq = [&](int c, int q) __attribute__((always_inline)) {
       c = c < nch ? c : nch - 1;
-      _Float16* dst = sm.x[c % XB] + 64 * cw * BK;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(xtile + (xoff[q] + 64 * c)),
-                                         (__attribute__((address_space(3))) void*)(dst + 8 * q * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(xtile + (xoff[q] + 64 * c)),
+                                       (__attribute__((address_space(3))) void*)(sm.x[c % XB] + (64 * cw + 8 * q) * BK),
+                                       16, 0, 0);
     };
-    // wait until the loads of every chunk but the newest XB - 2 have landed
+    // Chunk j goes to buffer j % XB and is loaded right after the barrier
+    // that ends the reads of chunk j - XB (the prologue loads chunks
+    // 0 .. XB - 1).  Waiting for chunk c + 1 at the end of chunk c leaves the
+    // loads of chunks c + 2 .. c + XB - 1 in flight.
     auto wait_x = [&]() __attribute__((always_inline)) {
       if constexpr (XB == 3)
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
@@ -246,10 +248,29 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     };
+    // The same MFMAs, each followed by one activation load of chunk cl: a
+    // load's issue can stall on a full address queue, which costs nothing
+    // while the MFMA before it runs.  (The loads sit here in program order:
+    // the compiler does not move direct-to-LDS loads past LDS reads.)
+    auto mfmas_loading = [&](const half8 (&a)[TMI], const half8 (&b)[2], int cl) {
+      static_assert(2 * TMI == 8, "one activation load per MFMA of a step");
 #pragma unroll
-    for (int c = 0; c < XB - 1; ++c) load_x(c);
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+          load_xq(cl, 2 * i + j);
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < XB; ++c)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) load_xq(c, q);
     lds_barrier();  // first unit staged
-    wait_x();         // chunk 0 landed
+    if constexpr (XB == 3)  // chunk 0 landed
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     lds_barrier();  // first chunk decoded
     constexpr int NF = TMI + 2, NM = 2 * TMI;
     // Rotated loop: the barrier that hands over chunk c + 1 sits after the
@@ -264,7 +285,6 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
     frags(sm.x[0], sm.w[0], 0, a0, b0);
     frags(sm.x[0], sm.w[0], 1, a1, b1);
     for (int c = 0; c < nch; ++c) {
-      load_x(c + XB - 1);
       const _Float16* xs = sm.x[c % XB];
       const _Float16* ws = sm.w[c & 1];
       half8 a2[TMI], b2[2], a3[TMI], b3[2];
@@ -272,7 +292,6 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
       frags(xs, ws, 2, a2, b2);
       mfmas(a1, b1);
       frags(xs, ws, 3, a3, b3);
-      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);   // activation loads of a later chunk
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 0 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // step 2 reads
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 1 MFMAs
@@ -284,11 +303,15 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
       const _Float16* xn = sm.x[(c + 1) % XB];
       const _Float16* wnx = sm.w[(c + 1) & 1];
       frags(xn, wnx, 0, a0, b0);
-      mfmas(a2, b2);
+      mfmas_loading(a2, b2, c + XB);  // chunk c's buffer is free: load chunk c + XB
       frags(xn, wnx, 1, a1, b1);
       mfmas(a3, b3);
       __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // next chunk's step 0 reads
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 2 MFMAs
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {                        // step 2 MFMAs, each followed by
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an activation load
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // next chunk's step 1 reads
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // step 3 MFMAs
       __builtin_amdgcn_sched_barrier(0);
