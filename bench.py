@@ -253,8 +253,11 @@ def cpu_baseline(synth, budget_s: float):
         return flops, time.perf_counter() - t0
 
     flops, dt = run(1)
-    ntok = int(max(1, min(512, budget_s / max(dt, 1e-3))))
-    if ntok > 1:
+    ntok = 1
+    # grow the sample until it takes about half the budget or more (the
+    # per-token cost falls as the dequant of each weight is shared)
+    while dt < 0.5 * budget_s and ntok < 512:
+        ntok = int(max(ntok + 1, min(512, ntok * budget_s / max(dt, 1e-3))))
         xs = {k: synth.activations_f16(ntok, k, synth.seed_for(2, 500 + k // 256)) for k in xs}
         flops, dt = run(ntok)
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=orc.num_threads(), kind="oracle",
