@@ -3,9 +3,10 @@
 One step is one pass of the path over one Qwen3-8B-shaped layer at T = 2048
 prompt tokens, in both Q6_K and Q2_K: the f32 and f16 dequant of every
 projection weight (q, k, v, o, gate, up, down), then every projection
-Y = X . W^T with W dequantized on load (q and k through the per-head QK-norm
-epilogue).  Inputs are seeded synthetic tensors resident in HBM before timing
-starts.  `value` is the projection TFLOP/s (sum of algorithmic flops over the
+Y = X . W^T with W dequantized on load: q, k (through the per-head QK-norm
+epilogue) and v in one call over their shared X, then o, gate, up and down.
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+`value` is the projection TFLOP/s (sum of algorithmic flops over the
 sum of the projection launches' HIP-event durations); the dequant GB/s is
 reported beside it.  After the timed region the remaining workloads -- the
 Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the fused
@@ -125,7 +126,7 @@ def build_8b(torch, synth, qp):
     maxw = max(p["n"] * p["k"] for p in projs)
     d32 = torch.empty(maxw, dtype=torch.float32, device=dev)
     d16 = torch.empty(maxw, dtype=torch.float16, device=dev)
-    return dict(t=t, hidden=hidden, xs=xs, projs=projs, gains=gains, d32=d32, d16=d16)
+    return dict(t=t, hidden=hidden, xs=xs, projs=projs, gains=gains, d32=d32, d16=d16, qtypes=(synth.Q6_K, synth.Q2_K))
 
 
 def step_8b(L, qp, timer):
@@ -133,14 +134,18 @@ def step_8b(L, qp, timer):
         n, k = p["n"], p["k"]
         timer.run("dequant_f32", lambda p=p: qp.dequant_f32(p["qtype"], p["w"], n, k, out=L["d32"][:n * k].view(n, k)))
         timer.run("dequant_f16", lambda p=p: qp.dequant_f16(p["qtype"], p["w"], n, k, out=L["d16"][:n * k].view(n, k)))
-    for p in L["projs"]:
-        x = L["xs"][p["k"]]
-        if p["name"] in ("q", "k"):
-            timer.run("gemm", lambda p=p, x=x: qp.prefill_gemm_qknorm(p["qtype"], p["w"], p["n"], p["k"], x, 128,
-                                                                       L["gains"][p["name"]], 0, 1e-6, out=p["y"]))
-        else:
+    for qt in L["qtypes"]:
+        pr = {p["name"]: p for p in L["projs"] if p["qtype"] == qt}
+        q, k, v = pr["q"], pr["k"], pr["v"]
+        x = L["xs"][q["k"]]
+        # q and k with the per-head RMSNorm and v, one call over the shared X
+        timer.run("gemm", lambda q=q, k=k, v=v, x=x: qp.prefill_gemm_qkv(
+            qt, q["w"], q["n"], k["w"], k["n"], v["w"], v["n"], q["k"], x, 128, L["gains"]["q"], L["gains"]["k"],
+            out_q=q["y"], out_k=k["y"], out_v=v["y"]))
+        for name in ("o", "gate", "up", "down"):
+            p = pr[name]
             cat = "gemm_dom" if p["dom"] else "gemm"
-            timer.run(cat, lambda p=p, x=x: qp.prefill_gemm(p["qtype"], p["w"], p["n"], p["k"], x, out=p["y"]))
+            timer.run(cat, lambda p=p: qp.prefill_gemm(p["qtype"], p["w"], p["n"], p["k"], L["xs"][p["k"]], out=p["y"]))
 
 
 def gemm_flops_8b(L):

@@ -140,6 +140,27 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
                                  hipStream_t stream);
 
 /*
+ * The attention-input projections of one chunk in one call ("What changes":
+ * batched prefill of QK-norm models in FP16, the per-head RMSNorm on Q and K):
+ *   y_q = the qp_prefill_gemm_qknorm result for (w_q, n_q, gain_q, gain_q_stride)
+ *   y_k = the qp_prefill_gemm_qknorm result for (w_k, n_k, gain_k, gain_k_stride)
+ *   y_v = the qp_prefill_gemm result for (w_v, n_v) with binary16 x
+ * over the same x (T x K binary16, row stride ldx), with one qtype, k,
+ * head_dim and eps.  When the three projections' output tiles together fill
+ * the GPU this is a single launch (k and v alone often do not: 1024 outputs
+ * at T = 2048 make 64 tiles); otherwise it is the three calls.  Results match
+ * the separate calls within the GEMM tolerance (summation order may differ).
+ * n_v == 0 leaves v out (w_v, y_v unused).  The three outputs must not
+ * overlap.  Requirements and errors are those of the two calls for each
+ * projection.
+ */
+qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const void* w_k, int64_t n_k,
+                              const void* w_v, int64_t n_v, int64_t k, const uint16_t* x, int64_t t, int64_t ldx,
+                              int64_t head_dim, const float* gain_q, int64_t gain_q_stride, const float* gain_k,
+                              int64_t gain_k_stride, float eps, float* y_q, int64_t ldy_q, float* y_k, int64_t ldy_k,
+                              float* y_v, int64_t ldy_v, hipStream_t stream);
+
+/*
  * Router of a routed-expert layer ("Correctness and safety": routing ids,
  * expert selection and route weights):  for each token t,
  * p = softmax(logits[t, :]) over n_experts; the top_k experts by logit,

@@ -29,6 +29,8 @@ SIGNATURES = {
     "qp_prefill_gemm": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP]),
     "qp_prefill_gemm_qknorm": (_INT, [_INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64, _F32C, _VP, _I64,
                                       _VP]),
+    "qp_prefill_gemm_qkv": (_INT, [_INT, _VP, _I64, _VP, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64,
+                                   _VP, _I64, _F32C, _VP, _I64, _VP, _I64, _VP, _I64, _VP]),
     "qp_moe_route_topk": (_INT, [_VP, _I64, _I64, _I64, _INT, _VP, _VP, _VP]),
     "qp_grouped_expert_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "qp_grouped_expert_gemm": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP, _VP,
@@ -149,6 +151,28 @@ def prefill_gemm_qknorm(qtype: int, w, n: int, k: int, x, head_dim: int, gain, g
                                        _dev(gain, "gain"), gain_head_stride, float(eps), out.data_ptr(),
                                        out.stride(0), _stream()))
     return out
+
+
+def prefill_gemm_qkv(qtype: int, w_q, n_q: int, w_k, n_k: int, w_v, n_v: int, k: int, x, head_dim: int,
+                     gain_q, gain_k, gain_q_stride: int = 0, gain_k_stride: int = 0, eps: float = 1e-6,
+                     out_q=None, out_k=None, out_v=None):
+    """q and k with the per-head RMSNorm, v plain, over one float16 x, in one call."""
+    torch = _torch()
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor with unit column stride")
+    t = x.shape[0]
+    outs = []
+    for o, n in ((out_q, n_q), (out_k, n_k), (out_v, n_v)):
+        outs.append(o if o is not None else torch.empty((t, max(n, 1)), dtype=torch.float32, device=x.device))
+    check(lib().qp_prefill_gemm_qkv(qtype, _dev(w_q, "w_q"), n_q, _dev(w_k, "w_k"), n_k,
+                                    _dev(w_v, "w_v") if n_v else None, n_v, k, x.data_ptr(), t, x.stride(0),
+                                    head_dim, _dev(gain_q, "gain_q"), gain_q_stride, _dev(gain_k, "gain_k"),
+                                    gain_k_stride, float(eps), outs[0].data_ptr(), outs[0].stride(0),
+                                    outs[1].data_ptr(), outs[1].stride(0), outs[2].data_ptr(), outs[2].stride(0),
+                                    _stream()))
+    return tuple(outs)
 
 
 def moe_route_topk(logits, top_k: int, renorm: bool = False, ids=None, weights=None):

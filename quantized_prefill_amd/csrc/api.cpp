@@ -134,6 +134,38 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
                   "gemm_qknorm launch");
 }
 
+qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const void* w_k, int64_t n_k,
+                              const void* w_v, int64_t n_v, int64_t k, const uint16_t* x, int64_t t, int64_t ldx,
+                              int64_t head_dim, const float* gain_q, int64_t gain_q_stride, const float* gain_k,
+                              int64_t gain_k_stride, float eps, float* y_q, int64_t ldy_q, float* y_k, int64_t ldy_k,
+                              float* y_v, int64_t ldy_v, hipStream_t stream) {
+  if (n_v < 0) return fail(QP_ERR_INVALID_PARAMETER, "n_v=%lld must be >= 0", (long long)n_v);
+  qp_status st = gemm_checks(qtype, w_q, n_q, k, x, t, ldx, 2, y_q, ldy_q);
+  if (st != QP_OK) return st;
+  st = gemm_checks(qtype, w_k, n_k, k, x, t, ldx, 2, y_k, ldy_k);
+  if (st != QP_OK) return st;
+  if (n_v > 0) {
+    st = gemm_checks(qtype, w_v, n_v, k, x, t, ldx, 2, y_v, ldy_v);
+    if (st != QP_OK) return st;
+  }
+  if (head_dim != 64 && head_dim != 128)
+    return fail(QP_ERR_INVALID_PARAMETER, "head_dim=%lld must be 64 or 128", (long long)head_dim);
+  if (n_q % head_dim != 0 || n_k % head_dim != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "n_q and n_k must be multiples of head_dim");
+  if (!(eps > 0.f) || !isfinite(eps)) return fail(QP_ERR_INVALID_PARAMETER, "eps must be finite and > 0");
+  if (gain_q_stride < 0 || gain_k_stride < 0) return fail(QP_ERR_INVALID_PARAMETER, "gain strides must be >= 0");
+  if (t == 0) return ok();
+  if (!gain_q || !gain_k) return fail(QP_ERR_INVALID_PARAMETER, "null gain");
+  const void* w[3] = {w_q, w_k, w_v};
+  const int64_t n[3] = {n_q, n_k, n_v};
+  const float* gain[3] = {gain_q, gain_k, nullptr};
+  const int64_t gstride[3] = {gain_q_stride, gain_k_stride, 0};
+  float* y[3] = {y_q, y_k, y_v};
+  const int64_t ldy[3] = {ldy_q, ldy_k, ldy_v};
+  return from_hip(qp::launch_gemm_qkv(qtype, w, n, k, x, t, ldx, head_dim, gain, gstride, eps, y, ldy, stream),
+                  "gemm_qkv launch");
+}
+
 qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k, int renorm,
                             int32_t* ids, float* weights, hipStream_t stream) {
   if (t < 0 || t > kMaxDim || n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > n_experts || top_k > 64)

@@ -247,6 +247,54 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   return launch_mode<kQkNorm>(qtype, grid, p, s);
 }
 
+// q, k and v over one X: when their output tiles together fill the GPU with
+// tall tiles, one launch covers all three (each tile resolves its projection
+// from its column index); otherwise three ordinary launches.
+hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3], int64_t k, const uint16_t* x,
+                           int64_t t, int64_t ldx, int64_t head_dim, const float* const gain[3],
+                           const int64_t gstride[3], float eps, float* const y[3], const int64_t ldy[3],
+                           hipStream_t s) {
+  int64_t ntiles = 0;
+  for (int i = 0; i < 3; ++i) ntiles += (n[i] + BN - 1) / BN;
+  const bool fused = t >= 512 && ntiles * ((t + 255) / 256) >= 256 && 256 * ldx * 2 < ((int64_t)1 << 31);
+  if (!fused) {
+    for (int i = 0; i < 3; ++i) {
+      if (n[i] == 0) continue;
+      hipError_t e = i < 2 ? launch_gemm_qknorm(qtype, w[i], n[i], k, x, t, ldx, head_dim, gain[i], gstride[i], eps,
+                                                y[i], ldy[i], s)
+                           : launch_gemm(qtype, w[i], n[i], k, x, false, t, ldx, y[i], ldy[i], s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GemmParams p = {};
+  p.rb = row_bytes_of(qtype, k);
+  p.k = (int)k;
+  p.x = x;
+  p.ldx = ldx;
+  p.t = (int)t;
+  p.hd = (int)head_dim;
+  p.eps = eps;
+  int nseg = 0, tile = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] == 0) continue;
+    p.seg.tile0[nseg] = tile;
+    p.seg.w[nseg] = (const uint8_t*)w[i];
+    p.seg.n[nseg] = (int)n[i];
+    p.seg.y[nseg] = y[i];
+    p.seg.ldy[nseg] = ldy[i];
+    p.seg.gain[nseg] = gain[i];
+    p.seg.gstride[nseg] = gstride[i];
+    p.seg.norm[nseg] = i < 2;
+    tile += (int)((n[i] + BN - 1) / BN);
+    ++nseg;
+  }
+  p.seg.nseg = nseg;
+  for (int i = nseg; i <= kMaxSeg; ++i) p.seg.tile0[i] = tile;
+  dim3 grid((uint32_t)tile, (uint32_t)((t + 255) / 256));
+  return launch_gemm_tall(qtype, kMulti, grid, p, s);
+}
+
 // ---------------------------------------------------------------------------
 // Routed experts: router, token lists, combine.
 

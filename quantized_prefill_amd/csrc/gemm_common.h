@@ -14,7 +14,23 @@ namespace qp {
 
 constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
 
-enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4 };
+enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4, kMulti = 5 };
+
+// Projections sharing one X fused into one launch of the tall kernel (mode
+// kMulti): segment s owns the output-column tiles [tile0[s], tile0[s + 1]) of
+// the grid's x dimension, with its own weights, output and epilogue.
+constexpr int kMaxSeg = 3;
+struct GemmSegments {
+  int nseg;
+  int tile0[kMaxSeg + 1];
+  const uint8_t* w[kMaxSeg];
+  int n[kMaxSeg];
+  float* y[kMaxSeg];
+  int64_t ldy[kMaxSeg];
+  const float* gain[kMaxSeg];
+  int64_t gstride[kMaxSeg];
+  int norm[kMaxSeg];  // 1: per-head RMSNorm epilogue, 0: plain
+};
 
 struct GemmParams {
   const uint8_t* w;      // W (or the gate tensors of all experts)
@@ -43,6 +59,7 @@ struct GemmParams {
   float* hbuf;           // [pairs][inter]
   float* dbuf;           // [pairs][hidden]
   const float* weights;  // [pairs]
+  GemmSegments seg;      // fused projections (kMulti)
 };
 
 // Power of two bringing a row's largest |h| into [2^14, 2^15): binary16 then

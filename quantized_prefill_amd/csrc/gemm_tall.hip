@@ -172,7 +172,7 @@ template <> __device__ __forceinline__ void staged_unit<kQ2_K>(const uint32_t* r
 }
 
 template <int QT, int MODE>
-__global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
+__global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   using SU = StageUnit<QT>;
   constexpr int RSD = SU::RSD, CPU = SU::KW / BK;  // chunks per staging unit
   constexpr int XB = xbuf_of<QT>();
@@ -190,7 +190,22 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
   // workgroup, each SIMD then runs one of each.
   const bool producer = (__builtin_popcount(wave) & 1) != 0;
   const int role_idx = wave >> 1;  // 0..3 within each role
-  const int n0 = blockIdx.x * BN;
+  // kMulti: this tile's projection (uniform per workgroup)
+  GemmParams p = pk;
+  int tile_x = blockIdx.x;
+  bool norm = MODE == kQkNorm;
+  if constexpr (MODE == kMulti) {
+    const int sg = (tile_x >= pk.seg.tile0[1]) + (pk.seg.nseg > 2 && tile_x >= pk.seg.tile0[2]);
+    tile_x -= pk.seg.tile0[sg];
+    p.w = pk.seg.w[sg];
+    p.n = pk.seg.n[sg];
+    p.y = pk.seg.y[sg];
+    p.ldy = pk.seg.ldy[sg];
+    p.gain = pk.seg.gain[sg];
+    p.gstride = pk.seg.gstride[sg];
+    norm = pk.seg.norm[sg] != 0;
+  }
+  const int n0 = tile_x * BN;
   const int m0 = blockIdx.y * TBM;
   const int m_rows = min(TBM, p.t - m0);
   const int nch = p.k / BK;
@@ -423,13 +438,22 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams p) {
   }
 
   // reduction scratch in the staging area: no asynchronous copy writes there
-  gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
+  if constexpr (MODE == kMulti) {
+    if (norm)
+      gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
+    else
+      gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
+  } else {
+    gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
+  }
 }
 
 hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p, hipStream_t s) {
 #define QP_TALL(QT)                                                                          \
   if (mode == kQkNorm)                                                                       \
     hipLaunchKernelGGL((gemm_tall_kernel<QT, kQkNorm>), grid, dim3(2 * NT), 0, s, p);        \
+  else if (mode == kMulti)                                                                   \
+    hipLaunchKernelGGL((gemm_tall_kernel<QT, kMulti>), grid, dim3(2 * NT), 0, s, p);         \
   else                                                                                       \
     hipLaunchKernelGGL((gemm_tall_kernel<QT, kPlainF16>), grid, dim3(2 * NT), 0, s, p);
   switch (qtype) {

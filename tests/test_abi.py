@@ -75,6 +75,17 @@ def test_gemm_rejections():
     assert q(qp.Q4_K, FAKE, 192, 256, FAKE, 8, 256, 128, FAKE, 0, 1e-6, FAKE, 192, None) == 1  # n % hd
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, FAKE, 0, 0.0, FAKE, 256, None) == 1   # eps
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, None, 0, 1e-6, FAKE, 256, None) == 1  # gain
+    f = L.qp_prefill_gemm_qkv
+    good = [qp.Q4_K, FAKE, 256, FAKE, 128, FAKE, 128, 256, FAKE, 8, 256, 128, FAKE, 0, FAKE, 0, 1e-6,
+            FAKE, 256, FAKE, 128, FAKE, 128, None]
+    assert f(*(good[:9] + [0] + good[10:])) == 0                  # t == 0: nothing to do
+    for i, v, why in ((0, 7, "type"), (2, 192, "n_q % hd"), (4, 64, "n_k % hd"), (6, -1, "n_v"), (7, 96, "k"),
+                      (11, 96, "head_dim"), (16, 0.0, "eps"), (12, None, "gain_q"), (14, None, "gain_k"),
+                      (20, 64, "ldy_k < n_k"), (22, 64, "ldy_v < n_v")):
+        bad = list(good)
+        bad[i] = v
+        want = 2 if why == "type" else 1
+        assert f(*bad) == want, why
 
 
 def test_moe_rejections():

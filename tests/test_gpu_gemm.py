@@ -191,3 +191,71 @@ def test_qknorm_tall_tile_ragged(orc, qtype, hd, n):
         y = run_qknorm(qtype, raw, n, k, x, hd, gain, gstride, 1e-6)
         ref = orc.prefill_gemm_qknorm(qtype, raw, n, k, x, hd, gain, gstride, 1e-6)
         assert_close(y, ref, f"qknorm tall {synth.NAMES[qtype]} hd={hd} stride={gstride}")
+
+
+def run_qkv(qtype, ws, ns, k, x, hd, gains, gstrides, eps=1e-6):
+    import torch
+    xt = to_dev(x).view(torch.float16)
+    wv = to_dev(ws[2]) if ns[2] else None
+    yq, yk, yv = qp.prefill_gemm_qkv(qtype, to_dev(ws[0]), ns[0], to_dev(ws[1]), ns[1], wv, ns[2], k, xt, hd,
+                                     to_dev(gains[0]), to_dev(gains[1]), gstrides[0], gstrides[1], eps)
+    torch.cuda.synchronize()
+    return yq.cpu().numpy(), yk.cpu().numpy(), (yv.cpu().numpy() if ns[2] else None)
+
+
+def check_qkv(orc, qtype, ws, ns, k, x, hd, gains, gstrides, tok, what):
+    yq, yk, yv = run_qkv(qtype, ws, ns, k, x, hd, gains, gstrides)
+    xs = x if tok is None else x[tok]
+    sel = (lambda a: a) if tok is None else (lambda a: a[tok])
+    for name, y, i in (("q", yq, 0), ("k", yk, 1)):
+        ref = orc.prefill_gemm_qknorm(qtype, ws[i], ns[i], k, x, hd, gains[i], gstrides[i], 1e-6, tokens=tok)
+        assert_close(sel(y), ref, f"{what} {name}")
+    if ns[2]:
+        assert_close(sel(yv), orc.prefill_gemm(qtype, ws[2], ns[2], k, x, tokens=tok), f"{what} v")
+    return yq, yk, yv
+
+
+@pytest.mark.parametrize("qtype", [Q6_K, Q2_K], ids=["Q6_K", "Q2_K"])
+def test_qkv_workload(orc, qtype):
+    """Qwen3-8B attention inputs at T = 2048 in one call (one fused launch:
+    384 tall tiles); q also matches the separate QK-norm call bit for bit."""
+    t, k, hd = 2048, 4096, 128
+    x = act_f16(t, k, synth.seed_for(2, 500 + k // 256))
+    names = [p for p in synth.PROJ_8B if p[0] in ("q", "k", "v")]
+    ws = [weights(qtype, n, k, synth.seed_for(2, 10 * qtype + synth.PROJ_8B.index(p))) for p in names for n in [p[1]]]
+    ns = [p[1] for p in names]
+    gains = [synth.gains(hd, synth.seed_for(2, 600 + j)) for j in range(2)]
+    say(f"qkv workload {synth.NAMES[qtype]} t={t} n={ns}")
+    tok = sample_tokens(t, 10, 9200)
+    yq, _, _ = check_qkv(orc, qtype, ws, ns, k, x, hd, gains, [0, 0], tok, f"qkv {synth.NAMES[qtype]}")
+    y_sep = run_qknorm(qtype, ws[0], ns[0], k, x, hd, gains[0], 0, 1e-6)
+    assert np.array_equal(yq, y_sep), "fused q differs from the separate QK-norm launch"
+    weights.cache_clear()
+
+
+@pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
+def test_qkv_ragged(orc, qtype):
+    """Fused launch with T off the tile (777), per-head gains, strided gains
+    for k; then head_dim 64 with a half-filled last q tile and no v."""
+    t, k = 777, 512
+    x = act_f16(t, k, 8701)
+    ns = [4096, 2048, 2048]
+    ws = [weights(qtype, n, k, 8710 + i) for i, n in enumerate(ns)]
+    gains = [synth.gains(ns[0], 8720), synth.gains(128, 8721)]
+    say(f"qkv ragged {synth.NAMES[qtype]} hd=128")
+    check_qkv(orc, qtype, ws, ns, k, x, 128, gains, [128, 0], None, f"qkv ragged {synth.NAMES[qtype]}")
+    ns = [6208, 2048, 0]
+    ws = [weights(qtype, ns[0], k, 8730), ws[1], None]
+    gains = [synth.gains(64, 8731), synth.gains(64, 8732)]
+    say(f"qkv ragged {synth.NAMES[qtype]} hd=64 no v")
+    check_qkv(orc, qtype, ws, ns, k, x, 64, gains, [0, 0], None, f"qkv ragged hd64 {synth.NAMES[qtype]}")
+
+
+def test_qkv_small_falls_back(orc):
+    """Too few tiles for one fused launch: the three separate launches."""
+    t, k = 50, 256
+    x = act_f16(t, k, 8801)
+    ns = [256, 128, 128]
+    ws = [weights(Q4_K, n, k, 8810 + i) for i, n in enumerate(ns)]
+    gains = [synth.gains(128, 8820), synth.gains(128, 8821)]
+    check_qkv(orc, Q4_K, ws, ns, k, x, 128, gains, [0, 0], None, "qkv small")
