@@ -219,6 +219,10 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   const int wm = role_idx >> 1, wn = role_idx & 1;
 
   if (!producer) {
+    // The consumer (the MFMA feeder) issues ahead of the producer on its
+    // SIMD; by default the older wave of a pair wins, which made the two
+    // halves of the tile finish a chunk at different times.
+    __builtin_amdgcn_s_setprio(1);
     // ---- consumer waves -------------------------------------------------
     // Activation copy: this wave's 8 load instructions cover tile rows
     // 64 cw + 8 q .. + 7; lane l lands in slot l & 7 of row 64 cw + 8 q + (l >> 3),
