@@ -136,11 +136,25 @@ template <> __device__ __forceinline__ void staged_unit<kQ4_K>(const uint32_t* r
 template <> __device__ __forceinline__ void staged_unit<kQ6_K>(const uint32_t* row, uint32_t delta, uint32_t u,
                                                               UnitRaw& r) {
   const uint32_t h = u >> 2, q4 = u & 3;
+  // all 20 dwords first, one LDS round trip (the scheduler otherwise waits
+  // for each field before reading the next)
+  const uint32_t bl = delta + 64 * h + 32 * (q4 & 1), bh = delta + 128 + 32 * h;
+  const uint32_t bs = delta + 192 + 2 * u, bd = delta + 208;
+  uint32_t dl[9], dh[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) dl[i] = row[(bl >> 2) + i];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) dh[i] = row[(bh >> 2) + i];
+  const uint32_t wsc = row[bs >> 2], wd = row[bd >> 2];
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t ql[8], qh[8];
-  staged32(row, delta, 64 * h + 32 * (q4 & 1), ql);
-  staged32(row, delta, 128 + 32 * h, qh);
-  const uint32_t scp = staged16(row, delta, 192 + 2 * u);
-  const float d = f16_to_f32(staged16(row, delta, 208));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ql[i] = __builtin_amdgcn_alignbyte(dl[i + 1], dl[i], bl & 3);
+    qh[i] = __builtin_amdgcn_alignbyte(dh[i + 1], dh[i], bh & 3);
+  }
+  const uint32_t scp = (wsc >> (8 * (bs & 3))) & 0xFFFFu;
+  const float d = f16_to_f32((wd >> (8 * (bd & 3))) & 0xFFFFu);
   const uint32_t shl = 4 * (q4 >> 1), shh = 2 * q4;
 #pragma unroll
   for (int j = 0; j < 8; ++j) r.code[j] = ((ql[j] >> shl) & 0x0F0F0F0Fu) | (((qh[j] >> shh) & 0x03030303u) << 4);
@@ -211,12 +225,23 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   const int nch = p.k / BK;
   const int nunits = p.k / SU::KW;
 
-  float16v acc[TMI][2];
-#pragma unroll
-  for (int i = 0; i < TMI; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (float16v){};
   const int wm = role_idx >> 1, wn = role_idx & 1;
+  // Epilogue of this tile; the producer waves only take its barriers.  Each
+  // role calls it from its own branch, so the accumulators are not live in
+  // the producer code (whose decode then has the registers to issue all of a
+  // unit's LDS reads at once).
+  auto epilogue = [&](float16v(&acc)[TMI][2], bool active) __attribute__((always_inline)) {
+    // reduction scratch in the staging area: no asynchronous copy writes there
+    float* red = (float*)sm.raw[0];
+    if constexpr (MODE == kMulti) {
+      if (norm)
+        gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
+      else
+        gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
+    } else {
+      gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
+    }
+  };
 
   if (!producer) {
     // The consumer (the MFMA feeder) issues ahead of the producer on its
@@ -224,6 +249,11 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     // halves of the tile finish a chunk at different times.
     __builtin_amdgcn_s_setprio(1);
     // ---- consumer waves -------------------------------------------------
+    float16v acc[TMI][2];
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = (float16v){};
     // Activation copy: this wave's 8 load instructions cover tile rows
     // 64 cw + 8 q .. + 7; lane l lands in slot l & 7 of row 64 cw + 8 q + (l >> 3),
     // which holds the piece that slot order puts there.
@@ -336,6 +366,7 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
+    epilogue(acc, true);
   } else {
     // ---- producer waves: stage and decode ---------------------------------
     const int pw = role_idx;  // 0..3
@@ -439,16 +470,8 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
       lds_barrier();  // next chunk decoded
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-
-  // reduction scratch in the staging area: no asynchronous copy writes there
-  if constexpr (MODE == kMulti) {
-    if (norm)
-      gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
-    else
-      gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
-  } else {
-    gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, (float*)sm.raw[0], !producer);
+    float16v none[TMI][2];  // not read: the producer side of the epilogue only synchronises
+    epilogue(none, false);
   }
 }
 
