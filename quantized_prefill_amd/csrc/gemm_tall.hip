@@ -147,17 +147,18 @@ template <> __device__ __forceinline__ void staged_unit<kQ6_K>(const uint32_t* r
   for (int i = 0; i < 9; ++i) dh[i] = row[(bh >> 2) + i];
   const uint32_t wsc = row[bs >> 2], wd = row[bd >> 2];
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t ql[8], qh[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ql[i] = __builtin_amdgcn_alignbyte(dl[i + 1], dl[i], bl & 3);
-    qh[i] = __builtin_amdgcn_alignbyte(dh[i + 1], dh[i], bh & 3);
-  }
   const uint32_t scp = (wsc >> (8 * (bs & 3))) & 0xFFFFu;
   const float d = f16_to_f32((wd >> (8 * (bd & 3))) & 0xFFFFu);
-  const uint32_t shl = 4 * (q4 >> 1), shh = 2 * q4;
+  // one funnel shift per dword both undoes the field's byte offset in its
+  // first dword and brings the wanted nibble (ql) or 2-bit field (qh) of each
+  // byte to bit 0 (shift amounts at most 16 + 6)
+  const uint32_t sa = 8 * (bl & 3) + 4 * (q4 >> 1), sb = 8 * (bh & 3) + 2 * q4;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r.code[j] = ((ql[j] >> shl) & 0x0F0F0F0Fu) | (((qh[j] >> shh) & 0x03030303u) << 4);
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t lo = __builtin_amdgcn_alignbit(dl[j + 1], dl[j], sa);
+    const uint32_t hi = __builtin_amdgcn_alignbit(dh[j + 1], dh[j], sb);
+    r.code[j] = (lo & 0x0F0F0F0Fu) | ((hi & 0x03030303u) << 4);
+  }
   const float a0 = __fmul_rn(d, (float)(int8_t)(scp & 0xFFu));
   const float a1 = __fmul_rn(d, (float)(int8_t)(scp >> 8));
   r.a0 = a0;
