@@ -373,72 +373,110 @@ hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t 
 
 // Count the pairs of each expert (one workgroup per expert) and clear the
 // row maxima of the h rows.
-__global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ ids, int npairs, int ne,
-                                                        int* __restrict__ counts, uint32_t* __restrict__ rowmax) {
-  __shared__ int red[4];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int i = threadIdx.x; i < npairs; i += 256) c += ids[i] == e;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) c += __shfl_xor(c, m, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+// Token lists of the routed experts, built chunk-parallel: chunk j holds
+// pairs [256 j, 256 j + 256).  Histogram per chunk; per expert, an exclusive
+// scan over its chunk counts; over experts, an exclusive scan of the totals;
+// then a stable scatter (rank among the earlier pairs of the chunk with the
+// same expert).  Each expert's list
+// is therefore in pair order.  Ids outside [0, n_experts) are dropped.
+constexpr int kMoeChunk = 256;
+
+__global__ __launch_bounds__(kMoeChunk) void moe_hist_kernel(const int32_t* __restrict__ ids, int npairs, int ne,
+                                                             int nchunks, int* __restrict__ ccount,
+                                                             uint32_t* __restrict__ rowmax) {
+  __shared__ int hist[1024];
+  const int ch = blockIdx.x;
+  for (int e = threadIdx.x; e < ne; e += kMoeChunk) hist[e] = 0;
   __syncthreads();
-  if (threadIdx.x == 0) counts[e] = red[0] + red[1] + red[2] + red[3];
-  for (int i = e * 256 + threadIdx.x; i < npairs; i += ne * 256) rowmax[i] = 0u;
+  const int i = ch * kMoeChunk + threadIdx.x;
+  if (i < npairs) {
+    const int e = ids[i];
+    if (e >= 0 && e < ne) atomicAdd(&hist[e], 1);
+    rowmax[i] = 0u;  // max |h| of compact row i, accumulated by the gate/up pass
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < ne; e += kMoeChunk) ccount[(int64_t)e * nchunks + ch] = hist[e];
 }
 
-// Exclusive scans of the counts (compact row offsets) and of the tiles per
-// expert; writes the tile table and the number of tiles.  One workgroup of
-// 1024 threads (n_experts <= 1024).
-__global__ __launch_bounds__(1024) void moe_scan_kernel(const int* __restrict__ counts, int ne,
-                                                        int* __restrict__ offsets, int* __restrict__ tiles,
-                                                        int* __restrict__ ntiles) {
-  __shared__ int sc[1024], st[1024];
+// Inclusive scan of v over the 1024 threads of a workgroup (wave shuffles,
+// then the wave totals through LDS); returns the scan, *total the sum.
+__device__ __forceinline__ int block_scan_1024(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int x = wsum[w];
+    base += w < wave ? x : 0;
+    all += x;
+  }
+  __syncthreads();  // wsum may be rewritten by the next call
+  *total = all;
+  return v + base;
+}
+
+// One workgroup per expert: cpref[e][j] = pairs of expert e in chunks before j.
+__global__ __launch_bounds__(1024) void moe_escan_kernel(const int* __restrict__ ccount, int nchunks,
+                                                         int* __restrict__ cpref, int* __restrict__ counts) {
+  __shared__ int wsum[16];
+  const int64_t row = (int64_t)blockIdx.x * nchunks;
+  int carry = 0;
+  for (int b = 0; b < nchunks; b += 1024) {
+    const int j = b + (int)threadIdx.x;
+    const int v = j < nchunks ? ccount[row + j] : 0;
+    int tot;
+    const int incl = block_scan_1024(v, wsum, &tot);
+    if (j < nchunks) cpref[row + j] = carry + incl - v;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[blockIdx.x] = carry;
+}
+
+// One workgroup: first compact row of each expert (exclusive scan of the
+// counts), the table of 128-row tiles per expert and the number of tiles.
+__global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__ counts, int ne,
+                                                         int* __restrict__ offsets, int* __restrict__ tiles,
+                                                         int* __restrict__ ntiles) {
+  __shared__ int wsum[16];
   const int e = threadIdx.x;
   const int c = e < ne ? counts[e] : 0;
   const int nt = (c + BM - 1) / BM;
-  sc[e] = c;
-  st[e] = nt;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
-    const int a = e >= d ? sc[e - d] : 0, b = e >= d ? st[e - d] : 0;
-    __syncthreads();
-    sc[e] += a;
-    st[e] += b;
-    __syncthreads();
-  }
+  int tot;
+  const int cin = block_scan_1024(c, wsum, &tot);
+  const int tin = block_scan_1024(nt, wsum, &tot);
   if (e < ne) {
-    offsets[e] = sc[e] - c;
-    const int t0 = st[e] - nt;
+    offsets[e] = cin - c;
+    const int t0 = tin - nt;
     for (int k = 0; k < nt; ++k) {
       tiles[2 * (t0 + k)] = e;
       tiles[2 * (t0 + k) + 1] = k * BM;
     }
   }
-  if (e == 1023) *ntiles = st[1023];
+  if (e == 0) *ntiles = tot;
 }
 
-// Stable compaction: compact row offsets[e] + r holds the r-th pair (in pair
-// order) routed to expert e.  One workgroup per expert.
-__global__ __launch_bounds__(256) void moe_fill_kernel(const int32_t* __restrict__ ids, int npairs,
-                                                       const int* __restrict__ offsets, int* __restrict__ list) {
-  __shared__ int wsum[4];
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int running = offsets[e];
-  for (int start = 0; start < npairs; start += 256) {
-    const int i = start + threadIdx.x;
-    const bool match = i < npairs && ids[i] == e;
-    const uint64_t bal = __ballot(match);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
-    __syncthreads();
-    int woff = 0;
-    for (int w = 0; w < wave; ++w) woff += wsum[w];
-    if (match) list[running + woff + before] = i;
-    running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-  }
+// Stable scatter: pair i of chunk j with expert e goes to compact row
+// offsets[e] + cpref[e][j] + (number of earlier pairs of chunk j with expert e).
+__global__ __launch_bounds__(kMoeChunk) void moe_scatter_kernel(const int32_t* __restrict__ ids, int npairs, int ne,
+                                                                int nchunks, const int* __restrict__ offsets,
+                                                                const int* __restrict__ cpref,
+                                                                int* __restrict__ list) {
+  __shared__ int sid[kMoeChunk];
+  const int ch = blockIdx.x;
+  const int i = ch * kMoeChunk + threadIdx.x;
+  const int e = i < npairs ? ids[i] : -1;
+  sid[threadIdx.x] = e;
+  __syncthreads();
+  if (e < 0 || e >= ne) return;
+  int rank = 0;
+  for (int j = 0; j < (int)threadIdx.x; ++j) rank += sid[j] == e;
+  list[offsets[e] + cpref[(int64_t)e * nchunks + ch] + rank] = i;
 }
 
 // out[t, :] = sum over slots s (in order) of the weighted expert outputs of
@@ -470,6 +508,9 @@ bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t h
   const int64_t pairs = t * top_k;
   ws.max_tiles = n_experts + (pairs + BM - 1) / BM;
   size_t o = 0;
+  ws.nchunks = (pairs + kMoeChunk - 1) / kMoeChunk;
+  ws.ccount = o;  o += align256(sizeof(int) * n_experts * ws.nchunks);
+  ws.cpref = o;   o += align256(sizeof(int) * n_experts * ws.nchunks);
   ws.counts = o;  o += align256(sizeof(int) * n_experts);
   ws.offsets = o; o += align256(sizeof(int) * n_experts);
   ws.ntiles = o;  o += align256(sizeof(int) * 4);
@@ -498,13 +539,23 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
   const int npairs = (int)(t * top_k);
   hipError_t err;
 
-  hipLaunchKernelGGL(moe_count_kernel, dim3((uint32_t)n_experts), dim3(256), 0, s, ids, npairs, (int)n_experts,
-                     counts, rowmax);
+  int* ccount = (int*)(wsb + ws.ccount);
+  int* cpref = (int*)(wsb + ws.cpref);
+  const int nch = (int)ws.nchunks;
+  if (nch > 0) {
+    hipLaunchKernelGGL(moe_hist_kernel, dim3((uint32_t)nch), dim3(kMoeChunk), 0, s, ids, npairs, (int)n_experts, nch,
+                       ccount, rowmax);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(moe_escan_kernel, dim3((uint32_t)n_experts), dim3(1024), 0, s, ccount, nch, cpref, counts);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles);
+  hipLaunchKernelGGL(moe_oscan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_fill_kernel, dim3((uint32_t)n_experts), dim3(256), 0, s, ids, npairs, offsets, list);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (nch > 0) {
+    hipLaunchKernelGGL(moe_scatter_kernel, dim3((uint32_t)nch), dim3(kMoeChunk), 0, s, ids, npairs, (int)n_experts,
+                       nch, offsets, cpref, list);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
   GemmParams p = {};
   p.tiles = tiles;
