@@ -196,10 +196,14 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
 
 // Token-tile height: 256 halves the decode work per flop and is used when the
 // launch still fills the 256 CUs with one 256-token tile each.  The tall
-// kernel addresses a tile's activation rows with 32-bit byte offsets.
-static bool use_tall_tiles(int64_t n, int64_t t, int64_t ldx) {
+// kernel addresses a tile's activation rows with 32-bit byte offsets and
+// stores outputs 16 bytes at a time (rows of Y a multiple of 16 bytes).
+static bool tall_strides_ok(int64_t ldx, int64_t ldy) {
+  return 256 * ldx * 2 < ((int64_t)1 << 31) && ldy % 4 == 0;
+}
+static bool use_tall_tiles(int64_t n, int64_t t, int64_t ldx, int64_t ldy) {
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + 255) / 256);
-  return t >= 512 && tiles >= 256 && 256 * ldx * 2 < ((int64_t)1 << 31);
+  return t >= 512 && tiles >= 256 && tall_strides_ok(ldx, ldy);
 }
 
 hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
@@ -214,7 +218,7 @@ hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const voi
   p.t = (int)t;
   p.y = y;
   p.ldy = ldy;
-  if (!x_f32 && use_tall_tiles(n, t, ldx)) {
+  if (!x_f32 && use_tall_tiles(n, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
   }
@@ -239,7 +243,7 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   p.gstride = gain_head_stride;
   p.hd = (int)head_dim;
   p.eps = eps;
-  if (use_tall_tiles(n, t, ldx)) {
+  if (use_tall_tiles(n, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kQkNorm, grid, p, s);
   }
@@ -256,7 +260,8 @@ hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3]
                            hipStream_t s) {
   int64_t ntiles = 0;
   for (int i = 0; i < 3; ++i) ntiles += (n[i] + BN - 1) / BN;
-  const bool fused = t >= 512 && ntiles * ((t + 255) / 256) >= 256 && 256 * ldx * 2 < ((int64_t)1 << 31);
+  const bool fused = t >= 512 && ntiles * ((t + 255) / 256) >= 256 && tall_strides_ok(ldx, ldy[0]) &&
+                     tall_strides_ok(ldx, ldy[1]) && (n[2] == 0 || tall_strides_ok(ldx, ldy[2]));
   if (!fused) {
     for (int i = 0; i < 3; ++i) {
       if (n[i] == 0) continue;

@@ -79,17 +79,71 @@ __device__ __forceinline__ float row_scale_from_max(uint32_t maxbits, bool inver
 // floats, free once the main loop's last barrier has passed.
 // `active` false: a wave holding no tile (the producer waves of the
 // specialised kernel) only takes part in the epilogue's barriers.
+// Plain f32 store of a wave's WM x 64 block with 16-byte stores: each 32 x 32
+// MFMA tile goes through a per-wave LDS buffer of 32 rows x 40 floats, written
+// in the register layout and read back as rows of float4.  (One 4-byte store
+// per value made the store instructions, not HBM, bound the epilogue.)  The
+// pitch of 40 floats puts the two half-waves of a register write in different
+// halves of the 64 banks.  The LDS operations of a wave complete in order, so
+// the read-back sees the writes.  Requires ldy % 4 == 0 (16-byte rows).
+template <int MI>
+__device__ __forceinline__ void store_block_vec(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
+                                                int n0, int wm, int wn, int lane, float* scr) {
+  constexpr int WM = 32 * MI, PITCH = 40;
+  const int ln = lane;  // from the lane counter (see gemm_epilogue)
+  const int l8 = ln >> 3;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        scr[(8 * (a >> 2) + 4 * (ln >> 5) + (a & 3)) * PITCH + (ln & 31)] = acc[i][j][a];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        asm volatile("" ::: "memory");  // one float4 in flight: the registers are nearly all taken
+        const int rr = 8 * q + l8, cg = ln & 7;
+        const float4v v = *(const float4v*)(scr + rr * PITCH + 4 * cg);
+        const int row = WM * wm + 32 * i + rr;
+        const int col = n0 + 64 * wn + 32 * j + 4 * cg;
+        if (row < m_rows) {
+          float* dst = p.y + (int64_t)(base + row) * p.ldy + col;
+          if (col + 3 < p.n) {
+            *(float4v*)dst = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < p.n) dst[e] = v[e];
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+}
+
+// vec_scratch: plain stores go through store_block_vec (the caller
+// guarantees ldy % 4 == 0); null: one 4-byte store per value.
 template <int MODE, int MI>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
-                                              int n0, int wm, int wn, int lane, float* red, bool active = true) {
+                                              int n0, int wm, int wn, int lane, float* red, bool active = true,
+                                              float* vec_scratch = nullptr) {
   constexpr int WM = 32 * MI;
   if (!active) {
     if constexpr (MODE == kQkNorm) __syncthreads();
     return;
   }
+  // The lane index from the hardware lane counter: lane-derived values here
+  // are then not shared with the main loop's address setup, which would keep
+  // them live across the loop past the register budget.
+  lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   auto row_of = [&](int i, int a) { return WM * wm + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3); };
 
   if constexpr (MODE == kPlainF16 || MODE == kPlainF32) {
+    if (vec_scratch) {
+      store_block_vec<MI>(p, acc, base, m_rows, n0, wm, wn, lane, vec_scratch);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll

@@ -234,13 +234,17 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   auto epilogue = [&](float16v(&acc)[TMI][2], bool active) __attribute__((always_inline)) {
     // reduction scratch in the staging area: no asynchronous copy writes there
     float* red = (float*)sm.raw[0];
+    // per-wave transpose buffers of the plain store in the weight tiles: no
+    // direct load targets them, and after the last barrier only the unused
+    // next-chunk fragment reads touch them
+    float* vec = (float*)sm.w[0] + 32 * 40 * role_idx;
     if constexpr (MODE == kMulti) {
       if (norm)
         gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
       else
-        gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
+        gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
     } else {
-      gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
+      gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
     }
   };
 

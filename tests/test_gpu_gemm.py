@@ -154,17 +154,19 @@ def test_qknorm_workload(orc):
 
 # Shapes that take the 256-token tile (at least 512 tokens and at least 256
 # output tiles) with T and N not multiples of the tile, in padded strides.
-TALL = [(777, 8269, 512), (513, 11009, 256)]
+# (the last case's output stride is not a multiple of 4 floats: the tall tile
+# stores 16-byte rows, so that shape goes to the 128 x 128 kernel)
+TALL = [(777, 8269, 512, 0), (513, 11009, 256, 0), (640, 8192, 256, 1)]
 
 
 @pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
-@pytest.mark.parametrize("t,n,k", TALL)
-def test_tall_tile_ragged(orc, qtype, t, n, k):
+@pytest.mark.parametrize("t,n,k,odd", TALL)
+def test_tall_tile_ragged(orc, qtype, t, n, k, odd):
     import torch
-    say(f"gemm tall {synth.NAMES[qtype]} t={t} n={n} k={k}")
+    say(f"gemm tall {synth.NAMES[qtype]} t={t} n={n} k={k} odd ldy={odd}")
     raw = weights(qtype, n, k, 8500 + t)
     x = act_f16(t, k, 8501 + t)
-    ldx, ldy = k + 64, (n + 7) // 4 * 4 + 4
+    ldx, ldy = k + 64, ((n + 7) // 4 * 4 + 4) + odd
     xpad = np.zeros((t, ldx), np.uint16)
     xpad[:, :k] = x
     xt = to_dev(xpad).view(torch.float16)
