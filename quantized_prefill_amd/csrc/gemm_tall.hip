@@ -186,6 +186,31 @@ template <> __device__ __forceinline__ void staged_unit<kQ2_K>(const uint32_t* r
   r.sm1 = r.b1;
 }
 
+// Q2_K to binary16 by table: a sub-block's 16 weights take only the values
+// v_q = RNE16(fma(d*sc, q, -dmin*m)), q = 0..3 (the same single-rounding f32
+// value as unit_to_f16), so the four values are computed once and each
+// weight picks its own with a byte permute.  The selector of two weights is
+// the bytes (2 q0, 2 q0 + 1, 2 q1, 2 q1 + 1), itself one permute of 2 q and
+// 2 q + 1.
+__device__ __forceinline__ void q2k_unit_to_f16_lut(const UnitRaw& r, uint32_t (&out)[16]) {
+  uint32_t t01[2], t23[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float a = h ? r.a1 : r.a0, b = h ? r.b1 : r.b0;
+    t01[h] = pack_f16x2(__builtin_fmaf(a, 0.f, -b), __builtin_fmaf(a, 1.f, -b));
+    t23[h] = pack_f16x2(__builtin_fmaf(a, 2.f, -b), __builtin_fmaf(a, 3.f, -b));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int h = j >> 2;
+    const uint32_t e = r.code[j] << 1, o = e | 0x01010101u;   // 2 q and 2 q + 1 per byte
+    const uint32_t s01 = __builtin_amdgcn_perm(o, e, 0x05010400u);
+    const uint32_t s23 = __builtin_amdgcn_perm(o, e, 0x07030602u);
+    out[2 * j] = __builtin_amdgcn_perm(t23[h], t01[h], s01);
+    out[2 * j + 1] = __builtin_amdgcn_perm(t23[h], t01[h], s23);
+  }
+}
+
 template <int QT, int MODE>
 __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   using SU = StageUnit<QT>;
@@ -433,7 +458,10 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
       UnitRaw ur;
       staged_unit<QT>(sm.raw[u & 1] + wn_t * RSD, delta, (uint32_t)(2 * (c % CPU) + kh), ur);
       uint32_t hw[16];
-      unit_to_f16<QT>(ur, hw);
+      if constexpr (QT == kQ2_K)
+        q2k_unit_to_f16_lut(ur, hw);
+      else
+        unit_to_f16<QT>(ur, hw);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *(u32x4*)(sm.w[buf] + swz(wn_t, 4 * kh + q)) = (u32x4){hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]};

@@ -261,3 +261,19 @@ def test_qkv_small_falls_back(orc):
     ws = [weights(Q4_K, n, k, 8810 + i) for i, n in enumerate(ns)]
     gains = [synth.gains(128, 8820), synth.gains(128, 8821)]
     check_qkv(orc, Q4_K, ws, ns, k, x, 128, gains, [0, 0], None, "qkv small")
+
+
+@pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
+def test_tall_tile_weights_exact(orc, qtype):
+    """One-hot rows (token t selects input column t % K) on the 256-token
+    tile: every output is one binary16 weight times 1, so the tall kernel's
+    in-LDS decode must equal the oracle's f16 dequant bit for bit."""
+    t, n, k = 512, 16384, 512
+    raw = weights(qtype, n, k, 8900)
+    x = np.zeros((t, k), np.uint16)
+    x[np.arange(t), np.arange(t) % k] = 0x3C00
+    y = run_gemm(qtype, raw, n, k, x)
+    w16 = orc.dequant_f16_bits(qtype, raw, n, k).view(np.float16).astype(np.float32)
+    want = w16[:, np.arange(t) % k].T
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:3].tolist()}"
