@@ -289,19 +289,24 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     // which holds the piece that slot order puts there.
     const int cw = role_idx;
     const _Float16* xtile = (const _Float16*)p.x + (int64_t)m0 * p.ldx;  // tile row 0
-    uint32_t xoff[8];  // halfs from xtile (a tile spans under 2^30 halfs)
+    uint32_t xoff[8];  // bytes from xtile (a tile spans under 2^31 bytes)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = 64 * cw + 8 * q + (lane >> 3);
       const int piece = (lane & 7) ^ swz_of(row);
-      xoff[q] = (uint32_t)(min(row, m_rows - 1) * p.ldx + 8 * piece);
+      xoff[q] = (uint32_t)(2 * (min(row, m_rows - 1) * p.ldx + 8 * piece));
     }
-    // load q (of 8) of this wave's share of chunk c (past the end: the last chunk again)
+    // load q (of 8) of this wave's share of chunk c (past the end: the last
+    // chunk again), as a buffer load over the tile's rows: the lane's byte
+    // offset is fixed and the chunk's goes in the scalar offset, so a load
+    // costs no vector address arithmetic.
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xtile, (short)0, -1, 0x00020000);
     auto load_xq = [&](int c, int q) __attribute__((always_inline)) {
       c = c < nch ? c : nch - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(xtile + (xoff[q] + 64 * c)),
-                                       (__attribute__((address_space(3))) void*)(sm.x[c % XB] + (64 * cw + 8 * q) * BK),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc,
+                                               (__attribute__((address_space(3))) void*)(sm.x[c % XB] + (64 * cw + 8 * q) * BK),
+                                               16, (int)xoff[q], 128 * c, 0, 0);
     };
     // Chunk j goes to buffer j % XB and is loaded right after the barrier
     // that ends the reads of chunk j - XB (the prologue loads chunks
@@ -313,12 +318,17 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
+    // Fragment reads of step s: rows 32 apart share the slot order (it
+    // depends on row bits 1..3), so one address per step and buffer serves
+    // all of them, the 32-row strides going into the reads' immediate offset.
     auto frags = [&](const _Float16* xs, const _Float16* ws, int s, half8 (&a)[TMI], half8 (&b)[2]) {
       const int piece = 2 * s + (lane >> 5);
+      const _Float16* pa = xs + swz(128 * wm + (lane & 31), piece);
+      const _Float16* pb = ws + swz(64 * wn + (lane & 31), piece);
 #pragma unroll
-      for (int i = 0; i < TMI; ++i) a[i] = *(const half8*)(xs + swz(128 * wm + 32 * i + (lane & 31), piece));
+      for (int i = 0; i < TMI; ++i) a[i] = *(const half8*)(pa + 32 * BK * i);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const half8*)(ws + swz(64 * wn + 32 * j + (lane & 31), piece));
+      for (int j = 0; j < 2; ++j) b[j] = *(const half8*)(pb + 32 * BK * j);
     };
     auto mfmas = [&](const half8 (&a)[TMI], const half8 (&b)[2]) {
 #pragma unroll
