@@ -122,8 +122,8 @@ __device__ __forceinline__ void store_block_vec(const GemmParams& p, float16v (&
     }
 }
 
-// vec_scratch: plain stores go through store_block_vec (the caller
-// guarantees ldy % 4 == 0); null: one 4-byte store per value.
+// vec_scratch: plain and normalised stores go through store_block_vec (the
+// caller guarantees ldy % 4 == 0); null: one 4-byte store per value.
 template <int MODE, int MI>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
                                               int n0, int wm, int wn, int lane, float* red, bool active = true,
@@ -172,6 +172,29 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
     __syncthreads();
     const float inv_hd = 1.f / (float)p.hd;
     const bool pair_heads = p.hd == 128;
+    if (vec_scratch) {
+      // normalise in place, then the plain 16-byte store (same products in
+      // the same order as below)
+      float g[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+        const int head = col / p.hd;
+        g[j] = col < p.n ? p.gain[(int64_t)head * p.gstride + (col - head * p.hd)] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int r = row_of(i, a);
+          const float ss = pair_heads ? red[r] + red[TM + r] : red[wn * TM + r];
+          const float scale = 1.f / __builtin_sqrtf(ss * inv_hd + p.eps);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j][a] = acc[i][j][a] * scale * g[j];
+        }
+      store_block_vec<MI>(p, acc, base, m_rows, n0, wm, wn, lane, vec_scratch);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     float* vec = (float*)sm.w[0] + 32 * 40 * role_idx;
     if constexpr (MODE == kMulti) {
       if (norm)
-        gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active);
+        gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
       else
         gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
     } else {
