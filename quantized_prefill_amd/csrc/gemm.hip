@@ -179,7 +179,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  gemm_epilogue<MODE, 2>(p, acc, base, m_rows, n0, wm, wn, lane, (float*)&sm);
+  // after the loop's last barrier the tiles are free: the norm's row sums
+  // (2 x 2 x 64 floats) and then one 32 x 40 transpose buffer per wave
+  float* const lds = (float*)&sm;
+  static_assert(sizeof(GemmSmem) >= (2 * 2 * 64 + 4 * 32 * 40) * 4, "epilogue scratch");
+  gemm_epilogue<MODE, 2>(p, acc, base, m_rows, n0, wm, wn, lane, lds,
+                         true, p.vec_store ? lds + 2 * 2 * 64 + 32 * 40 * wave : nullptr);
 }
 
 template <int MODE>
@@ -218,6 +223,7 @@ hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const voi
   p.t = (int)t;
   p.y = y;
   p.ldy = ldy;
+  p.vec_store = ldy % 4 == 0;
   if (!x_f32 && use_tall_tiles(n, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
@@ -243,6 +249,7 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   p.gstride = gain_head_stride;
   p.hd = (int)head_dim;
   p.eps = eps;
+  p.vec_store = ldy % 4 == 0;
   if (use_tall_tiles(n, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kQkNorm, grid, p, s);
@@ -573,6 +580,7 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
   p.hbuf = hbuf;
   p.dbuf = dbuf;
   p.weights = weights;
+  p.vec_store = inter % 4 == 0 && hidden % 4 == 0;  // h and expert-output rows of 16-byte multiples
 
   // gate/up: A = gathered token rows, W tile = 64 gate rows + 64 up rows
   p.w = (const uint8_t*)w_gate;

@@ -60,6 +60,7 @@ struct GemmParams {
   float* dbuf;           // [pairs][hidden]
   const float* weights;  // [pairs]
   GemmSegments seg;      // fused projections (kMulti)
+  int vec_store;         // 128-tile kernel: output rows are 16-byte multiples (16-byte stores)
 };
 
 // Power of two bringing a row's largest |h| into [2^14, 2^15): binary16 then
@@ -79,42 +80,45 @@ __device__ __forceinline__ float row_scale_from_max(uint32_t maxbits, bool inver
 // floats, free once the main loop's last barrier has passed.
 // `active` false: a wave holding no tile (the producer waves of the
 // specialised kernel) only takes part in the epilogue's barriers.
-// Plain f32 store of a wave's WM x 64 block with 16-byte stores: each 32 x 32
-// MFMA tile goes through a per-wave LDS buffer of 32 rows x 40 floats, written
-// in the register layout and read back as rows of float4.  (One 4-byte store
-// per value made the store instructions, not HBM, bound the epilogue.)  The
-// pitch of 40 floats puts the two half-waves of a register write in different
-// halves of the 64 banks.  The LDS operations of a wave complete in order, so
-// the read-back sees the writes.  Requires ldy % 4 == 0 (16-byte rows).
-template <int MI>
-__device__ __forceinline__ void store_block_vec(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
-                                                int n0, int wm, int wn, int lane, float* scr) {
-  constexpr int WM = 32 * MI, PITCH = 40;
+// f32 store of a wave's block of MI x JB MFMA tiles (32 x 32 each) with
+// 16-byte stores: each tile goes through a per-wave LDS buffer of 32 rows x
+// 40 floats, written in the register layout and read back as rows of
+// float4.  (One 4-byte store per value made the store instructions, not HBM,
+// bound the epilogue.)  The pitch of 40 floats puts the two half-waves of a
+// register write in different halves of the 64 banks.  The LDS operations of
+// a wave complete in order, so the read-back sees the writes.
+// Tile (i, j) covers the block's rows 32 i .. + 31 and columns col0 + 32 j ..
+// + 31; rows >= m_rows and columns >= ncols are not written.  row_ptr(r)
+// gives the start of the block's row r in memory (16-byte aligned rows).
+template <int MI, int JB, typename RowPtr>
+__device__ __forceinline__ void store_tiles_vec(float16v (&v)[MI][JB], int m_rows, int col0, int ncols, int lane,
+                                                float* scr, RowPtr&& row_ptr) {
+  constexpr int PITCH = 40;
   const int ln = lane;  // from the lane counter (see gemm_epilogue)
   const int l8 = ln >> 3;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JB; ++j) {
 #pragma unroll
       for (int a = 0; a < 16; ++a)
-        scr[(8 * (a >> 2) + 4 * (ln >> 5) + (a & 3)) * PITCH + (ln & 31)] = acc[i][j][a];
+        scr[(8 * (a >> 2) + 4 * (ln >> 5) + (a & 3)) * PITCH + (ln & 31)] = v[i][j][a];
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         asm volatile("" ::: "memory");  // one float4 in flight: the registers are nearly all taken
         const int rr = 8 * q + l8, cg = ln & 7;
-        const float4v v = *(const float4v*)(scr + rr * PITCH + 4 * cg);
-        const int row = WM * wm + 32 * i + rr;
-        const int col = n0 + 64 * wn + 32 * j + 4 * cg;
+        const float4v x = *(const float4v*)(scr + rr * PITCH + 4 * cg);
+        const int row = 32 * i + rr;
+        const int col = col0 + 32 * j + 4 * cg;
+        float* const dst = row_ptr(row) + col;  // (computed by every lane: row_ptr may use wave shuffles)
         if (row < m_rows) {
-          float* dst = p.y + (int64_t)(base + row) * p.ldy + col;
-          if (col + 3 < p.n) {
-            *(float4v*)dst = v;
+          if (col + 3 < ncols) {
+            *(float4v*)dst = x;
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (col + e < p.n) dst[e] = v[e];
+              if (col + e < ncols) dst[e] = x[e];
           }
         }
       }
@@ -122,8 +126,20 @@ __device__ __forceinline__ void store_block_vec(const GemmParams& p, float16v (&
     }
 }
 
-// vec_scratch: plain and normalised stores go through store_block_vec (the
-// caller guarantees ldy % 4 == 0); null: one 4-byte store per value.
+// Plain store of a 2 x 2 tile's wave block (WM x 64) into p.y (ldy % 4 == 0).
+template <int MI>
+__device__ __forceinline__ void store_block_vec(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
+                                                int n0, int wm, int wn, int lane, float* scr) {
+  constexpr int WM = 32 * MI;
+  const int r0 = base + WM * wm;
+  store_tiles_vec<MI, 2>(acc, m_rows - WM * wm, n0 + 64 * wn, p.n, lane, scr,
+                         [&](int r) __attribute__((always_inline)) { return p.y + (int64_t)(r0 + r) * p.ldy; });
+}
+
+// vec_scratch (32 x 40 floats of per-wave LDS): every mode stores through
+// store_tiles_vec, 16 bytes at a time (the caller guarantees 16-byte output
+// rows: ldy % 4 == 0, and for the routed passes n % 4 == 0); null: one
+// 4-byte store per value.
 template <int MODE, int MI>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
                                               int n0, int wm, int wn, int lane, float* red, bool active = true,
@@ -213,6 +229,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
   } else if constexpr (MODE == kGateUp) {
     // acc[i][0] = gate, acc[i][1] = up for output column n0 + 32 wn + lane%32
     const int col = n0 + 32 * wn + (lane & 31);
+    float16v hv[MI][1];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -220,14 +237,42 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
         const int r = row_of(i, a);
         const float g = acc[i][0][a], u = acc[i][1][a];
         const float h = g / (1.f + __expf(-g)) * u;
+        hv[i][0][a] = h;
         const bool ok = r < m_rows && col < p.n;
-        if (ok) p.hbuf[(int64_t)(base + r) * p.n + col] = h;
+        if (ok && !vec_scratch) p.hbuf[(int64_t)(base + r) * p.n + col] = h;
         float mx = ok ? __builtin_fabsf(h) : 0.f;
 #pragma unroll
         for (int m = 1; m < 32; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
         if ((lane & 31) == 0 && r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
       }
+    if (vec_scratch) {
+      const int r0 = base + WM * wm;
+      store_tiles_vec<MI, 1>(hv, m_rows - WM * wm, n0 + 32 * wn, p.n, lane, vec_scratch,
+                             [&](int r) __attribute__((always_inline)) { return p.hbuf + (int64_t)(r0 + r) * p.n; });
+    }
   } else {  // kDown
+    if (vec_scratch) {
+      // Lane l looks up row l of the wave's block (its pair and factor); the
+      // accumulator rows take them by shuffle.  Scale in registers (same
+      // products as below), then 16-byte rows into each pair's dbuf row.
+      static_assert(WM <= 64, "one block row per lane");
+      const int rl = min(WM * wm + (lane & (WM - 1)), m_rows - 1);
+      const int pair_l = p.list[base + rl];
+      const float f_l = row_scale_from_max(p.rowmax[base + rl], true) * p.weights[pair_l];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const float f = __shfl(f_l, 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3), 64);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j][a] = acc[i][j][a] * f;
+        }
+      store_tiles_vec<MI, 2>(acc, m_rows - WM * wm, n0 + 64 * wn, p.n, lane, vec_scratch,
+                             [&](int r) __attribute__((always_inline)) {
+                               return p.dbuf + (int64_t)__shfl(pair_l, r, 64) * p.n;
+                             });
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
