@@ -46,6 +46,7 @@
 #define OR_Q8_0 8
 #define OR_Q2_K 10
 #define OR_Q4_K 12
+#define OR_Q5_K 13
 #define OR_Q6_K 14
 
 /* Plant codes are macros: #if compares them in the preprocessor. */
@@ -73,14 +74,16 @@
 #define PLANT_ROUTER_TIE       21  /* ties go to the higher expert index */
 #define PLANT_ROUTER_RENORM    22  /* route weights renormalised over the top-k */
 #define PLANT_MOE_UP           23  /* up projection dropped from the product */
-#define PLANT_COUNT            24
+#define PLANT_Q5_NO_HIGH       24  /* Q5_K qh bit dropped */
+#define PLANT_Q5_HIGH_BIT      25  /* Q5_K qh bit chosen by the nibble half only, not the sub-block */
+#define PLANT_COUNT            26
 
 static const char* const plant_names[PLANT_COUNT] = {
     "none", "q8_unsigned", "q6_no_offset", "q6_no_high", "q4_scale_high",
     "scale_select", "d_for_dmin", "row_stride", "tail", "f16_rtz", "f16_scale",
     "q2_nibbles", "q4_nibble", "q6_shift", "gemm_transpose", "gemm_drop_k",
     "qkn_sum", "qkn_eps", "qkn_gain", "silu_sign", "moe_weight", "router_tie",
-    "router_renorm", "moe_up"};
+    "router_renorm", "moe_up", "q5_no_high", "q5_high_bit"};
 
 int or_plant(void) { return QP_PLANT; }
 int or_plant_count(void) { return PLANT_COUNT; }
@@ -162,7 +165,7 @@ void or_float_to_half_array(const float* src, uint16_t* dst, int64_t n) {
 int64_t or_block_size(int qtype) {
   switch (qtype) {
     case OR_Q8_0: return 32;
-    case OR_Q4_K: case OR_Q6_K: case OR_Q2_K: return 256;
+    case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: case OR_Q2_K: return 256;
     default: return -1;
   }
 }
@@ -171,6 +174,7 @@ int64_t or_type_size(int qtype) {
   switch (qtype) {
     case OR_Q8_0: return 34;
     case OR_Q4_K: return 144;
+    case OR_Q5_K: return 176;
     case OR_Q6_K: return 210;
     case OR_Q2_K: return 84;
     default: return -1;
@@ -265,6 +269,44 @@ static float q4_k_value(const uint8_t* b, int i) {
   return dsc * (float)q - dm;
 }
 
+/* Q5_K: the Q4_K layout with a plane of fifth bits between the scales and
+ * the nibbles: d @0, dmin @2, 12 scale bytes @4 (packed as for Q4_K), qh[32]
+ * @16, qs[128] @48.  Weight i takes its low four bits from qs exactly as in
+ * Q4_K, and its fifth bit from bit i/32 (its sub-block) of qh[i%32].
+ * q = low | fifth << 4, in [0, 31].  w = (d*sc)*q - dmin*m. */
+static float q5_k_value(const uint8_t* b, int i) {
+  float d = f16_at(b), dmin = f16_at(b + 2);
+  const uint8_t* scales = b + 4;
+  const uint8_t* qh = b + 16;
+  const uint8_t* qs = b + 48;
+#if QP_PLANT == PLANT_SCALE_SELECT
+  int j = (i / 32 + 1) % 8;
+#else
+  int j = i / 32;
+#endif
+  int sc, m;
+  q4_k_scale_min(scales, j, &sc, &m);
+  uint8_t byte = qs[32 * (i / 64) + i % 32];
+  int low = (i % 64) >= 32 ? (byte >> 4) : (byte & 15);
+#if QP_PLANT == PLANT_Q5_NO_HIGH
+  int fifth = 0;
+#elif QP_PLANT == PLANT_Q5_HIGH_BIT
+  int fifth = (qh[i % 32] >> ((i % 64) / 32)) & 1;
+#else
+  int fifth = (qh[i % 32] >> (i / 32)) & 1;
+#endif
+  int q = low | (fifth << 4);
+#if QP_PLANT == PLANT_D_FOR_DMIN
+  d = dmin;
+#endif
+  float dsc = d * (float)sc;
+#if QP_PLANT == PLANT_F16_SCALE
+  dsc = through_f16(dsc);
+#endif
+  float dm = dmin * (float)m;
+  return dsc * (float)q - dm;
+}
+
 /* Q6_K: half h = i/128 of the block, r = i%128, quarter c = r/32, l = r%32.
  * Low 4 bits: ql[64h + 32*(c%2) + l], low nibble for c < 2, high for c >= 2.
  * High 2 bits: bits 2c..2c+1 of qh[32h + l].  q = (low | high << 4) - 32.
@@ -340,6 +382,7 @@ static float block_value(int qtype, const uint8_t* b, int i) {
   switch (qtype) {
     case OR_Q8_0: return q8_0_value(b, i);
     case OR_Q4_K: return q4_k_value(b, i);
+    case OR_Q5_K: return q5_k_value(b, i);
     case OR_Q6_K: return q6_k_value(b, i);
     default: return q2_k_value(b, i);
   }

@@ -19,6 +19,7 @@ quants are random, the scale ranges are the workloads' stated ones):
   * fp16 scales d, dmin      : binary16(RNE) of U(1e-3, 1e-2)
   * Q8_0 quants              : integers uniform in [-127, 127]
   * Q4_K 12 scale bytes, qs  : uniform random bytes
+  * Q5_K 12 scale bytes, qh, qs : uniform random bytes
   * Q6_K ql, qh              : uniform random bytes; scales int8 uniform over [-128, 127]
   * Q2_K scales, qs          : uniform random bytes
   * activations X            : N(0, 1), as f32 or rounded to binary16 (RNE)
@@ -28,6 +29,7 @@ quants are random, the scale ranges are the workloads' stated ones):
 Block byte maps (GGUF / ggml on-disk convention; offsets in bytes):
   Q8_0  34 B / 32 weights : d f16 @0, qs int8[32] @2
   Q4_K 144 B / 256        : d f16 @0, dmin f16 @2, scales u8[12] @4, qs u8[128] @16
+  Q5_K 176 B / 256        : d f16 @0, dmin f16 @2, scales u8[12] @4, qh u8[32] @16, qs u8[128] @48
   Q6_K 210 B / 256        : ql u8[128] @0, qh u8[64] @128, scales i8[16] @192, d f16 @208
   Q2_K  84 B / 256        : scales u8[16] @0, qs u8[64] @16, d f16 @80, dmin f16 @82
 A row of `cols` weights is ceil(cols / QK) whole blocks; a tensor is `rows`
@@ -43,9 +45,9 @@ M2 = np.uint64(0x94D049BB133111EB)
 MASK64 = (1 << 64) - 1
 
 # ggml type ids
-Q8_0, Q2_K, Q4_K, Q6_K = 8, 10, 12, 14
-BLOCK = {Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q2_K: (256, 84)}
-NAMES = {Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q2_K: "Q2_K"}
+Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 8, 10, 12, 13, 14
+BLOCK = {Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84)}
+NAMES = {Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K", Q2_K: "Q2_K"}
 BY_NAME = {v: k for k, v in NAMES.items()}
 
 BASE_SEED = 0x9E3779B9
@@ -138,7 +140,7 @@ def quant_weights(qtype: int, rows: int, cols: int, seed: int,
         q = np.floor(uniform(substream(seed, 2), nb * 32) * 255.0).astype(np.int64) - 127
         blocks[:, 2:34] = q.astype(np.int8).view(np.uint8).reshape(nb, 32)
         _put_f16(blocks, 0, d)
-    elif qtype == Q4_K:
+    elif qtype in (Q4_K, Q5_K):
         dmin = f16_bits(uniform_range(substream(seed, 3), nb, scale_lo, scale_hi))
         _put_f16(blocks, 0, d)
         _put_f16(blocks, 2, dmin)

@@ -23,7 +23,7 @@ import os
 import numpy as np
 
 import synth
-from synth import Q8_0, Q4_K, Q6_K, Q2_K
+from synth import Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "hand_blocks.json")
@@ -75,6 +75,21 @@ def enc_q4_k(d_bits: int, dmin_bits: int, sc, m, q) -> np.ndarray:
             qs[idx] |= q[i] & 15
         else:
             qs[idx] |= (q[i] & 15) << 4
+    return b
+
+
+def enc_q5_k(d_bits: int, dmin_bits: int, sc, m, q) -> np.ndarray:
+    """sc, m: 8 six-bit values; q: 256 five-bit values (weight order).  The
+    scales and the low four bits are placed as for Q4_K (qs at byte 48); the
+    fifth bit of weight i is bit i // 32 of qh[i % 32] (qh at byte 16)."""
+    q = np.asarray(q, dtype=np.int64)
+    lo = enc_q4_k(d_bits, dmin_bits, sc, m, q & 15)
+    b = np.zeros(176, np.uint8)
+    b[0:16] = lo[0:16]
+    b[48:176] = lo[16:144]
+    qh = b[16:48]
+    for i in range(256):
+        qh[i % 32] |= ((int(q[i]) >> 4) & 1) << (i // 32)
     return b
 
 
@@ -180,6 +195,26 @@ def pin_sweep_q4_k(o):
             f"Q4_K sweep d={d_bits:#06x} dmin={dmin_bits:#06x}"
 
 
+def pin_sweep_q5_k(o):
+    # every (sc, m) pair once per sub-block; each sub-block holds q = 0..31 once
+    pairs = [(sc, m) for sc in range(64) for m in range(64)]
+    qsub = np.arange(32)
+    for d_bits, dmin_bits in SCALE_PAIRS:
+        raws, want = [], []
+        for bi in range(0, len(pairs), 8):
+            grp = pairs[bi:bi + 8]
+            sc = [p[0] for p in grp]
+            m = [p[1] for p in grp]
+            # rotate the quants per sub-block so every qh bit position meets both values
+            q = np.concatenate([np.roll(qsub, 5 * j + bi // 8) for j in range(8)])
+            raws.append(enc_q5_k(d_bits, dmin_bits, sc, m, q))
+            want.append(_closed_form_f32(d_bits, dmin_bits, np.repeat(sc, 32), q, np.repeat(m, 32)))
+        raw = np.concatenate(raws)
+        got = o.dequant_f32(Q5_K, raw, len(raws), 256).reshape(-1)
+        assert np.array_equal(f32_bits(got), f32_bits(np.concatenate(want))), \
+            f"Q5_K sweep d={d_bits:#06x} dmin={dmin_bits:#06x}"
+
+
 def pin_sweep_q6_k(o):
     # every signed scale with every quant in [-32, 31]
     qgrp = np.arange(-32, 32)
@@ -223,6 +258,13 @@ def pin_positions(o):
     got = o.dequant_f32(Q4_K, enc_q4_k(d_bits, dmin_bits, sc, m, q), 1, 256)[0]
     want = _closed_form_f32(d_bits, dmin_bits, np.repeat(sc, 32), q, np.repeat(m, 32))
     assert np.array_equal(f32_bits(got), f32_bits(want)), "Q4_K positions"
+    # Q5_K
+    sc = rng.integers(0, 64, 8)
+    m = rng.integers(0, 64, 8)
+    q = rng.integers(0, 32, 256)
+    got = o.dequant_f32(Q5_K, enc_q5_k(d_bits, dmin_bits, sc, m, q), 1, 256)[0]
+    want = _closed_form_f32(d_bits, dmin_bits, np.repeat(sc, 32), q, np.repeat(m, 32))
+    assert np.array_equal(f32_bits(got), f32_bits(want)), "Q5_K positions"
     # Q6_K
     sc = rng.integers(-128, 128, 16)
     q = rng.integers(-32, 32, 256)
@@ -244,7 +286,7 @@ def pin_positions(o):
 
 def pin_f16_from_f32(o):
     """The f16 copy is numpy's RNE binary16 of the f32 dequant (random blocks)."""
-    for qt in (Q8_0, Q4_K, Q6_K, Q2_K):
+    for qt in (Q8_0, Q4_K, Q5_K, Q6_K, Q2_K):
         cols = 512
         raw = synth.quant_weights(qt, 3, cols, synth.seed_for(90, qt))
         f32 = o.dequant_f32(qt, raw, 3, cols)
@@ -267,7 +309,7 @@ def pin_f16_convert_edges(o):
 def pin_partial_rows(o):
     """Rows of a tensor with a partial last block: each row is the prefix of
     its own blocks decoded as a full row; no write lands outside rows x cols."""
-    for qt in (Q8_0, Q4_K, Q6_K, Q2_K):
+    for qt in (Q8_0, Q4_K, Q5_K, Q6_K, Q2_K):
         qk, ts = synth.BLOCK[qt]
         tails = [1, 3, 5, 17, 31] if qt == Q8_0 else [1, 16, 77, 129, 255]
         for tail in tails:
@@ -332,7 +374,8 @@ def pin_gemm_identity(o):
 
 def pin_gemm_matmul(o):
     """Against numpy's float64 matmul of the (separately pinned) f32 dequant."""
-    for qt, n, k, t in ((Q4_K, 48, 512, 5), (Q6_K, 33, 256, 3), (Q2_K, 17, 768, 4), (Q8_0, 40, 96, 7)):
+    for qt, n, k, t in ((Q4_K, 48, 512, 5), (Q5_K, 21, 512, 6), (Q6_K, 33, 256, 3), (Q2_K, 17, 768, 4),
+                        (Q8_0, 40, 96, 7)):
         raw = synth.quant_weights(qt, n, k, synth.seed_for(92, qt))
         x = synth.activations_f16(t, k, synth.seed_for(93, qt))
         w = o.dequant_f32(qt, raw, n, k).astype(np.float64)
