@@ -9,7 +9,8 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.
 `value` is the projection TFLOP/s (sum of algorithmic flops over the
 sum of the projection launches' HIP-event durations); the dequant GB/s is
 reported beside it.  After the timed region the remaining workloads -- the
-Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the fused
+Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the Q5_K
+Qwen3-8B layer at T = 2048 (projections one by one), the fused
 QK-norm projections at T = 8192 and the routed 128-expert FFN -- are timed
 and reported under "rows".
 """
@@ -203,6 +204,23 @@ def other_rows(torch, synth, qp, iters):
         dbytes += n * synth.row_bytes(synth.Q4_K, k) + 4.0 * n * k
     rows["q4_k_qwen3_1p7b_t512"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
                                         dequant_f32_gbps=dbytes / dms / 1e6)
+    # Q5_K, Qwen3-8B layer at T = 2048 (the seven projections, each on its own)
+    flops, tms, dbytes, dms = 0.0, 0.0, 0.0, 0.0
+    x8 = {}
+    for i, (name, n, k) in enumerate(synth.PROJ_8B):
+        if k not in x8:
+            x8[k] = d(synth.activations_f16(2048, k, synth.seed_for(2, 500 + k // 256))).view(torch.float16)
+        w = d(synth.quant_weights(synth.Q5_K, n, k, synth.seed_for(2, 10 * synth.Q5_K + i)))
+        y = torch.empty((2048, n), device=dev)
+        tms += time_fn(torch, lambda: qp.prefill_gemm(synth.Q5_K, w, n, k, x8[k], out=y), iters)
+        flops += 2.0 * 2048 * n * k
+        o32 = torch.empty((n, k), device=dev)
+        dms += time_fn(torch, lambda: qp.dequant_f32(synth.Q5_K, w, n, k, out=o32), iters)
+        dbytes += n * synth.row_bytes(synth.Q5_K, k) + 4.0 * n * k
+        del w, y, o32
+    rows["q5_k_qwen3_8b_t2048"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
+                                       dequant_f32_gbps=dbytes / dms / 1e6)
+    del x8
     # fused QK norm, T = 8192
     t = 8192
     x = d(synth.activations_f16(t, 4096, synth.seed_for(3, 0))).view(torch.float16)

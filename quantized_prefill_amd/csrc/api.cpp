@@ -34,7 +34,7 @@ qp_status from_hip(hipError_t e, const char* what) {
 }
 
 bool supported(int qtype) {
-  return qtype == QP_Q8_0 || qtype == QP_Q4_K || qtype == QP_Q6_K || qtype == QP_Q2_K;
+  return qtype == QP_Q8_0 || qtype == QP_Q4_K || qtype == QP_Q5_K || qtype == QP_Q6_K || qtype == QP_Q2_K;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -48,7 +48,7 @@ extern "C" {
 int64_t qp_block_size(int qtype) {
   switch (qtype) {
     case QP_Q8_0: return 32;
-    case QP_Q4_K: case QP_Q6_K: case QP_Q2_K: return 256;
+    case QP_Q4_K: case QP_Q5_K: case QP_Q6_K: case QP_Q2_K: return 256;
     default: return -1;
   }
 }
@@ -57,6 +57,7 @@ int64_t qp_type_size(int qtype) {
   switch (qtype) {
     case QP_Q8_0: return 34;
     case QP_Q4_K: return 144;
+    case QP_Q5_K: return 176;
     case QP_Q6_K: return 210;
     case QP_Q2_K: return 84;
     default: return -1;

@@ -133,6 +133,8 @@ hipError_t launch_dequant(int qtype, bool f16out, const void* src, int64_t rows,
                               : launch_dequant_t<kQ8_0, false>(src, rows, cols, dst, s);
     case kQ4_K: return f16out ? launch_dequant_t<kQ4_K, true>(src, rows, cols, dst, s)
                               : launch_dequant_t<kQ4_K, false>(src, rows, cols, dst, s);
+    case kQ5_K: return f16out ? launch_dequant_t<kQ5_K, true>(src, rows, cols, dst, s)
+                              : launch_dequant_t<kQ5_K, false>(src, rows, cols, dst, s);
     case kQ6_K: return f16out ? launch_dequant_t<kQ6_K, true>(src, rows, cols, dst, s)
                               : launch_dequant_t<kQ6_K, false>(src, rows, cols, dst, s);
     case kQ2_K: return f16out ? launch_dequant_t<kQ2_K, true>(src, rows, cols, dst, s)

@@ -192,6 +192,7 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
   switch (qtype) {
     case kQ8_0: hipLaunchKernelGGL((gemm_kernel<kQ8_0, MODE>), grid, dim3(NT), 0, s, p); break;
     case kQ4_K: hipLaunchKernelGGL((gemm_kernel<kQ4_K, MODE>), grid, dim3(NT), 0, s, p); break;
+    case kQ5_K: hipLaunchKernelGGL((gemm_kernel<kQ5_K, MODE>), grid, dim3(NT), 0, s, p); break;
     case kQ6_K: hipLaunchKernelGGL((gemm_kernel<kQ6_K, MODE>), grid, dim3(NT), 0, s, p); break;
     case kQ2_K: hipLaunchKernelGGL((gemm_kernel<kQ2_K, MODE>), grid, dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;

@@ -294,6 +294,7 @@ static inline int64_t row_bytes_of(int qtype, int64_t cols) {
   switch (qtype) {
     case kQ8_0: return (cols + 31) / 32 * 34;
     case kQ4_K: return (cols + 255) / 256 * 144;
+    case kQ5_K: return (cols + 255) / 256 * 176;
     case kQ6_K: return (cols + 255) / 256 * 210;
     case kQ2_K: return (cols + 255) / 256 * 84;
     default: return -1;

@@ -50,6 +50,7 @@ constexpr int TMI = TBM / 2 / 32;  // MFMA tiles per wave along M
 // per row (RSD >= (UB + 2 + 3) / 4, odd).
 template <int QT> struct StageUnit;
 template <> struct StageUnit<kQ4_K> { static constexpr int KW = 256, UB = 144, RSD = 37; };
+template <> struct StageUnit<kQ5_K> { static constexpr int KW = 256, UB = 176, RSD = 45; };
 template <> struct StageUnit<kQ6_K> { static constexpr int KW = 256, UB = 210, RSD = 53; };
 template <> struct StageUnit<kQ2_K> { static constexpr int KW = 256, UB = 84, RSD = 21; };
 template <> struct StageUnit<kQ8_0> { static constexpr int KW = 128, UB = 136, RSD = 35; };
@@ -126,6 +127,23 @@ template <> __device__ __forceinline__ void staged_unit<kQ4_K>(const uint32_t* r
   const uint32_t sh = 4 * (u & 1);
 #pragma unroll
   for (int j = 0; j < 8; ++j) r.code[j] = (qs[j] >> sh) & 0x0F0F0F0Fu;
+  const float dsc = __fmul_rn(d, (float)sc);
+  const float dm = __fmul_rn(dmin, (float)m);
+  r.a0 = r.a1 = dsc;
+  r.b0 = r.b1 = dm;
+  r.sm0 = r.sm1 = dm;
+}
+
+template <> __device__ __forceinline__ void staged_unit<kQ5_K>(const uint32_t* row, uint32_t, uint32_t u, UnitRaw& r) {
+  const uint32_t h0 = row[0], s0 = row[1], s1 = row[2], s2 = row[3];  // 176-byte blocks: delta is 0
+  const float d = f16_to_f32(h0 & 0xFFFFu), dmin = f16_to_f32(h0 >> 16);
+  uint32_t sc, m;
+  q4k_scale_min(s0, s1, s2, u, sc, m);
+  const uint32_t* qh = row + 4;
+  const uint32_t* qs = row + 12 + 8 * (u >> 1);
+  const uint32_t sh = 4 * (u & 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.code[j] = ((qs[j] >> sh) & 0x0F0F0F0Fu) | (((qh[j] >> u) & 0x01010101u) << 4);
   const float dsc = __fmul_rn(d, (float)sc);
   const float dm = __fmul_rn(dmin, (float)m);
   r.a0 = r.a1 = dsc;
@@ -529,6 +547,7 @@ hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p,
   switch (qtype) {
     case kQ8_0: QP_TALL(kQ8_0) break;
     case kQ4_K: QP_TALL(kQ4_K) break;
+    case kQ5_K: QP_TALL(kQ5_K) break;
     case kQ6_K: QP_TALL(kQ6_K) break;
     case kQ2_K: QP_TALL(kQ2_K) break;
     default: return hipErrorInvalidValue;

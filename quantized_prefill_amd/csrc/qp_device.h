@@ -9,6 +9,8 @@
 //   Q4_K 144 B / 256 : d @0, dmin @2, 12 packed 6-bit (sc, m) @4, qs[128] @16
 //                      w = (d*sc)*q - dmin*m, q the nibble of qs[32*(i/64) + i%32]
 //                      (low nibble for i%64 < 32), sub-block i/32
+//   Q5_K 176 B / 256 : d @0, dmin @2, 12 packed (sc, m) @4, qh[32] @16, qs[128] @48
+//                      w = (d*sc)*q - dmin*m, q = the Q4_K nibble | bit i/32 of qh[i%32] << 4
 //   Q6_K 210 B / 256 : ql[128] @0, qh[64] @128, int8 scales[16] @192, d @208
 //                      w = (d*sc[i/16])*(q-32), q = low4 | hi2 << 4
 //   Q2_K  84 B / 256 : scales[16] @0 (sc low nibble, m high), qs[64] @16, d @80, dmin @82
@@ -25,11 +27,12 @@
 
 namespace qp {
 
-constexpr int kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ6_K = 14;
+constexpr int kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14;
 
 template <int QT> struct Fmt;
 template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, TS = 34, UNITS = 1; };
 template <> struct Fmt<kQ4_K> { static constexpr int QK = 256, TS = 144, UNITS = 8; };
+template <> struct Fmt<kQ5_K> { static constexpr int QK = 256, TS = 176, UNITS = 8; };
 template <> struct Fmt<kQ6_K> { static constexpr int QK = 256, TS = 210, UNITS = 8; };
 template <> struct Fmt<kQ2_K> { static constexpr int QK = 256, TS = 84, UNITS = 8; };
 
@@ -181,6 +184,38 @@ template <> struct Raw<kQ4_K> {
   }
 };
 
+// Q5_K: the code of a weight is its Q4_K nibble plus the fifth bit, which for
+// all 32 weights of unit u is bit u of their qh bytes (qh byte l serves weight
+// l of every unit).
+template <> struct Raw<kQ5_K> {
+  u32x4 hdr, h0, h1, q0, q1;
+  uint32_t u;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
+    u = u_;
+    hdr = *(const u32x4*)blk;  // 176-byte blocks keep 16-byte alignment
+    h0 = *(const u32x4*)(blk + 16);
+    h1 = *(const u32x4*)(blk + 32);
+    const u32x4* qs = (const u32x4*)(blk + 48 + 32 * (u_ >> 1));
+    q0 = qs[0];
+    q1 = qs[1];
+  }
+  __device__ __forceinline__ void finish(UnitRaw& r) const {
+    const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
+    uint32_t sc, m;
+    q4k_scale_min(hdr.y, hdr.z, hdr.w, u, sc, m);
+    const uint32_t sh = 4 * (u & 1);
+    const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const uint32_t hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.code[j] = ((qq[j] >> sh) & 0x0F0F0F0Fu) | (((hh[j] >> u) & 0x01010101u) << 4);
+    const float dsc = __fmul_rn(d, (float)sc);
+    const float dm = __fmul_rn(dmin, (float)m);
+    r.a0 = r.a1 = dsc;
+    r.b0 = r.b1 = dm;
+    r.sm0 = r.sm1 = dm;
+  }
+};
+
 template <> struct Raw<kQ6_K> {
   uint32_t ql[9], qh[9], shl_a, shh_a, scp, d16, u;
   __device__ __forceinline__ void load(const uint8_t* blk, uint32_t u_) {
@@ -295,6 +330,32 @@ template <int V> struct Span<kQ4_K, V> {
     uint32_t sc, m;
     q4k_scale_min(hdr.y, hdr.z, hdr.w, j, sc, m);
     const uint32_t code = (q[i / 4] >> (8 * (i & 3) + 4 * (j & 1))) & 15u;
+    const float dsc = __fmul_rn(f16_to_f32(hdr.x & 0xFFFFu), (float)sc);
+    const float dm = __fmul_rn(f16_to_f32(hdr.x >> 16), (float)m);
+    return __fsub_rn(__fmul_rn(dsc, (float)code), dm);
+  }
+};
+
+template <int V> struct Span<kQ5_K, V> {
+  static constexpr int N = V / 4;
+  u32x4 hdr;
+  uint32_t q[N], h[N], j;
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t i0) {
+    hdr = *(const u32x4*)blk;
+    j = i0 / 32;
+    const uint32_t* qs = (const uint32_t*)(blk + 48 + 32 * (i0 / 64) + (i0 % 32));
+    const uint32_t* qh = (const uint32_t*)(blk + 16 + (i0 % 32));
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      q[k] = qs[k];
+      h[k] = qh[k];
+    }
+  }
+  __device__ __forceinline__ float value(int i) const {
+    uint32_t sc, m;
+    q4k_scale_min(hdr.y, hdr.z, hdr.w, j, sc, m);
+    const uint32_t b = 8 * (i & 3);
+    const uint32_t code = ((q[i / 4] >> (b + 4 * (j & 1))) & 15u) | (((h[i / 4] >> (b + j)) & 1u) << 4);
     const float dsc = __fmul_rn(f16_to_f32(hdr.x & 0xFFFFu), (float)sc);
     const float dm = __fmul_rn(f16_to_f32(hdr.x >> 16), (float)m);
     return __fsub_rn(__fmul_rn(dsc, (float)code), dm);

@@ -8,11 +8,11 @@ import pins
 import synth
 import quantized_prefill_amd as qp
 from gpu_helpers import GUARD, NAN16, NAN32, say, to_dev, weights
-from synth import Q8_0, Q4_K, Q6_K, Q2_K
+from synth import Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 pytestmark = pytest.mark.gpu
 
-QTYPES = [Q8_0, Q4_K, Q6_K, Q2_K]
+QTYPES = [Q8_0, Q4_K, Q5_K, Q6_K, Q2_K]
 
 
 def gpu_dequant(qtype, raw: np.ndarray, rows: int, cols: int, f16: bool):
@@ -65,6 +65,9 @@ def test_hand_blocks_and_sweeps(orc, qtype):
             elif qtype == Q4_K:
                 blocks.append(pins.enc_q4_k(d_bits, dmin_bits, rng.integers(0, 64, 8), rng.integers(0, 64, 8),
                                             rng.integers(0, 16, 256)))
+            elif qtype == Q5_K:
+                blocks.append(pins.enc_q5_k(d_bits, dmin_bits, rng.integers(0, 64, 8), rng.integers(0, 64, 8),
+                                            rng.integers(0, 32, 256)))
             elif qtype == Q6_K:
                 blocks.append(pins.enc_q6_k(d_bits, rng.integers(-128, 128, 16), rng.integers(-32, 32, 256)))
             else:
@@ -124,6 +127,9 @@ def _config_tensors():
     for qt in (Q6_K, Q2_K):
         for i, (name, n, k) in enumerate(synth.PROJ_8B):
             out.append((f"8b_{name}_{synth.NAMES[qt]}", qt, n, k, synth.seed_for(2, 10 * qt + i)))
+    for i, (name, n, k) in enumerate(synth.PROJ_8B):
+        if name in ("q", "gate"):
+            out.append((f"8b_{name}_Q5_K", Q5_K, n, k, synth.seed_for(2, 10 * Q5_K + i)))
     out.append(("qknorm_wq", Q4_K, 4096, 4096, synth.seed_for(3, 1)))
     out.append(("qknorm_wk", Q6_K, 1024, 4096, synth.seed_for(3, 2)))
     return out
