@@ -43,6 +43,7 @@
 #define QP_PLANT 0
 #endif
 
+#define OR_F16 1
 #define OR_Q8_0 8
 #define OR_Q2_K 10
 #define OR_Q4_K 12
@@ -76,14 +77,15 @@
 #define PLANT_MOE_UP           23  /* up projection dropped from the product */
 #define PLANT_Q5_NO_HIGH       24  /* Q5_K qh bit dropped */
 #define PLANT_Q5_HIGH_BIT      25  /* Q5_K qh bit chosen by the nibble half only, not the sub-block */
-#define PLANT_COUNT            26
+#define PLANT_F16W_BYTES       26  /* F16 weights read big-endian */
+#define PLANT_COUNT            27
 
 static const char* const plant_names[PLANT_COUNT] = {
     "none", "q8_unsigned", "q6_no_offset", "q6_no_high", "q4_scale_high",
     "scale_select", "d_for_dmin", "row_stride", "tail", "f16_rtz", "f16_scale",
     "q2_nibbles", "q4_nibble", "q6_shift", "gemm_transpose", "gemm_drop_k",
     "qkn_sum", "qkn_eps", "qkn_gain", "silu_sign", "moe_weight", "router_tie",
-    "router_renorm", "moe_up", "q5_no_high", "q5_high_bit"};
+    "router_renorm", "moe_up", "q5_no_high", "q5_high_bit", "f16w_bytes"};
 
 int or_plant(void) { return QP_PLANT; }
 int or_plant_count(void) { return PLANT_COUNT; }
@@ -164,6 +166,7 @@ void or_float_to_half_array(const float* src, uint16_t* dst, int64_t n) {
 
 int64_t or_block_size(int qtype) {
   switch (qtype) {
+    case OR_F16: return 1;
     case OR_Q8_0: return 32;
     case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: case OR_Q2_K: return 256;
     default: return -1;
@@ -172,6 +175,7 @@ int64_t or_block_size(int qtype) {
 
 int64_t or_type_size(int qtype) {
   switch (qtype) {
+    case OR_F16: return 2;
     case OR_Q8_0: return 34;
     case OR_Q4_K: return 144;
     case OR_Q5_K: return 176;
@@ -202,6 +206,16 @@ static float through_f16(float v) { return or_half_to_float(or_float_to_half(v))
 
 /* ------------------------------------------------------------------------ */
 /* per-type value of weight i (0 <= i < QK) of one block                     */
+
+/* F16 weights (ggml type 1): each "block" is one little-endian binary16
+ * value, and the weight is that value (widening to binary32 is exact). */
+static float f16w_value(const uint8_t* b) {
+#if QP_PLANT == PLANT_F16W_BYTES
+  return or_half_to_float((uint16_t)((b[0] << 8) | b[1]));
+#else
+  return f16_at(b);
+#endif
+}
 
 /* Q8_0: w = d * q, q the signed byte qs[i]. */
 static float q8_0_value(const uint8_t* b, int i) {
@@ -380,6 +394,7 @@ static float q2_k_value(const uint8_t* b, int i) {
 
 static float block_value(int qtype, const uint8_t* b, int i) {
   switch (qtype) {
+    case OR_F16: return f16w_value(b);
     case OR_Q8_0: return q8_0_value(b, i);
     case OR_Q4_K: return q4_k_value(b, i);
     case OR_Q5_K: return q5_k_value(b, i);

@@ -22,11 +22,13 @@ quants are random, the scale ranges are the workloads' stated ones):
   * Q5_K 12 scale bytes, qh, qs : uniform random bytes
   * Q6_K ql, qh              : uniform random bytes; scales int8 uniform over [-128, 127]
   * Q2_K scales, qs          : uniform random bytes
+  * F16 weights              : binary16 (RNE) of N(0, 1) * 2^-6
   * activations X            : N(0, 1), as f32 or rounded to binary16 (RNE)
   * QK-norm gains            : f32 U(0.5, 1.5)
   * router logits            : f32 N(0, 1)
 
 Block byte maps (GGUF / ggml on-disk convention; offsets in bytes):
+  F16    2 B / 1 weight   : the weight as little-endian binary16
   Q8_0  34 B / 32 weights : d f16 @0, qs int8[32] @2
   Q4_K 144 B / 256        : d f16 @0, dmin f16 @2, scales u8[12] @4, qs u8[128] @16
   Q5_K 176 B / 256        : d f16 @0, dmin f16 @2, scales u8[12] @4, qh u8[32] @16, qs u8[128] @48
@@ -45,9 +47,9 @@ M2 = np.uint64(0x94D049BB133111EB)
 MASK64 = (1 << 64) - 1
 
 # ggml type ids
-Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 8, 10, 12, 13, 14
-BLOCK = {Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84)}
-NAMES = {Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K", Q2_K: "Q2_K"}
+F16W, Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 1, 8, 10, 12, 13, 14
+BLOCK = {F16W: (1, 2), Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84)}
+NAMES = {F16W: "F16", Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K", Q2_K: "Q2_K"}
 BY_NAME = {v: k for k, v in NAMES.items()}
 
 BASE_SEED = 0x9E3779B9
@@ -133,6 +135,8 @@ def quant_weights(qtype: int, rows: int, cols: int, seed: int,
                   scale_lo: float = 1e-3, scale_hi: float = 1e-2) -> np.ndarray:
     """A rows x cols weight tensor in `qtype` blocks, as a flat uint8 array."""
     qk, ts = BLOCK[qtype]
+    if qtype == F16W:
+        return f16_bits(normal(seed, rows * cols) * 2.0 ** -6).view(np.uint8).reshape(-1)
     nb = rows * nblocks(qtype, cols)
     blocks = random_bytes(substream(seed, 0), nb * ts).reshape(nb, ts)
     d = f16_bits(uniform_range(substream(seed, 1), nb, scale_lo, scale_hi))

@@ -23,7 +23,7 @@ import os
 import numpy as np
 
 import synth
-from synth import Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
+from synth import F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "hand_blocks.json")
@@ -286,12 +286,28 @@ def pin_positions(o):
 
 def pin_f16_from_f32(o):
     """The f16 copy is numpy's RNE binary16 of the f32 dequant (random blocks)."""
-    for qt in (Q8_0, Q4_K, Q5_K, Q6_K, Q2_K):
+    for qt in (F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K):
         cols = 512
         raw = synth.quant_weights(qt, 3, cols, synth.seed_for(90, qt))
         f32 = o.dequant_f32(qt, raw, 3, cols)
         f16 = o.dequant_f16_bits(qt, raw, 3, cols)
         assert np.array_equal(f16, f32.astype(np.float16).view(np.uint16)), f"f16 copy {qt}"
+
+
+def pin_f16_weights(o):
+    """F16 weights: every binary16 pattern, laid out little-endian, widens to
+    numpy's float32 of it (NaN stays NaN), in one row and as a 256 x 256
+    tensor; the f16 copy gives back the same bits for every non-NaN pattern."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    raw = bits.astype("<u2").view(np.uint8)
+    want = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    for rows, cols in ((1, 1 << 16), (256, 256)):
+        got = o.dequant_f32(F16W, raw, rows, cols).reshape(-1)
+        assert np.array_equal(np.isnan(got), nan), "F16 weights: NaN patterns"
+        assert np.array_equal(f32_bits(got[~nan]), f32_bits(want[~nan])), f"F16 weights {rows}x{cols}"
+        g16 = o.dequant_f16_bits(F16W, raw, rows, cols).reshape(-1)
+        assert np.array_equal(g16[~nan], bits[~nan]), "F16 weights: f16 copy"
 
 
 def pin_f16_convert_edges(o):
@@ -374,7 +390,7 @@ def pin_gemm_identity(o):
 
 def pin_gemm_matmul(o):
     """Against numpy's float64 matmul of the (separately pinned) f32 dequant."""
-    for qt, n, k, t in ((Q4_K, 48, 512, 5), (Q5_K, 21, 512, 6), (Q6_K, 33, 256, 3), (Q2_K, 17, 768, 4),
+    for qt, n, k, t in ((F16W, 9, 256, 3), (Q4_K, 48, 512, 5), (Q5_K, 21, 512, 6), (Q6_K, 33, 256, 3), (Q2_K, 17, 768, 4),
                         (Q8_0, 40, 96, 7)):
         raw = synth.quant_weights(qt, n, k, synth.seed_for(92, qt))
         x = synth.activations_f16(t, k, synth.seed_for(93, qt))
