@@ -288,6 +288,43 @@ def cpu_baseline(synth, budget_s: float):
                        f"binary64 dot products over the oracle's f32 dequant; {dt:.1f} s")
 
 
+def two_pass_row(torch, synth, qp, L, iters):
+    """The f16-cache mode as a comparator: the Q6_K layer's weights are
+    dequantized once to binary16 (qp.dequant_f16), then the same projections
+    run as plain F16-weight products.  Reported beside the dequant-on-load
+    time of the same calls: the products alone on the cached weights, the
+    whole two passes, and the memory each form of the weights takes."""
+    qt = synth.Q6_K
+    pr = {p["name"]: p for p in L["projs"] if p["qtype"] == qt}
+    cache = {nm: torch.empty((p["n"], p["k"]), dtype=torch.float16, device="cuda") for nm, p in pr.items()}
+
+    def deq():
+        for nm, p in pr.items():
+            qp.dequant_f16(qt, p["w"], p["n"], p["k"], out=cache[nm])
+
+    def gemms(wt, ws):
+        q, k, v = pr["q"], pr["k"], pr["v"]
+        qp.prefill_gemm_qkv(wt, ws["q"], q["n"], ws["k"], k["n"], ws["v"], v["n"], q["k"], L["xs"][q["k"]], 128,
+                            L["gains"]["q"], L["gains"]["k"], out_q=q["y"], out_k=k["y"], out_v=v["y"])
+        for nm in ("o", "gate", "up", "down"):
+            p = pr[nm]
+            qp.prefill_gemm(wt, ws[nm], p["n"], p["k"], L["xs"][p["k"]], out=p["y"])
+
+    quant = {nm: p["w"] for nm, p in pr.items()}
+    flops = sum(2.0 * L["t"] * p["n"] * p["k"] for p in pr.values())
+    ms_load = time_fn(torch, lambda: gemms(qt, quant), iters)
+    deq()
+    ms_cached = time_fn(torch, lambda: gemms(qp.F16W, cache), iters)
+    ms_deq = time_fn(torch, deq, iters)
+    row = dict(dequant_on_load_tflops=flops / ms_load / 1e9, dequant_on_load_us=ms_load * 1e3,
+               f16_cache_gemm_tflops=flops / ms_cached / 1e9, f16_cache_gemm_us=ms_cached * 1e3,
+               f16_cache_dequant_us=ms_deq * 1e3, two_pass_us=(ms_deq + ms_cached) * 1e3,
+               weights_mb_quantized=sum(p["w"].numel() for p in pr.values()) / 1e6,
+               weights_mb_f16_cache=sum(c.numel() * 2 for c in cache.values()) / 1e6)
+    del cache
+    return row
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,11 +410,16 @@ def main():
             "avg_launch_us": round(dom_ms * 1e3, 2),
         },
     }
+    if not args.no_rows:
+        print("bench: f16-cache comparator", file=sys.stderr, flush=True)
+        two_pass = two_pass_row(torch, synth, qp, L, 10)
     del L
     torch.cuda.empty_cache()
     if not args.no_rows:
         print("bench: other workloads", file=sys.stderr, flush=True)
-        res["rows"] = {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in other_rows(torch, synth, qp, 10).items()}
+        rows = other_rows(torch, synth, qp, 10)
+        rows["two_pass_f16_cache_q6_k_qwen3_8b_t2048"] = two_pass
+        res["rows"] = {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in rows.items()}
     if not args.no_cpu:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(synth, args.cpu_budget)

@@ -31,6 +31,7 @@
  *     nothing is launched and no output is written.  There is no CPU
  *     fallback for any operation.
  *   - Block layouts (GGUF / ggml on-disk convention, little-endian fp16):
+ *       F16    2 B per weight      : the weight as binary16 (ggml type 1);  w = that value
  *       Q8_0  34 B per 32 weights  : d f16 @0, qs int8[32] @2;  w = d*q
  *       Q4_K 144 B per 256 weights : d f16 @0, dmin f16 @2, 12 bytes of packed
  *                                    6-bit (scale, min) for 8 sub-blocks of 32 @4,
@@ -63,19 +64,19 @@ extern "C" {
 typedef enum {
   QP_OK = 0,
   QP_ERR_INVALID_PARAMETER = 1,   /* bad size, stride, alignment, pointer or option */
-  QP_ERR_UNSUPPORTED_TYPE = 2,    /* qtype is not Q8_0, Q4_K, Q5_K, Q6_K or Q2_K */
+  QP_ERR_UNSUPPORTED_TYPE = 2,    /* qtype is not F16, Q8_0, Q4_K, Q5_K, Q6_K or Q2_K */
   QP_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the size query */
   QP_ERR_DEVICE = 4               /* the HIP runtime reported an error at launch */
 } qp_status;
 
-typedef enum { QP_Q8_0 = 8, QP_Q2_K = 10, QP_Q4_K = 12, QP_Q5_K = 13, QP_Q6_K = 14 } qp_qtype;
+typedef enum { QP_F16W = 1, QP_Q8_0 = 8, QP_Q2_K = 10, QP_Q4_K = 12, QP_Q5_K = 13, QP_Q6_K = 14 } qp_qtype;
 
 typedef enum { QP_F32 = 0, QP_F16 = 1 } qp_dtype;
 
-/* Weights per block: 32 (Q8_0) or 256 (K types); -1 for an unsupported type. */
+/* Weights per block: 1 (F16), 32 (Q8_0) or 256 (K types); -1 for an unsupported type. */
 int64_t qp_block_size(int qtype);
 
-/* Bytes per block: 34, 144, 176, 210, 84; -1 for an unsupported type. */
+/* Bytes per block: 2, 34, 144, 176, 210, 84; -1 for an unsupported type. */
 int64_t qp_type_size(int qtype);
 
 /* Bytes of one row of `cols` weights: ceil(cols / QK) * type_size.
@@ -91,7 +92,7 @@ int64_t qp_row_bytes(int qtype, int64_t cols);
  *                 are written: the unused quants of a partial last block are
  *                 ignored.
  * Values are computed in binary32, left to right, nearest-even:
- *   Q8_0 d*q;  Q4_K, Q5_K, Q2_K (d*sc)*q - dmin*m;  Q6_K (d*sc)*(q-32).
+ *   F16 the value itself;  Q8_0 d*q;  Q4_K, Q5_K, Q2_K (d*sc)*q - dmin*m;  Q6_K (d*sc)*(q-32).
  * rows == 0 is a no-op.  Errors: QP_ERR_UNSUPPORTED_TYPE, or
  * QP_ERR_INVALID_PARAMETER for rows < 0, cols <= 0, a NULL or misaligned
  * pointer.

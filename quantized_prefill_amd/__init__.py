@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqprefill.so")
 
-Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 8, 10, 12, 13, 14
+F16W, Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 1, 8, 10, 12, 13, 14
 F32, F16 = 0, 1
 
 STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_PARAMETER", 2: "QP_ERR_UNSUPPORTED_TYPE",

@@ -34,7 +34,8 @@ qp_status from_hip(hipError_t e, const char* what) {
 }
 
 bool supported(int qtype) {
-  return qtype == QP_Q8_0 || qtype == QP_Q4_K || qtype == QP_Q5_K || qtype == QP_Q6_K || qtype == QP_Q2_K;
+  return qtype == QP_F16W || qtype == QP_Q8_0 || qtype == QP_Q4_K || qtype == QP_Q5_K || qtype == QP_Q6_K ||
+         qtype == QP_Q2_K;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -47,6 +48,7 @@ extern "C" {
 
 int64_t qp_block_size(int qtype) {
   switch (qtype) {
+    case QP_F16W: return 1;
     case QP_Q8_0: return 32;
     case QP_Q4_K: case QP_Q5_K: case QP_Q6_K: case QP_Q2_K: return 256;
     default: return -1;
@@ -55,6 +57,7 @@ int64_t qp_block_size(int qtype) {
 
 int64_t qp_type_size(int qtype) {
   switch (qtype) {
+    case QP_F16W: return 2;
     case QP_Q8_0: return 34;
     case QP_Q4_K: return 144;
     case QP_Q5_K: return 176;
@@ -79,9 +82,7 @@ static qp_status dequant_common(int qtype, const void* src, int64_t rows, int64_
   if (!src || !dst) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
   if (!aligned(src, 16)) return fail(QP_ERR_INVALID_PARAMETER, "src must be 16-byte aligned");
   if (!aligned(dst, f16 ? 2 : 4)) return fail(QP_ERR_INVALID_PARAMETER, "dst misaligned");
-  const int64_t qk = qp_block_size(qtype);
-  const int64_t units = rows * ((cols + qk - 1) / qk) * (qk / 32);
-  if (units > ((int64_t)1 << 40)) return fail(QP_ERR_INVALID_PARAMETER, "tensor too large");
+  if (rows * cols > ((int64_t)1 << 40)) return fail(QP_ERR_INVALID_PARAMETER, "tensor too large");
   return from_hip(qp::launch_dequant(qtype, f16, src, rows, cols, dst, stream), "dequant launch");
 }
 

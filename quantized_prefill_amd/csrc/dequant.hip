@@ -106,6 +106,47 @@ __global__ __launch_bounds__(256) void dequant_flat_kernel(const uint8_t* __rest
   }
 }
 
+// F16 weights (one binary16 per weight): the f32 output is the exact
+// widening, the f16 output the nearest-even binary16 of that f32 value (the
+// same bits, NaN payloads aside).  A thread owns 8 consecutive weights: one
+// 16-byte load and 16-byte stores where the run is whole and aligned, else
+// element by element.
+template <bool F16OUT>
+__global__ __launch_bounds__(256) void dequant_f16w_kernel(const uint16_t* __restrict__ src, uint64_t total,
+                                                           void* __restrict__ dst_) {
+  const uint64_t i0 = 8 * ((uint64_t)blockIdx.x * 256u + threadIdx.x);
+  if (i0 >= total) return;
+  const bool vec = i0 + 8 <= total && (((uintptr_t)dst_ | (uintptr_t)src) & 15) == 0;
+  if (vec) {
+    const u32x4 v = *(const u32x4*)(src + i0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = f16_to_f32(w[j] & 0xFFFFu);
+      f[2 * j + 1] = f16_to_f32(w[j] >> 16);
+    }
+    if constexpr (!F16OUT) {
+      float4v* o = (float4v*)((float*)dst_ + i0);
+      __builtin_nontemporal_store((float4v){f[0], f[1], f[2], f[3]}, o);
+      __builtin_nontemporal_store((float4v){f[4], f[5], f[6], f[7]}, o + 1);
+    } else {
+      __builtin_nontemporal_store((u32x4){pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]), pack_f16x2(f[4], f[5]),
+                                          pack_f16x2(f[6], f[7])},
+                                  (u32x4*)((uint16_t*)dst_ + i0));
+    }
+    return;
+  }
+  const uint64_t n = total - i0 < 8 ? total - i0 : 8;
+  for (uint64_t j = 0; j < n; ++j) {
+    const float f = f16_to_f32(src[i0 + j]);
+    if constexpr (!F16OUT)
+      ((float*)dst_)[i0 + j] = f;
+    else
+      ((uint16_t*)dst_)[i0 + j] = f32_to_f16_bits(f);
+  }
+}
+
 template <int QT, bool F16OUT>
 static hipError_t launch_dequant_t(const void* src, int64_t rows, int64_t cols, void* dst, hipStream_t s) {
   using F = Fmt<QT>;
@@ -129,6 +170,15 @@ static hipError_t launch_dequant_t(const void* src, int64_t rows, int64_t cols, 
 hipError_t launch_dequant(int qtype, bool f16out, const void* src, int64_t rows, int64_t cols, void* dst,
                           hipStream_t s) {
   switch (qtype) {
+    case kF16: {
+      const uint64_t total = (uint64_t)rows * cols;
+      const dim3 grid((uint32_t)((total + 8 * 256 - 1) / (8 * 256)));
+      if (f16out)
+        hipLaunchKernelGGL(dequant_f16w_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src, total, dst);
+      else
+        hipLaunchKernelGGL(dequant_f16w_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)src, total, dst);
+      return hipGetLastError();
+    }
     case kQ8_0: return f16out ? launch_dequant_t<kQ8_0, true>(src, rows, cols, dst, s)
                               : launch_dequant_t<kQ8_0, false>(src, rows, cols, dst, s);
     case kQ4_K: return f16out ? launch_dequant_t<kQ4_K, true>(src, rows, cols, dst, s)

@@ -136,10 +136,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
         *(u32x4*)(xs + r * LDK + xcol) = xv[i];
       }
     }
-    UnitRaw ur;
-    wr.finish(ur);
     uint32_t hw[16];
-    unit_to_f16<QT>(ur, hw);
+    if constexpr (QT == kF16) {
+      wr.halves(hw);
+    } else {
+      UnitRaw ur;
+      wr.finish(ur);
+      unit_to_f16<QT>(ur, hw);
+    }
     _Float16* ws = sm.w[buf] + wn_t * LDK + 32 * kh;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -190,6 +194,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
 template <int MODE>
 static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStream_t s) {
   switch (qtype) {
+    case kF16: hipLaunchKernelGGL((gemm_kernel<kF16, MODE>), grid, dim3(NT), 0, s, p); break;
     case kQ8_0: hipLaunchKernelGGL((gemm_kernel<kQ8_0, MODE>), grid, dim3(NT), 0, s, p); break;
     case kQ4_K: hipLaunchKernelGGL((gemm_kernel<kQ4_K, MODE>), grid, dim3(NT), 0, s, p); break;
     case kQ5_K: hipLaunchKernelGGL((gemm_kernel<kQ5_K, MODE>), grid, dim3(NT), 0, s, p); break;
@@ -207,9 +212,14 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
 static bool tall_strides_ok(int64_t ldx, int64_t ldy) {
   return 256 * ldx * 2 < ((int64_t)1 << 31) && ldy % 4 == 0;
 }
-static bool use_tall_tiles(int64_t n, int64_t t, int64_t ldx, int64_t ldy) {
+// F16 weight rows are copied with 32-bit byte offsets from a tile's first
+// row: 128 rows must span under 2^31 bytes.
+static bool tall_weights_ok(int qtype, int64_t k) {
+  return qtype != kF16 || 128 * row_bytes_of(qtype, k) < ((int64_t)1 << 31);
+}
+static bool use_tall_tiles(int qtype, int64_t n, int64_t k, int64_t t, int64_t ldx, int64_t ldy) {
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + 255) / 256);
-  return t >= 512 && tiles >= 256 && tall_strides_ok(ldx, ldy);
+  return t >= 512 && tiles >= 256 && tall_strides_ok(ldx, ldy) && tall_weights_ok(qtype, k);
 }
 
 hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
@@ -225,7 +235,7 @@ hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const voi
   p.y = y;
   p.ldy = ldy;
   p.vec_store = ldy % 4 == 0;
-  if (!x_f32 && use_tall_tiles(n, t, ldx, ldy)) {
+  if (!x_f32 && use_tall_tiles(qtype, n, k, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
   }
@@ -251,7 +261,7 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   p.hd = (int)head_dim;
   p.eps = eps;
   p.vec_store = ldy % 4 == 0;
-  if (use_tall_tiles(n, t, ldx, ldy)) {
+  if (use_tall_tiles(qtype, n, k, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kQkNorm, grid, p, s);
   }
@@ -268,7 +278,8 @@ hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3]
                            hipStream_t s) {
   int64_t ntiles = 0;
   for (int i = 0; i < 3; ++i) ntiles += (n[i] + BN - 1) / BN;
-  const bool fused = t >= 512 && ntiles * ((t + 255) / 256) >= 256 && tall_strides_ok(ldx, ldy[0]) &&
+  const bool fused = t >= 512 && ntiles * ((t + 255) / 256) >= 256 && tall_weights_ok(qtype, k) &&
+                     tall_strides_ok(ldx, ldy[0]) &&
                      tall_strides_ok(ldx, ldy[1]) && (n[2] == 0 || tall_strides_ok(ldx, ldy[2]));
   if (!fused) {
     for (int i = 0; i < 3; ++i) {

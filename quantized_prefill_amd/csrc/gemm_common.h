@@ -292,6 +292,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
 
 static inline int64_t row_bytes_of(int qtype, int64_t cols) {
   switch (qtype) {
+    case kF16: return cols * 2;
     case kQ8_0: return (cols + 31) / 32 * 34;
     case kQ4_K: return (cols + 255) / 256 * 144;
     case kQ5_K: return (cols + 255) / 256 * 176;

@@ -54,19 +54,29 @@ template <> struct StageUnit<kQ5_K> { static constexpr int KW = 256, UB = 176, R
 template <> struct StageUnit<kQ6_K> { static constexpr int KW = 256, UB = 210, RSD = 53; };
 template <> struct StageUnit<kQ2_K> { static constexpr int KW = 256, UB = 84, RSD = 21; };
 template <> struct StageUnit<kQ8_0> { static constexpr int KW = 128, UB = 136, RSD = 35; };
+// F16 weights are not staged: the producers copy each chunk's binary16 rows
+// straight into the weight tile.  The small area only holds the epilogue's
+// reduction scratch.
+template <> struct StageUnit<kF16> { static constexpr int KW = 64, UB = 128, RSD = 5; };
 
 constexpr int kLdsBytes = 160 * 1024;
+// Weight tile ring: two buffers where the producers decode one chunk ahead;
+// three for F16 weights, whose direct loads are issued two chunks ahead.
+template <int QT>
+constexpr int wbuf_of() {
+  return QT == kF16 ? 3 : 2;
+}
 // Activation ring depth: three buffers where the LDS allows, else two.
 template <int QT>
 constexpr int xbuf_of() {
-  return 3 * TBM * BK * 2 + 2 * BN * BK * 2 + 2 * BN * StageUnit<QT>::RSD * 4 <= kLdsBytes ? 3 : 2;
+  return 3 * TBM * BK * 2 + wbuf_of<QT>() * BN * BK * 2 + 2 * BN * StageUnit<QT>::RSD * 4 <= kLdsBytes ? 3 : 2;
 }
-static_assert(BN * 21 >= 4 * TBM / 2 * 2 / 2, "staging area holds the epilogue reduction scratch");
+static_assert(BN * 5 >= 4 * TBM / 2 * 2 / 2, "staging area holds the epilogue reduction scratch");
 
 template <int QT>
 struct TallSmem {
   _Float16 x[xbuf_of<QT>()][TBM * BK];
-  _Float16 w[2][BN * BK];
+  _Float16 w[wbuf_of<QT>()][BN * BK];
   uint32_t raw[2][BN * StageUnit<QT>::RSD];
 };
 
@@ -234,6 +244,7 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   using SU = StageUnit<QT>;
   constexpr int RSD = SU::RSD, CPU = SU::KW / BK;  // chunks per staging unit
   constexpr int XB = xbuf_of<QT>();
+  constexpr int WB = wbuf_of<QT>();
   // staging of the next unit is issued over the first NPART chunks of a unit
   // (all but its last chunk, at most three), each part a slice of the 32 rows
   // of a producer wave
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     frags(sm.x[0], sm.w[0], 1, a1, b1);
     for (int c = 0; c < nch; ++c) {
       const _Float16* xs = sm.x[c % XB];
-      const _Float16* ws = sm.w[c & 1];
+      const _Float16* ws = sm.w[c % WB];
       half8 a2[TMI], b2[2], a3[TMI], b3[2];
       mfmas(a0, b0);
       frags(xs, ws, 2, a2, b2);
@@ -408,7 +419,7 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
       lds_barrier();    // chunk c + 1 decoded; this wave's reads of chunk c are done
       __builtin_amdgcn_sched_barrier(0);
       const _Float16* xn = sm.x[(c + 1) % XB];
-      const _Float16* wnx = sm.w[(c + 1) & 1];
+      const _Float16* wnx = sm.w[(c + 1) % WB];
       frags(xn, wnx, 0, a0, b0);
       mfmas_loading(a2, b2, c + XB);  // chunk c's buffer is free: load chunk c + XB
       frags(xn, wnx, 1, a1, b1);
@@ -425,6 +436,48 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
     epilogue(acc, true);
+  } else if constexpr (QT == kF16) {
+    // ---- producer waves, F16 weights: copy rows into the weight tile ------
+    // Wave pw fills tile rows 32 pw .. + 31 of each chunk with 4 direct
+    // 16-byte loads per lane, laid out like the activation copy (lane l lands
+    // in slot l & 7 of row 32 pw + 8 q + (l >> 3), which holds the piece the
+    // slot order puts there).  Rows past the tensor repeat its last row.
+    // Chunk c + 2 is issued into its ring slot right after the barrier that
+    // ends the reads of chunk c - 1, the slot's previous chunk, and waited
+    // for at the barrier that hands over chunk c + 1.
+    const int pw = role_idx;
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + (int64_t)n0 * p.rb), (short)0, -1, 0x00020000);
+    uint32_t woff[4];  // bytes from row n0 (128 rows span under 2^31 bytes)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * pw + 8 * q + (lane >> 3);
+      const int piece = (lane & 7) ^ swz_of(row);
+      woff[q] = (uint32_t)(min(row, p.n - 1 - n0) * p.rb + 16 * piece);
+    }
+    auto load_w = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc,
+                                                 (__attribute__((address_space(3))) void*)(sm.w[c % WB] + (32 * pw + 8 * q) * BK),
+                                                 16, (int)woff[q], 128 * c, 0, 0);
+    };
+    load_w(0);
+    load_w(1);  // K is a multiple of 256: at least 4 chunks
+    lds_barrier();
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // chunk 0 landed
+    lds_barrier();
+    for (int c = 0; c < nch; ++c) {
+      if (c + 2 < nch) {
+        load_w(c + 2);
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // chunk c + 1 landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      lds_barrier();  // chunk c + 1 in place; the consumers' reads of chunk c are done
+    }
+    float16v none[TMI][2];  // not read: the producer side of the epilogue only synchronises
+    epilogue(none, false);
   } else {
     // ---- producer waves: stage and decode ---------------------------------
     const int pw = role_idx;  // 0..3
@@ -545,6 +598,7 @@ hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p,
   else                                                                                       \
     hipLaunchKernelGGL((gemm_tall_kernel<QT, kPlainF16>), grid, dim3(2 * NT), 0, s, p);
   switch (qtype) {
+    case kF16: QP_TALL(kF16) break;
     case kQ8_0: QP_TALL(kQ8_0) break;
     case kQ4_K: QP_TALL(kQ4_K) break;
     case kQ5_K: QP_TALL(kQ5_K) break;

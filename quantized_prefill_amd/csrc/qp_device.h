@@ -27,9 +27,13 @@
 
 namespace qp {
 
-constexpr int kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14;
+constexpr int kF16 = 1, kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14;
 
 template <int QT> struct Fmt;
+// F16 weights (one binary16 per weight) are handled by the GEMM kernels as
+// blocks of 32 weights (64 bytes): K is a multiple of 256, so a row is whole
+// such blocks.  The streaming dequant has its own kernel for them.
+template <> struct Fmt<kF16> { static constexpr int QK = 32, TS = 64, UNITS = 1; };
 template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, TS = 34, UNITS = 1; };
 template <> struct Fmt<kQ4_K> { static constexpr int QK = 256, TS = 144, UNITS = 8; };
 template <> struct Fmt<kQ5_K> { static constexpr int QK = 256, TS = 176, UNITS = 8; };
@@ -135,6 +139,25 @@ struct UnitRaw {
 // finish() turning them into a UnitRaw.  Splitting the two lets a caller keep
 // the loads of the next unit in flight while it works on the current one.
 template <int QT> struct Raw;
+
+// F16 weights: the unit's 32 binary16 values, already the MFMA operand.
+template <> struct Raw<kF16> {
+  u32x4 v[4];
+  __device__ __forceinline__ void load(const uint8_t* blk, uint32_t) {
+    const u32x4* q = (const u32x4*)blk;  // rows are 512-byte multiples from a 16-byte-aligned base
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = q[i];
+  }
+  __device__ __forceinline__ void halves(uint32_t (&out)[16]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[4 * i] = v[i].x;
+      out[4 * i + 1] = v[i].y;
+      out[4 * i + 2] = v[i].z;
+      out[4 * i + 3] = v[i].w;
+    }
+  }
+};
 
 template <> struct Raw<kQ8_0> {
   uint32_t d16, w[9], sh;

@@ -32,8 +32,10 @@ def test_exports_every_declared_symbol():
 
 
 def test_geometry():
-    assert [qp.block_size(t) for t in (qp.Q8_0, qp.Q4_K, qp.Q5_K, qp.Q6_K, qp.Q2_K)] == [32, 256, 256, 256, 256]
-    assert [qp.type_size(t) for t in (qp.Q8_0, qp.Q4_K, qp.Q5_K, qp.Q6_K, qp.Q2_K)] == [34, 144, 176, 210, 84]
+    assert [qp.block_size(t) for t in (qp.F16W, qp.Q8_0, qp.Q4_K, qp.Q5_K, qp.Q6_K, qp.Q2_K)] == [1, 32, 256, 256, 256,
+                                                                                                256]
+    assert [qp.type_size(t) for t in (qp.F16W, qp.Q8_0, qp.Q4_K, qp.Q5_K, qp.Q6_K, qp.Q2_K)] == [2, 34, 144, 176, 210,
+                                                                                               84]
     assert qp.row_bytes(qp.Q6_K, 4173) == 17 * 210
     assert qp.row_bytes(qp.Q8_0, 33) == 2 * 34
     assert qp.block_size(2) == -1 and qp.row_bytes(qp.Q4_K, 0) == -1

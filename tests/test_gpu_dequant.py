@@ -8,7 +8,7 @@ import pins
 import synth
 import quantized_prefill_amd as qp
 from gpu_helpers import GUARD, NAN16, NAN32, say, to_dev, weights
-from synth import Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
+from synth import F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,36 @@ def test_determinism():
     a, _ = gpu_dequant(Q6_K, raw, 64, 4096, False)
     b, _ = gpu_dequant(Q6_K, raw, 64, 4096, False)
     assert np.array_equal(a, b)
+
+
+def test_f16_weights_every_pattern(orc):
+    """F16 weights: all 65,536 binary16 patterns (a 256 x 256 tensor and one
+    row) widen exactly to f32 and come back unchanged as f16; NaN stays NaN
+    (payloads are not part of the definition)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    raw = bits.astype("<u2").view(np.uint8)
+    nan = np.isnan(bits.view(np.float16))
+    want32 = orc.dequant_f32(F16W, raw, 256, 256).view(np.uint32).reshape(-1)
+    for rows, cols in ((256, 256), (1, 1 << 16)):
+        say(f"dequant F16 weights every pattern {rows}x{cols}")
+        got32, ok32 = gpu_dequant(F16W, raw, rows, cols, False)
+        got16, ok16 = gpu_dequant(F16W, raw, rows, cols, True)
+        assert ok32 and ok16, "wrote outside rows x cols"
+        g32, g16 = got32.reshape(-1), got16.reshape(-1)
+        assert np.array_equal(g32[~nan], want32[~nan])
+        assert np.all(np.isnan(g32[nan].view(np.float32)))
+        assert np.array_equal(g16[~nan], bits[~nan])
+        assert np.all(np.isnan(g16[nan].view(np.float16)))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 7), (5, 1001), (33, 4096)])
+def test_f16_weights_ragged(orc, rows, cols):
+    """Tensors whose size is not a multiple of the 8-weight vector step."""
+    raw = weights(F16W, rows, cols, 7600 + cols)
+    check_bits(orc, F16W, raw, rows, cols, f"F16 {rows}x{cols}")
+
+
+def test_f16_weights_8b_gate(orc):
+    raw = weights(F16W, 12288, 4096, synth.seed_for(2, 10 * F16W + 4))
+    check_bits(orc, F16W, raw, 12288, 4096, "F16 8B gate")
+    weights.cache_clear()

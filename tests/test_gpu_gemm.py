@@ -6,11 +6,11 @@ import pytest
 import synth
 import quantized_prefill_amd as qp
 from gpu_helpers import assert_close, act_f16, sample_tokens, say, to_dev, weights
-from synth import Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
+from synth import F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 pytestmark = pytest.mark.gpu
 
-QTYPES = [Q8_0, Q4_K, Q5_K, Q6_K, Q2_K]
+QTYPES = [F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K]
 
 
 def run_gemm(qtype, raw, n, k, x: np.ndarray):
@@ -93,11 +93,12 @@ def _projection_cases():
         for i, (name, n, k) in enumerate(synth.PROJ_8B):
             cases.append((f"8b_{name}_{synth.NAMES[qt]}", qt, n, k, 2048, synth.seed_for(2, 10 * qt + i),
                           synth.seed_for(2, 500 + k // 256)))
-    # Q5_K at two of the 8B shapes (a wider weight type than the workload's)
-    for i, (name, n, k) in enumerate(synth.PROJ_8B):
-        if name in ("gate", "down"):
-            cases.append((f"8b_{name}_Q5_K", Q5_K, n, k, 2048, synth.seed_for(2, 10 * Q5_K + i),
-                          synth.seed_for(2, 500 + k // 256)))
+    # Q5_K and F16 weights at two of the 8B shapes
+    for qt in (Q5_K, F16W):
+        for i, (name, n, k) in enumerate(synth.PROJ_8B):
+            if name in ("gate", "down"):
+                cases.append((f"8b_{name}_{synth.NAMES[qt]}", qt, n, k, 2048, synth.seed_for(2, 10 * qt + i),
+                              synth.seed_for(2, 500 + k // 256)))
     return cases
 
 

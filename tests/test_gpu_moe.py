@@ -5,7 +5,7 @@ import pytest
 import synth
 import quantized_prefill_amd as qp
 from gpu_helpers import assert_close, act_f16, sample_tokens, say, to_dev
-from synth import Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
+from synth import F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,8 @@ def run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("qtype", [Q4_K, Q5_K, Q8_0, Q6_K, Q2_K], ids=["Q4_K", "Q5_K", "Q8_0", "Q6_K", "Q2_K"])
+@pytest.mark.parametrize("qtype", [Q4_K, Q5_K, Q8_0, Q6_K, Q2_K, F16W], ids=["Q4_K", "Q5_K", "Q8_0", "Q6_K", "Q2_K",
+                                                                          "F16"])
 def test_moe_small(orc, qtype):
     """8 experts, top-2, ragged per-expert counts (some experts empty)."""
     t, ne, k, hidden, inter = 157, 8, 2, 256, 512
