@@ -257,6 +257,16 @@ def test_qkv_ragged(orc, qtype):
     gains = [synth.gains(64, 8731), synth.gains(64, 8732)]
     say(f"qkv ragged {synth.NAMES[qtype]} hd=64 no v")
     check_qkv(orc, qtype, ws, ns, k, x, 64, gains, [0, 0], None, f"qkv ragged hd64 {synth.NAMES[qtype]}")
+    # 256 q tiles + 64 k + 64 v tiles (one and a half rounds of the GPU) with
+    # per-head k gains; twice in a row, identical bits
+    ns = [8192, 2048, 2048]
+    ws = [weights(qtype, ns[0], k, 8740), ws[1], weights(qtype, ns[2], k, 8741)]
+    gains = [synth.gains(128, 8742), synth.gains(ns[1], 8743)]
+    say(f"qkv ragged {synth.NAMES[qtype]} 384 tiles")
+    a = check_qkv(orc, qtype, ws, ns, k, x, 128, gains, [0, 128], None, f"qkv 384 tiles {synth.NAMES[qtype]}")
+    b = run_qkv(qtype, ws, ns, k, x, 128, gains, [0, 128])
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v), "q/k/v results differ between two calls"
 
 
 def test_qkv_small_falls_back(orc):
