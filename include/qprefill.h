@@ -154,16 +154,33 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
  * head_dim and eps.  When the three projections' output tiles together fill
  * the GPU this is a single launch (k and v alone often do not: 1024 outputs
  * at T = 2048 make 64 tiles); otherwise it is the three calls.  Results match
- * the separate calls within the GEMM tolerance (summation order may differ).
+ * the separate calls within the GEMM tolerance (summation order may differ);
+ * y_q matches its separate call bit for bit, and every call with the same
+ * inputs gives the same bits.
+ *   workspace (device, optional): qp_prefill_gemm_qkv_workspace_bytes(...)
+ *     bytes, 16-byte aligned, no initial contents needed.  With it, where the
+ *     single launch's last round of tiles would be only partly filled (and
+ *     k % 512 == 0, n_k and n_v multiples of 8, ldy_k and ldy_v multiples of
+ *     4), k and v each run as two K
+ *     halves that write partial sums there; a second pass adds the halves in
+ *     order and applies k's head norm.  NULL: no split.  Calls that share a
+ *     workspace must not run concurrently.
  * n_v == 0 leaves v out (w_v, y_v unused).  The three outputs must not
  * overlap.  Requirements and errors are those of the two calls for each
- * projection.
+ * projection, and QP_ERR_WORKSPACE_TOO_SMALL for a non-NULL workspace below
+ * the query.
  */
 qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const void* w_k, int64_t n_k,
                               const void* w_v, int64_t n_v, int64_t k, const uint16_t* x, int64_t t, int64_t ldx,
                               int64_t head_dim, const float* gain_q, int64_t gain_q_stride, const float* gain_k,
                               int64_t gain_k_stride, float eps, float* y_q, int64_t ldy_q, float* y_k, int64_t ldy_k,
-                              float* y_v, int64_t ldy_v, hipStream_t stream);
+                              float* y_v, int64_t ldy_v, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Bytes of the optional workspace of qp_prefill_gemm_qkv (partial sums of k
+ * and v: 2 * t * (n_k + n_v) floats, rounded up to 256); 0 for sizes out of
+ * range. */
+size_t qp_prefill_gemm_qkv_workspace_bytes(int64_t n_q, int64_t n_k, int64_t n_v, int64_t t);
 
 /*
  * Router of a routed-expert layer ("Correctness and safety": routing ids,

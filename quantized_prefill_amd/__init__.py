@@ -30,7 +30,8 @@ SIGNATURES = {
     "qp_prefill_gemm_qknorm": (_INT, [_INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64, _F32C, _VP, _I64,
                                       _VP]),
     "qp_prefill_gemm_qkv": (_INT, [_INT, _VP, _I64, _VP, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64,
-                                   _VP, _I64, _F32C, _VP, _I64, _VP, _I64, _VP, _I64, _VP]),
+                                   _VP, _I64, _F32C, _VP, _I64, _VP, _I64, _VP, _I64, _VP, _SZ, _VP]),
+    "qp_prefill_gemm_qkv_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "qp_moe_route_topk": (_INT, [_VP, _I64, _I64, _I64, _INT, _VP, _VP, _VP]),
     "qp_grouped_expert_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "qp_grouped_expert_gemm": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP, _VP,
@@ -153,16 +154,37 @@ def prefill_gemm_qknorm(qtype: int, w, n: int, k: int, x, head_dim: int, gain, g
     return out
 
 
+_QKV_WORKSPACE = {}
+
+
+def qkv_workspace(n_q: int, n_k: int, n_v: int, t: int, device):
+    """Workspace for prefill_gemm_qkv, kept per device and grown as needed."""
+    torch = _torch()
+    nbytes = lib().qp_prefill_gemm_qkv_workspace_bytes(n_q, n_k, n_v, t)
+    key = torch.device(device).index
+    ws = _QKV_WORKSPACE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _QKV_WORKSPACE[key] = ws
+    return ws
+
+
 def prefill_gemm_qkv(qtype: int, w_q, n_q: int, w_k, n_k: int, w_v, n_v: int, k: int, x, head_dim: int,
                      gain_q, gain_k, gain_q_stride: int = 0, gain_k_stride: int = 0, eps: float = 1e-6,
-                     out_q=None, out_k=None, out_v=None):
-    """q and k with the per-head RMSNorm, v plain, over one float16 x, in one call."""
+                     out_q=None, out_k=None, out_v=None, workspace=None):
+    """q and k with the per-head RMSNorm, v plain, over one float16 x, in one call.
+    workspace: a uint8 GPU tensor, None for the cached one (qkv_workspace), or
+    False for none (no K split)."""
     torch = _torch()
     if x.dtype != torch.float16:
         raise TypeError("x must be float16")
     if not x.is_cuda or x.stride(1) != 1:
         raise ValueError("x must be a GPU tensor with unit column stride")
     t = x.shape[0]
+    if workspace is None:
+        ws = qkv_workspace(n_q, n_k, n_v, t, x.device)
+    else:
+        ws = None if workspace is False else workspace
     outs = []
     for o, n in ((out_q, n_q), (out_k, n_k), (out_v, n_v)):
         outs.append(o if o is not None else torch.empty((t, max(n, 1)), dtype=torch.float32, device=x.device))
@@ -171,7 +193,8 @@ def prefill_gemm_qkv(qtype: int, w_q, n_q: int, w_k, n_k: int, w_v, n_v: int, k:
                                     head_dim, _dev(gain_q, "gain_q"), gain_q_stride, _dev(gain_k, "gain_k"),
                                     gain_k_stride, float(eps), outs[0].data_ptr(), outs[0].stride(0),
                                     outs[1].data_ptr(), outs[1].stride(0), outs[2].data_ptr(), outs[2].stride(0),
-                                    _stream()))
+                                    _dev(ws, "workspace") if ws is not None else None,
+                                    ws.numel() if ws is not None else 0, _stream()))
     return tuple(outs)
 
 

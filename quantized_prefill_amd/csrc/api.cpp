@@ -140,7 +140,8 @@ qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const voi
                               const void* w_v, int64_t n_v, int64_t k, const uint16_t* x, int64_t t, int64_t ldx,
                               int64_t head_dim, const float* gain_q, int64_t gain_q_stride, const float* gain_k,
                               int64_t gain_k_stride, float eps, float* y_q, int64_t ldy_q, float* y_k, int64_t ldy_k,
-                              float* y_v, int64_t ldy_v, hipStream_t stream) {
+                              float* y_v, int64_t ldy_v, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   if (n_v < 0) return fail(QP_ERR_INVALID_PARAMETER, "n_v=%lld must be >= 0", (long long)n_v);
   qp_status st = gemm_checks(qtype, w_q, n_q, k, x, t, ldx, 2, y_q, ldy_q);
   if (st != QP_OK) return st;
@@ -164,8 +165,20 @@ qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const voi
   const int64_t gstride[3] = {gain_q_stride, gain_k_stride, 0};
   float* y[3] = {y_q, y_k, y_v};
   const int64_t ldy[3] = {ldy_q, ldy_k, ldy_v};
-  return from_hip(qp::launch_gemm_qkv(qtype, w, n, k, x, t, ldx, head_dim, gain, gstride, eps, y, ldy, stream),
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 16)) return fail(QP_ERR_INVALID_PARAMETER, "workspace must be 16-byte aligned");
+    if (workspace_bytes < qp_prefill_gemm_qkv_workspace_bytes(n_q, n_k, n_v, t))
+      return fail(QP_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu below the query", workspace_bytes);
+  }
+  return from_hip(qp::launch_gemm_qkv(qtype, w, n, k, x, t, ldx, head_dim, gain, gstride, eps, y, ldy,
+                                      (float*)workspace, stream),
                   "gemm_qkv launch");
+}
+
+size_t qp_prefill_gemm_qkv_workspace_bytes(int64_t n_q, int64_t n_k, int64_t n_v, int64_t t) {
+  if (n_q < 0 || n_k < 0 || n_v < 0 || t < 0 || n_k > kMaxDim || n_v > kMaxDim || t > kMaxDim) return 0;
+  const int64_t n[3] = {n_q, n_k, n_v};
+  return (size_t)((qp::qkv_split_partial_floats(n, t) * 4 + 255) / 256 * 256);
 }
 
 qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k, int renorm,

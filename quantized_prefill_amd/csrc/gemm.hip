@@ -28,6 +28,9 @@
 // MFMA 32x32x16 operand layout (lane l, 8 halfs per lane): A row l%32 (B
 // column l%32), k = 8*(l/32) + e; result register a of lane l holds
 // D[8*(a/4) + 4*(l/32) + a%4][l%32].
+#include <algorithm>
+#include <vector>
+
 #include "gemm_common.h"
 
 namespace qp {
@@ -269,16 +272,110 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   return launch_mode<kQkNorm>(qtype, grid, p, s);
 }
 
+// Sums of the two K halves of split projections (k and v of the fused
+// q/k/v launch), in that order: y = p0 + p1 (t x n, partials dense with row
+// stride n, n % 8 == 0).  With hd > 0 the per-head RMSNorm follows, with the
+// operations of the fused epilogue (sum of squares in f32, 1 / sqrt(ss *
+// (1 / hd) + eps), then y * scale * gain).  One wave per (token, 512-column
+// slab of its row); lane l holds columns 8 l .. 8 l + 7 of the slab, so a
+// head (hd = 64 or 128) is hd / 8 adjacent lanes.  Both projections in one
+// launch: the first one's waves, then the second one's.
+struct SplitSum {
+  const float* p0;
+  const float* p1;
+  float* y;
+  int64_t ldy;
+  int n, hd;
+  const float* gain;
+  int64_t gstride;
+  int64_t items;  // waves: t * ceil(n / 512)
+};
+
+__global__ __launch_bounds__(256) void split_combine_kernel(SplitSum a, SplitSum b, float eps) {
+  const int lane = threadIdx.x & 63;
+  int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool first = item < a.items;
+  const SplitSum& q = first ? a : b;
+  if (!first) item -= a.items;
+  if (item >= q.items) return;
+  const int slabs = (q.n + 511) / 512;
+  const int64_t tok = item / slabs;
+  const int c = (int)(item - tok * slabs) * 512 + 8 * lane;
+  const bool ok = c < q.n;  // n % 8 == 0: all 8 columns or none
+  float4v lo = (float4v){0.f, 0.f, 0.f, 0.f}, hi = lo;
+  if (ok) {
+    const float4v* r0 = (const float4v*)(q.p0 + tok * q.n + c);
+    const float4v* r1 = (const float4v*)(q.p1 + tok * q.n + c);
+    lo = r0[0] + r1[0];
+    hi = r0[1] + r1[1];
+  }
+  float4v* dst = (float4v*)(q.y + tok * q.ldy + c);
+  if (q.hd == 0) {
+    if (ok) {
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+    return;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
+  const int lanes = q.hd / 8;  // 8 or 16 lanes per head
+  for (int m = 1; m < lanes; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  const float scale = 1.f / __builtin_sqrtf(ss * (1.f / (float)q.hd) + eps);
+  if (ok) {
+    const int head = c / q.hd;
+    const float* g = q.gain + (int64_t)head * q.gstride + (c - head * q.hd);
+    float4v o0, o1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = lo[e] * scale * g[e];
+      o1[e] = hi[e] * scale * g[4 + e];
+    }
+    dst[0] = o0;
+    dst[1] = o1;
+  }
+}
+
+static int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// Finish time of workgroups issued in order onto `slots` compute units, one
+// at a time each (a tall tile takes a whole CU), with the given costs.
+static double list_makespan(const std::vector<double>& cost, int slots) {
+  std::vector<double> free_at((size_t)slots, 0.0);
+  double end = 0.0;
+  for (double c : cost) {
+    const size_t best = (size_t)(std::min_element(free_at.begin(), free_at.end()) - free_at.begin());
+    free_at[best] += c;
+    end = std::max(end, free_at[best]);
+  }
+  return end;
+}
+
+int64_t qkv_split_partial_floats(const int64_t n[3], int64_t t) { return 2 * t * (n[1] + n[2]); }
+
 // q, k and v over one X: when their output tiles together fill the GPU with
 // tall tiles, one launch covers all three (each tile resolves its projection
 // from its column index); otherwise three ordinary launches.
+// In the fused launch the q tiles (largest projection, QK-norm epilogue) come
+// first.  When the tiles fill the last round only in part and the caller gave
+// room for partial sums, k and v are each split into two K halves (twice as
+// many workgroups of half the work) that write partial sums; a combine pass
+// then adds the halves in order and applies k's head norm.
 hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3], int64_t k, const uint16_t* x,
                            int64_t t, int64_t ldx, int64_t head_dim, const float* const gain[3],
                            const int64_t gstride[3], float eps, float* const y[3], const int64_t ldy[3],
-                           hipStream_t s) {
+                           float* partial, hipStream_t s) {
   int64_t ntiles = 0;
   for (int i = 0; i < 3; ++i) ntiles += (n[i] + BN - 1) / BN;
-  const bool fused = t >= 512 && ntiles * ((t + 255) / 256) >= 256 && tall_weights_ok(qtype, k) &&
+  const int64_t mt = (t + 255) / 256;
+  const bool fused = t >= 512 && ntiles * mt >= 256 && tall_weights_ok(qtype, k) &&
                      tall_strides_ok(ldx, ldy[0]) &&
                      tall_strides_ok(ldx, ldy[1]) && (n[2] == 0 || tall_strides_ok(ldx, ldy[2]));
   if (!fused) {
@@ -291,6 +388,18 @@ hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3]
     }
     return hipSuccess;
   }
+  // Split when the launch gets 10% shorter (halves start on a 256-weight
+  // block: K % 512 == 0; the combine pass moves 8 floats per lane with
+  // 16-byte accesses: n % 8 == 0 and 16-byte output rows).
+  bool split = false;
+  if (partial != nullptr && k % 512 == 0 && n[1] % 8 == 0 && n[2] % 8 == 0 && ldy[1] % 4 == 0 &&
+      (n[2] == 0 || ldy[2] % 4 == 0)) {
+    const int64_t cq = (n[0] + BN - 1) / BN, ckv = ntiles - cq;
+    std::vector<double> whole((size_t)(ntiles * mt), 1.0), halves((size_t)(cq * mt), 1.0);
+    halves.resize((size_t)((cq + 2 * ckv) * mt), 0.55);
+    const int cus = cu_count();
+    split = list_makespan(halves, cus) <= 0.9 * list_makespan(whole, cus);
+  }
   GemmParams p = {};
   p.rb = row_bytes_of(qtype, k);
   p.k = (int)k;
@@ -300,23 +409,56 @@ hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3]
   p.hd = (int)head_dim;
   p.eps = eps;
   int nseg = 0, tile = 0;
-  for (int i = 0; i < 3; ++i) {
-    if (n[i] == 0) continue;
+  auto add_seg = [&](int i, int64_t k0, int64_t kk, float* out, int64_t ldo, int norm) {
     p.seg.tile0[nseg] = tile;
-    p.seg.w[nseg] = (const uint8_t*)w[i];
+    p.seg.w[nseg] = (const uint8_t*)w[i] + row_bytes_of(qtype, k0);  // blocks before the K part
     p.seg.n[nseg] = (int)n[i];
-    p.seg.y[nseg] = y[i];
-    p.seg.ldy[nseg] = ldy[i];
+    p.seg.k[nseg] = (int)kk;
+    p.seg.xoff[nseg] = k0;
+    p.seg.y[nseg] = out;
+    p.seg.ldy[nseg] = ldo;
     p.seg.gain[nseg] = gain[i];
     p.seg.gstride[nseg] = gstride[i];
-    p.seg.norm[nseg] = i < 2;
+    p.seg.norm[nseg] = norm;
     tile += (int)((n[i] + BN - 1) / BN);
     ++nseg;
+  };
+  float* part[3][2] = {};
+  float* next = partial;
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] == 0) continue;
+    if (split && i > 0) {
+      for (int h = 0; h < 2; ++h) {
+        part[i][h] = next;
+        next += t * n[i];
+        add_seg(i, h * (k / 2), k / 2, part[i][h], n[i], 0);
+      }
+    } else {
+      add_seg(i, 0, k, y[i], ldy[i], i < 2);
+    }
   }
   p.seg.nseg = nseg;
   for (int i = nseg; i <= kMaxSeg; ++i) p.seg.tile0[i] = tile;
-  dim3 grid((uint32_t)tile, (uint32_t)((t + 255) / 256));
-  return launch_gemm_tall(qtype, kMulti, grid, p, s);
+  dim3 grid((uint32_t)mt, (uint32_t)tile);
+  hipError_t e = launch_gemm_tall(qtype, kMulti, grid, p, s);
+  if (e != hipSuccess || !split) return e;
+  SplitSum sum[2] = {};
+  for (int i = 1; i < 3; ++i) {
+    SplitSum& q = sum[i - 1];
+    if (n[i] == 0) continue;  // items 0: no waves
+    q.p0 = part[i][0];
+    q.p1 = part[i][1];
+    q.y = y[i];
+    q.ldy = ldy[i];
+    q.n = (int)n[i];
+    q.hd = i == 1 ? (int)head_dim : 0;
+    q.gain = gain[i];
+    q.gstride = gstride[i];
+    q.items = t * ((n[i] + 511) / 512);
+  }
+  const int64_t waves = sum[0].items + sum[1].items;
+  hipLaunchKernelGGL(split_combine_kernel, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0, s, sum[0], sum[1], eps);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

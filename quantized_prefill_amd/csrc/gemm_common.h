@@ -17,14 +17,19 @@ constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
 enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4, kMulti = 5 };
 
 // Projections sharing one X fused into one launch of the tall kernel (mode
-// kMulti): segment s owns the output-column tiles [tile0[s], tile0[s + 1]) of
-// the grid's x dimension, with its own weights, output and epilogue.
-constexpr int kMaxSeg = 3;
+// kMulti): segment s owns the output-column tiles [tile0[s], tile0[s + 1]),
+// with its own weights, output and epilogue.  A segment may reduce over one
+// part of K only: its weights and activations start xoff weights into each
+// row and it sums k of them (the halves of a split projection, each writing
+// its partial sums to an output of its own).
+constexpr int kMaxSeg = 5;
 struct GemmSegments {
   int nseg;
   int tile0[kMaxSeg + 1];
-  const uint8_t* w[kMaxSeg];
+  const uint8_t* w[kMaxSeg];  // first weight block of the segment's K part, row 0
   int n[kMaxSeg];
+  int k[kMaxSeg];
+  int64_t xoff[kMaxSeg];      // offset of the K part into each activation row (elements)
   float* y[kMaxSeg];
   int64_t ldy[kMaxSeg];
   const float* gain[kMaxSeg];

@@ -260,14 +260,22 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
   const bool producer = (__builtin_popcount(wave) & 1) != 0;
   const int role_idx = wave >> 1;  // 0..3 within each role
   // kMulti: this tile's projection (uniform per workgroup)
+  // kMulti: this tile's projection (uniform per workgroup).  Its grid is
+  // (token tiles, column tiles), so a segment's workgroups are issued
+  // together, in segment order (whole-K segments first).
   GemmParams p = pk;
-  int tile_x = blockIdx.x;
+  int tile_x = MODE == kMulti ? blockIdx.y : blockIdx.x;
+  const int tile_m = MODE == kMulti ? blockIdx.x : blockIdx.y;
   bool norm = MODE == kQkNorm;
   if constexpr (MODE == kMulti) {
-    const int sg = (tile_x >= pk.seg.tile0[1]) + (pk.seg.nseg > 2 && tile_x >= pk.seg.tile0[2]);
+    int sg = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
     tile_x -= pk.seg.tile0[sg];
     p.w = pk.seg.w[sg];
     p.n = pk.seg.n[sg];
+    p.k = pk.seg.k[sg];
+    p.x = (const _Float16*)pk.x + pk.seg.xoff[sg];
     p.y = pk.seg.y[sg];
     p.ldy = pk.seg.ldy[sg];
     p.gain = pk.seg.gain[sg];
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     norm = pk.seg.norm[sg] != 0;
   }
   const int n0 = tile_x * BN;
-  const int m0 = blockIdx.y * TBM;
+  const int m0 = tile_m * TBM;
   const int m_rows = min(TBM, p.t - m0);
   const int nch = p.k / BK;
   const int nunits = p.k / SU::KW;

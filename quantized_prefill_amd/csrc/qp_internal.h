@@ -17,11 +17,14 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
                               int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
                               float eps, float* y, int64_t ldy, hipStream_t s);
 
-// q, k (per-head RMSNorm) and v (plain) projections of one X; n[i] == 0 skips one
+// q, k (per-head RMSNorm) and v (plain) projections of one X; n[i] == 0 skips
+// one.  partial: room for qkv_split_partial_floats() floats that lets k and v
+// run as two K halves (null: never split).
 hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3], int64_t k, const uint16_t* x,
                            int64_t t, int64_t ldx, int64_t head_dim, const float* const gain[3],
                            const int64_t gstride[3], float eps, float* const y[3], const int64_t ldy[3],
-                           hipStream_t s);
+                           float* partial, hipStream_t s);
+int64_t qkv_split_partial_floats(const int64_t n[3], int64_t t);
 
 hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t top_k, int renorm, int32_t* ids,
                              float* weights, hipStream_t s);

@@ -79,8 +79,13 @@ def test_gemm_rejections():
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, None, 0, 1e-6, FAKE, 256, None) == 1  # gain
     f = L.qp_prefill_gemm_qkv
     good = [qp.Q4_K, FAKE, 256, FAKE, 128, FAKE, 128, 256, FAKE, 8, 256, 128, FAKE, 0, FAKE, 0, 1e-6,
-            FAKE, 256, FAKE, 128, FAKE, 128, None]
+            FAKE, 256, FAKE, 128, FAKE, 128, None, 0, None]
     assert f(*(good[:9] + [0] + good[10:])) == 0                  # t == 0: nothing to do
+    need = L.qp_prefill_gemm_qkv_workspace_bytes(256, 128, 128, 8)
+    assert need == 2 * 8 * 256 * 4                                # partial sums of k and v, two halves
+    assert L.qp_prefill_gemm_qkv_workspace_bytes(256, -1, 128, 8) == 0
+    assert f(*(good[:23] + [FAKE, need - 4] + good[25:])) == 3    # workspace below the query
+    assert f(*(good[:23] + [FAKE + 4, need] + good[25:])) == 1    # workspace misaligned
     for i, v, why in ((0, 7, "type"), (2, 192, "n_q % hd"), (4, 64, "n_k % hd"), (6, -1, "n_v"), (7, 96, "k"),
                       (11, 96, "head_dim"), (16, 0.0, "eps"), (12, None, "gain_q"), (14, None, "gain_k"),
                       (20, 64, "ldy_k < n_k"), (22, 64, "ldy_v < n_v")):

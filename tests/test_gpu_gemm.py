@@ -201,18 +201,19 @@ def test_qknorm_tall_tile_ragged(orc, qtype, hd, n):
         assert_close(y, ref, f"qknorm tall {synth.NAMES[qtype]} hd={hd} stride={gstride}")
 
 
-def run_qkv(qtype, ws, ns, k, x, hd, gains, gstrides, eps=1e-6):
+def run_qkv(qtype, ws, ns, k, x, hd, gains, gstrides, eps=1e-6, workspace=None):
     import torch
     xt = to_dev(x).view(torch.float16)
     wv = to_dev(ws[2]) if ns[2] else None
     yq, yk, yv = qp.prefill_gemm_qkv(qtype, to_dev(ws[0]), ns[0], to_dev(ws[1]), ns[1], wv, ns[2], k, xt, hd,
-                                     to_dev(gains[0]), to_dev(gains[1]), gstrides[0], gstrides[1], eps)
+                                     to_dev(gains[0]), to_dev(gains[1]), gstrides[0], gstrides[1], eps,
+                                     workspace=workspace)
     torch.cuda.synchronize()
     return yq.cpu().numpy(), yk.cpu().numpy(), (yv.cpu().numpy() if ns[2] else None)
 
 
-def check_qkv(orc, qtype, ws, ns, k, x, hd, gains, gstrides, tok, what):
-    yq, yk, yv = run_qkv(qtype, ws, ns, k, x, hd, gains, gstrides)
+def check_qkv(orc, qtype, ws, ns, k, x, hd, gains, gstrides, tok, what, workspace=None):
+    yq, yk, yv = run_qkv(qtype, ws, ns, k, x, hd, gains, gstrides, workspace=workspace)
     xs = x if tok is None else x[tok]
     sel = (lambda a: a) if tok is None else (lambda a: a[tok])
     for name, y, i in (("q", yq, 0), ("k", yk, 1)):
@@ -258,15 +259,21 @@ def test_qkv_ragged(orc, qtype):
     say(f"qkv ragged {synth.NAMES[qtype]} hd=64 no v")
     check_qkv(orc, qtype, ws, ns, k, x, 64, gains, [0, 0], None, f"qkv ragged hd64 {synth.NAMES[qtype]}")
     # 256 q tiles + 64 k + 64 v tiles (one and a half rounds of the GPU) with
-    # per-head k gains; twice in a row, identical bits
+    # per-head k gains: with the workspace k and v run as K halves plus a
+    # combine pass, without it as whole tiles; both against the oracle, the
+    # split one twice for identical bits, q identical in both
     ns = [8192, 2048, 2048]
     ws = [weights(qtype, ns[0], k, 8740), ws[1], weights(qtype, ns[2], k, 8741)]
     gains = [synth.gains(128, 8742), synth.gains(ns[1], 8743)]
-    say(f"qkv ragged {synth.NAMES[qtype]} 384 tiles")
-    a = check_qkv(orc, qtype, ws, ns, k, x, 128, gains, [0, 128], None, f"qkv 384 tiles {synth.NAMES[qtype]}")
+    say(f"qkv ragged {synth.NAMES[qtype]} 384 tiles, K halves")
+    a = check_qkv(orc, qtype, ws, ns, k, x, 128, gains, [0, 128], None, f"qkv split {synth.NAMES[qtype]}")
     b = run_qkv(qtype, ws, ns, k, x, 128, gains, [0, 128])
     for u, v in zip(a, b):
         assert np.array_equal(u, v), "q/k/v results differ between two calls"
+    say(f"qkv ragged {synth.NAMES[qtype]} 384 tiles, whole")
+    c = check_qkv(orc, qtype, ws, ns, k, x, 128, gains, [0, 128], None, f"qkv whole {synth.NAMES[qtype]}",
+                  workspace=False)
+    assert np.array_equal(a[0], c[0]), "q differs between the split and the whole launch"
 
 
 def test_qkv_small_falls_back(orc):
