@@ -161,6 +161,39 @@ def dequant_bytes_8b(L, synth):
     return tot
 
 
+def dequant_graph_gbps(torch, qp, L, synth, replays=10):
+    """The layer's 28 dequant launches (f32 and f16 of every weight), captured
+    once into a HIP graph and replayed back to back: the kernels' rate without
+    the per-launch event pairs and host dispatch between them.  Reported beside
+    the per-launch figure, never instead of it."""
+    def deq():
+        for p in L["projs"]:
+            n, k = p["n"], p["k"]
+            qp.dequant_f32(p["qtype"], p["w"], n, k, out=L["d32"][:n * k].view(n, k))
+            qp.dequant_f16(p["qtype"], p["w"], n, k, out=L["d16"][:n * k].view(n, k))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        deq()  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        deq()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / replays
+    del g
+    return dequant_bytes_8b(L, synth) / ms / 1e6
+
+
 def time_fn(torch, fn, iters):
     fn()
     torch.cuda.synchronize()
@@ -410,6 +443,10 @@ def main():
             "avg_launch_us": round(dom_ms * 1e3, 2),
         },
     }
+    print("bench: dequant as one graph", file=sys.stderr, flush=True)
+    dq_graph = dequant_graph_gbps(torch, qp, L, synth)
+    res["dequant_graph_gbps"] = round(dq_graph, 1)
+    res["dequant_graph_hbm_frac"] = round(dq_graph / PEAK_HBM_GBPS, 4)
     if not args.no_rows:
         print("bench: f16-cache comparator", file=sys.stderr, flush=True)
         two_pass = two_pass_row(torch, synth, qp, L, 10)
