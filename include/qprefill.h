@@ -128,6 +128,31 @@ qp_status qp_prefill_gemm(int qtype, const void* w, int64_t n, int64_t k, const 
                           int64_t t, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 
 /*
+ * qp_prefill_gemm with an optional workspace (the callers that give one let
+ * a launch that would leave the GPU under-filled use all of it, the
+ * stream-K-style split of the pages' shape-adaptive prefill):
+ *   workspace (device): qp_prefill_gemm_workspace_bytes(n, k, t) bytes,
+ *     16-byte aligned, no initial contents needed; NULL (or a query of 0):
+ *     exactly qp_prefill_gemm.
+ * Where the 128-token tile's launch has fewer tiles than the GPU has compute
+ * units, K is split into 2, 4 or 8 parts of whole 256-weight blocks; each
+ * part writes its partial sums into the workspace and one more pass adds
+ * them in part order into y.  The result is the same on every call with the
+ * same inputs and matches qp_prefill_gemm within the GEMM tolerance (the
+ * summation order differs).  Calls that share a workspace must not run
+ * concurrently.  Errors: those of qp_prefill_gemm, and
+ * QP_ERR_WORKSPACE_TOO_SMALL for a non-NULL workspace below the query.
+ */
+qp_status qp_prefill_gemm_ws(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype,
+                             int64_t t, int64_t ldx, float* y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the workspace qp_prefill_gemm_ws uses for these sizes on the
+ * current device (parts * t * n floats, rounded up to 256); 0 when it would
+ * not split, or for sizes out of range. */
+size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t);
+
+/*
  * Prefill projection with the per-head RMSNorm of QK-norm models fused into
  * the epilogue ("What changes": per-head QK norm):  with Y = X . W^T as in
  * qp_prefill_gemm, for each token t and head h (columns h*head_dim ..

@@ -27,6 +27,8 @@ SIGNATURES = {
     "qp_dequant_f32": (_INT, [_INT, _VP, _I64, _I64, _VP, _VP]),
     "qp_dequant_f16": (_INT, [_INT, _VP, _I64, _I64, _VP, _VP]),
     "qp_prefill_gemm": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP]),
+    "qp_prefill_gemm_ws": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP, _SZ, _VP]),
+    "qp_prefill_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qp_prefill_gemm_qknorm": (_INT, [_INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64, _F32C, _VP, _I64,
                                       _VP]),
     "qp_prefill_gemm_qkv": (_INT, [_INT, _VP, _I64, _VP, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64,
@@ -119,8 +121,28 @@ def dequant_f16(qtype: int, w, rows: int, cols: int, out=None):
     return out
 
 
-def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None):
-    """y = x . W^T; x is [T, K] float16 or float32 (rows may be strided)."""
+_GEMM_WORKSPACE = {}
+
+
+def gemm_workspace(n: int, k: int, t: int, device):
+    """Workspace for prefill_gemm's K split (None when it would not split),
+    kept per device and grown as needed."""
+    torch = _torch()
+    nbytes = lib().qp_prefill_gemm_workspace_bytes(n, k, t)
+    if nbytes == 0:
+        return None
+    key = torch.device(device).index
+    ws = _GEMM_WORKSPACE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _GEMM_WORKSPACE[key] = ws
+    return ws
+
+
+def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None, workspace=None):
+    """y = x . W^T; x is [T, K] float16 or float32 (rows may be strided).
+    workspace: a uint8 GPU tensor, None for the cached one (gemm_workspace),
+    or False for none (qp_prefill_gemm exactly)."""
     torch = _torch()
     t = x.shape[0]
     if x.dtype == torch.float16:
@@ -133,8 +155,10 @@ def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None):
         raise ValueError("x must be a GPU tensor with unit column stride")
     if out is None:
         out = torch.empty((t, n), dtype=torch.float32, device=x.device)
-    check(lib().qp_prefill_gemm(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0), out.data_ptr(), out.stride(0),
-                                _stream()))
+    ws = gemm_workspace(n, k, t, x.device) if workspace is None else (None if workspace is False else workspace)
+    check(lib().qp_prefill_gemm_ws(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0), out.data_ptr(),
+                                   out.stride(0), _dev(ws, "workspace") if ws is not None else None,
+                                   ws.numel() if ws is not None else 0, _stream()))
     return out
 
 

@@ -113,10 +113,30 @@ static qp_status gemm_checks(int qtype, const void* w, int64_t n, int64_t k, con
 
 qp_status qp_prefill_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype, int64_t t,
                           int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+  return qp_prefill_gemm_ws(qtype, w, n, k, x, x_dtype, t, ldx, y, ldy, nullptr, 0, stream);
+}
+
+qp_status qp_prefill_gemm_ws(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype, int64_t t,
+                             int64_t ldx, float* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   if (x_dtype != QP_F16 && x_dtype != QP_F32) return fail(QP_ERR_INVALID_PARAMETER, "x_dtype must be QP_F16 or QP_F32");
   qp_status st = gemm_checks(qtype, w, n, k, x, t, ldx, x_dtype == QP_F32 ? 4 : 2, y, ldy);
   if (st != QP_OK || t == 0) return st;
-  return from_hip(qp::launch_gemm(qtype, w, n, k, x, x_dtype == QP_F32, t, ldx, y, ldy, stream), "gemm launch");
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 16)) return fail(QP_ERR_INVALID_PARAMETER, "workspace must be 16-byte aligned");
+    if (workspace_bytes < qp_prefill_gemm_workspace_bytes(n, k, t))
+      return fail(QP_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu below the query", workspace_bytes);
+  }
+  return from_hip(qp::launch_gemm_split(qtype, w, n, k, x, x_dtype == QP_F32, t, ldx, y, ldy, (float*)workspace,
+                                        (int64_t)(workspace_bytes / 4), stream),
+                  "gemm launch");
+}
+
+size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  if (n <= 0 || k <= 0 || t < 0 || n > kMaxDim || k > kMaxDim || t > kMaxDim) return 0;
+  const int parts = qp::gemm_ksplit_parts(n, k, t);
+  if (parts <= 1) return 0;
+  return (size_t)((parts * t * n * 4 + 255) / 256 * 256);
 }
 
 qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,

@@ -66,6 +66,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
     const int m0 = blockIdx.y * BM;
     m_rows = min(BM, p.t - m0);
     base = m0;
+    // K split over gridDim.z parts of p.k weights each: part z starts
+    // z * p.k weights into every W and X row and writes its partial sums to
+    // its own dense output
+    if (gridDim.z > 1) {
+      const int z = blockIdx.z;
+      p.w += (int64_t)z * (p.k / F::QK) * F::TS;
+      p.x = (const char*)p.x + (int64_t)z * p.k * (MODE == kPlainF32 ? 4 : 2);
+      p.y += (int64_t)z * p.part_stride;
+    }
   }
 
   // ---- per-thread activation rows ---------------------------------------
@@ -208,6 +217,14 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
   return hipGetLastError();
 }
 
+static int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
 // Token-tile height: 256 halves the decode work per flop and is used when the
 // launch still fills the 256 CUs with one 256-token tile each.  The tall
 // kernel addresses a tile's activation rows with 32-bit byte offsets and
@@ -225,8 +242,45 @@ static bool use_tall_tiles(int qtype, int64_t n, int64_t k, int64_t t, int64_t l
   return t >= 512 && tiles >= 256 && tall_strides_ok(ldx, ldy) && tall_weights_ok(qtype, k);
 }
 
+// Sum of a plain projection's K parts, in part order:
+// y[r, c] = (..((p_0 + p_1) + p_2) ..) + p_{S-1}, partials dense (row stride n)
+// and part_stride floats apart.  One thread per 4 columns of a row.
+__global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict__ part, int64_t part_stride,
+                                                         int nparts, float* __restrict__ y, int64_t ldy, int t,
+                                                         int n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = (n + 3) / 4;
+  if (i >= (int64_t)t * q) return;
+  const int64_t r = i / q;
+  const int c = (int)(i - r * q) * 4;
+  const float* src = part + r * n + c;
+  float* dst = y + r * ldy + c;
+  for (int e = 0; e < 4 && c + e < n; ++e) {
+    float v = src[e];
+    for (int z = 1; z < nparts; ++z) v = v + src[(int64_t)z * part_stride + e];
+    dst[e] = v;
+  }
+}
+
+// K parts for a plain 128-tile launch that leaves the GPU under-filled: the
+// smallest power of two (at most 8) that gives one workgroup per CU, with
+// parts of whole 256-weight blocks.  1: no split.
+int gemm_ksplit_parts(int64_t n, int64_t k, int64_t t) {
+  const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
+  const int cus = cu_count();
+  int parts = 1;
+  while (parts < 8 && tiles * parts < cus && k % (256 * 2 * parts) == 0) parts *= 2;
+  return parts;
+}
+
 hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
                        int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+  return launch_gemm_split(qtype, w, n, k, x, x_f32, t, ldx, y, ldy, nullptr, 0, s);
+}
+
+hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
+                             int64_t ldx, float* y, int64_t ldy, float* partial, int64_t partial_floats,
+                             hipStream_t s) {
   GemmParams p = {};
   p.w = (const uint8_t*)w;
   p.rb = row_bytes_of(qtype, k);
@@ -241,6 +295,23 @@ hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const voi
   if (!x_f32 && use_tall_tiles(qtype, n, k, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
+  }
+  const int parts = partial != nullptr ? gemm_ksplit_parts(n, k, t) : 1;
+  if (parts > 1 && (int64_t)parts * t * n <= partial_floats) {
+    // the parts write dense partial sums (row stride n, 16-byte rows when
+    // n % 4 == 0), then one pass adds them in order into y
+    p.k = (int)(k / parts);
+    p.y = partial;
+    p.ldy = n;
+    p.part_stride = t * n;
+    p.vec_store = n % 4 == 0;
+    dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM), (uint32_t)parts);
+    hipError_t e = x_f32 ? launch_mode<kPlainF32>(qtype, grid, p, s) : launch_mode<kPlainF16>(qtype, grid, p, s);
+    if (e != hipSuccess) return e;
+    const int64_t threads = t * ((n + 3) / 4);
+    hipLaunchKernelGGL(ksplit_sum_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, s, partial, t * n,
+                       parts, y, ldy, (int)t, (int)n);
+    return hipGetLastError();
   }
   dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
   return x_f32 ? launch_mode<kPlainF32>(qtype, grid, p, s) : launch_mode<kPlainF16>(qtype, grid, p, s);
@@ -337,13 +408,6 @@ __global__ __launch_bounds__(256) void split_combine_kernel(SplitSum a, SplitSum
   }
 }
 
-static int cu_count() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return 256;
-  return cus;
-}
 
 // Finish time of workgroups issued in order onto `slots` compute units, one
 // at a time each (a tall tile takes a whole CU), with the given costs.

@@ -65,6 +65,7 @@ struct GemmParams {
   float* dbuf;           // [pairs][hidden]
   const float* weights;  // [pairs]
   GemmSegments seg;      // fused projections (kMulti)
+  int64_t part_stride;   // 128-tile plain modes split over gridDim.z K parts: floats between partial outputs
   int vec_store;         // 128-tile kernel: output rows are 16-byte multiples (16-byte stores)
 };
 

@@ -12,6 +12,13 @@ hipError_t launch_dequant(int qtype, bool f16out, const void* src, int64_t rows,
 
 hipError_t launch_gemm(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
                        int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+// The same with room for partial sums (partial_floats floats, 16-byte
+// aligned; null: none): an under-filled 128-tile launch is split into
+// gemm_ksplit_parts() K parts whose sums one pass adds in order.
+hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
+                             int64_t ldx, float* y, int64_t ldy, float* partial, int64_t partial_floats,
+                             hipStream_t s);
+int gemm_ksplit_parts(int64_t n, int64_t k, int64_t t);
 
 hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,
                               int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,

@@ -77,6 +77,15 @@ def test_gemm_rejections():
     assert q(qp.Q4_K, FAKE, 192, 256, FAKE, 8, 256, 128, FAKE, 0, 1e-6, FAKE, 192, None) == 1  # n % hd
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, FAKE, 0, 0.0, FAKE, 256, None) == 1   # eps
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, None, 0, 1e-6, FAKE, 256, None) == 1  # gain
+    # the K-split variant: same checks, plus its workspace
+    gw = L.qp_prefill_gemm_ws
+    assert gw(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 8, 128, FAKE, 64, None, 0, None) == 1   # ldx < k
+    assert L.qp_prefill_gemm_workspace_bytes(0, 256, 8) == 0
+    need = L.qp_prefill_gemm_workspace_bytes(128, 2048, 128)    # one tile: split into 8 parts of 256
+    assert need == 8 * 128 * 128 * 4
+    assert L.qp_prefill_gemm_workspace_bytes(128, 256, 128) == 0  # one 256-weight block: nothing to split
+    assert gw(qp.Q4_K, FAKE, 128, 2048, FAKE, qp.F16, 128, 2048, FAKE, 128, FAKE, need - 16, None) == 3
+    assert gw(qp.Q4_K, FAKE, 128, 2048, FAKE, qp.F16, 128, 2048, FAKE, 128, FAKE + 4, need, None) == 1
     f = L.qp_prefill_gemm_qkv
     good = [qp.Q4_K, FAKE, 256, FAKE, 128, FAKE, 128, 256, FAKE, 8, 256, 128, FAKE, 0, FAKE, 0, 1e-6,
             FAKE, 256, FAKE, 128, FAKE, 128, None, 0, None]

@@ -44,6 +44,32 @@ def test_small_shapes(orc, qtype, t, n, k):
     assert_close(y, ref, f"{synth.NAMES[qtype]} {t}x{n}x{k}")
 
 
+# launches with fewer 128-token tiles than the GPU has CUs: with a workspace
+# K is split into parts whose sums one pass adds in order
+KSPLIT = [(Q4_K, 512, 2048, 2048), (Q6_K, 64, 1024, 4096), (Q2_K, 300, 96, 2048), (F16W, 40, 256, 1024),
+          (Q5_K, 1, 128, 6144)]
+
+
+@pytest.mark.parametrize("qtype,t,n,k", KSPLIT, ids=[f"{synth.NAMES[c[0]]}-{c[1]}x{c[2]}x{c[3]}" for c in KSPLIT])
+def test_ksplit_against_whole(orc, qtype, t, n, k):
+    import torch
+    say(f"gemm ksplit {synth.NAMES[qtype]} t={t} n={n} k={k}")
+    raw = weights(qtype, n, k, 8050 + n)
+    x = act_f16(t, k, 8051 + t)
+    w, xt = to_dev(raw), to_dev(x).view(torch.float16)
+    assert qp.gemm_workspace(n, k, t, "cuda") is not None, "this shape should split"
+    ys = qp.prefill_gemm(qtype, w, n, k, xt)
+    ys2 = qp.prefill_gemm(qtype, w, n, k, xt)
+    yw = qp.prefill_gemm(qtype, w, n, k, xt, workspace=False)
+    torch.cuda.synchronize()
+    ys, ys2, yw = ys.cpu().numpy(), ys2.cpu().numpy(), yw.cpu().numpy()
+    tok = sample_tokens(t, 12, 8052) if t > 64 else np.arange(t)
+    ref = orc.prefill_gemm(qtype, raw, n, k, x, tokens=tok)
+    assert_close(ys[tok], ref, f"split {synth.NAMES[qtype]} {t}x{n}x{k}")
+    assert_close(yw[tok], ref, f"whole {synth.NAMES[qtype]} {t}x{n}x{k}")
+    assert np.array_equal(ys, ys2), "split results differ between two calls"
+
+
 def test_f32_activations(orc):
     """f32 X (rounded to binary16 on load), the 64 x 1024 x 1024 Q8_0 projection."""
     raw = weights(Q8_0, 1024, 1024, synth.seed_for(0, 0))
