@@ -13,8 +13,8 @@
 // store instruction of a wave writes 1 KB of contiguous output.  Each lane
 // reads only the few bytes of its V weights (quants, scale, d), which the
 // wave's lanes fetch from the same one or two blocks.  A wave handles G such
-// groups, issuing all loads before the first store: G = 1 for f32 (the HBM
-// write stream wants many short-lived waves), G = 2 for f16.
+// groups, issuing all loads before the first store; G = 1 measured fastest
+// (the HBM write stream wants many short-lived waves).
 //
 // Partial last blocks (cols % QK != 0): one thread decodes one unit (32
 // consecutive weights of a block).  Rows of the tensor are whole blocks back
@@ -151,10 +151,7 @@ template <int QT, bool F16OUT>
 static hipError_t launch_dequant_t(const void* src, int64_t rows, int64_t cols, void* dst, hipStream_t s) {
   using F = Fmt<QT>;
   if (cols % F::QK == 0 && ((uintptr_t)dst & 15) == 0) {
-    // f32: one group (1 KB of output) per wave, more waves in flight beat
-    // more stores per wave; f16: two adjacent groups per wave (a group is
-    // only 512 weights there), measured ~3% faster on the 8B tensors
-    constexpr int G = F16OUT ? 2 : 1;
+    constexpr int G = 1;  // one group per wave: more waves in flight beat more stores per wave
     const uint64_t total = (uint64_t)rows * cols;
     const uint64_t gw = F16OUT ? 512 : 256;
     const uint64_t waves = ((total + gw - 1) / gw + G - 1) / G;
