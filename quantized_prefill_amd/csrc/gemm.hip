@@ -346,8 +346,8 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
 // Sums of the two K halves of split projections (k and v of the fused
 // q/k/v launch), in that order: y = p0 + p1 (t x n, partials dense with row
 // stride n, n % 8 == 0).  With hd > 0 the per-head RMSNorm follows, with the
-// operations of the fused epilogue (sum of squares in f32, 1 / sqrt(ss *
-// (1 / hd) + eps), then y * scale * gain).  One wave per (token, 512-column
+// operations of the fused epilogue (sum of squares in f32, scale =
+// rsq(ss * (1 / hd) + eps) with v_rsq_f32, then y * scale * gain).  One wave per (token, 512-column
 // slab of its row); lane l holds columns 8 l .. 8 l + 7 of the slab, so a
 // head (hd = 64 or 128) is hd / 8 adjacent lanes.  Both projections in one
 // launch: the first one's waves, then the second one's.
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(SplitSum a, SplitSum
   for (int e = 0; e < 4; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
   const int lanes = q.hd / 8;  // 8 or 16 lanes per head
   for (int m = 1; m < lanes; m <<= 1) ss += __shfl_xor(ss, m, 64);
-  const float scale = 1.f / __builtin_sqrtf(ss * (1.f / (float)q.hd) + eps);
+  const float scale = __builtin_amdgcn_rsqf(ss * (1.f / (float)q.hd) + eps);
   if (ok) {
     const int head = c / q.hd;
     const float* g = q.gain + (int64_t)head * q.gstride + (c - head * q.hd);

@@ -149,10 +149,13 @@ __device__ __forceinline__ void store_block_vec(const GemmParams& p, float16v (&
 template <int MODE, int MI>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&acc)[MI][2], int base, int m_rows,
                                               int n0, int wm, int wn, int lane, float* red, bool active = true,
-                                              float* vec_scratch = nullptr) {
+                                              float* vec_scratch = nullptr, float* sum_scratch = nullptr) {
   constexpr int WM = 32 * MI;
   if (!active) {
-    if constexpr (MODE == kQkNorm) __syncthreads();
+    if constexpr (MODE == kQkNorm) {
+      if (sum_scratch) __syncthreads();
+      __syncthreads();
+    }
     return;
   }
   // The lane index from the hardware lane counter: lane-derived values here
@@ -182,15 +185,43 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
     // the 32 lanes that share a row, parked in LDS; after one barrier a head
     // of 64 columns reads its wave's sum, a head of 128 adds the two waves'.
     constexpr int TM = 2 * WM;
+    if (sum_scratch && MI % 2 == 0) {
+      // Through LDS instead of 5 dependent lane shuffles per row: after one
+      // barrier (other waves may still read their last chunk or have copies
+      // in flight until then) each wave owns 64 rows x 36 floats of
+      // sum_scratch.  Per 64 rows (two MFMA tiles along M) every lane writes
+      // its squares row-major, then lane l adds up row l with 16-byte reads.
+      // (The row pitch of 36 floats keeps those reads free of conflicts.)
+      __syncthreads();
+      constexpr int SP = 36;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int h = 0; h < MI / 2; ++h) {
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        float v = acc[i][0][a] * acc[i][0][a] + acc[i][1][a] * acc[i][1][a];
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
-        if ((lane & 31) == 0) red[wn * TM + row_of(i, a)] = v;
+          for (int a = 0; a < 16; ++a) {
+            const int rl = 32 * ii + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3);
+            const int i = 2 * h + ii;
+            sum_scratch[rl * SP + (lane & 31)] = acc[i][0][a] * acc[i][0][a] + acc[i][1][a] * acc[i][1][a];
+          }
+        const float4v* rowp = (const float4v*)(sum_scratch + lane * SP);
+        float4v t4 = rowp[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) t4 += rowp[q];
+        red[wn * TM + WM * wm + 64 * h + lane] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+        asm volatile("" ::: "memory");  // the next 64 rows overwrite the scratch
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          float v = acc[i][0][a] * acc[i][0][a] + acc[i][1][a] * acc[i][1][a];
+#pragma unroll
+          for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
+          if ((lane & 31) == 0) red[wn * TM + row_of(i, a)] = v;
+        }
+    }
     __syncthreads();
     const float inv_hd = 1.f / (float)p.hd;
     const bool pair_heads = p.hd == 128;
@@ -210,7 +241,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
         for (int a = 0; a < 16; ++a) {
           const int r = row_of(i, a);
           const float ss = pair_heads ? red[r] + red[TM + r] : red[wn * TM + r];
-          const float scale = 1.f / __builtin_sqrtf(ss * inv_hd + p.eps);
+          const float scale = __builtin_amdgcn_rsqf(ss * inv_hd + p.eps);  // v_rsq_f32 (about 1 ulp)
 #pragma unroll
           for (int j = 0; j < 2; ++j) acc[i][j][a] = acc[i][j][a] * scale * g[j];
         }
@@ -223,7 +254,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
       for (int a = 0; a < 16; ++a) {
         const int r = row_of(i, a);
         const float ss = pair_heads ? red[r] + red[TM + r] : red[wn * TM + r];
-        const float scale = 1.f / __builtin_sqrtf(ss * inv_hd + p.eps);
+        const float scale = __builtin_amdgcn_rsqf(ss * inv_hd + p.eps);  // v_rsq_f32 (about 1 ulp)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + 64 * wn + 32 * j + (lane & 31);

@@ -300,13 +300,17 @@ __global__ __launch_bounds__(2 * NT) void gemm_tall_kernel(GemmParams pk) {
     // direct load targets them, and after the last barrier only the unused
     // next-chunk fragment reads touch them
     float* vec = (float*)sm.w[0] + 32 * 40 * role_idx;
+    // QK-norm row sums: 64 x 36 floats per consumer wave in the activation
+    // ring, free once every wave has passed the epilogue's first barrier
+    float* sums = (float*)sm.x + 64 * 36 * role_idx;
+    static_assert(sizeof(sm.x) >= 4 * 64 * 36 * sizeof(float), "activation ring holds the row-sum scratch");
     if constexpr (MODE == kMulti) {
       if (norm)
-        gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
+        gemm_epilogue<kQkNorm, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec, sums);
       else
         gemm_epilogue<kPlainF16, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
     } else {
-      gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec);
+      gemm_epilogue<MODE, TMI>(p, acc, m0, m_rows, n0, wm, wn, lane, red, active, vec, sums);
     }
   };
 
