@@ -185,6 +185,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
     // the 32 lanes that share a row, parked in LDS; after one barrier a head
     // of 64 columns reads its wave's sum, a head of 128 adds the two waves'.
     constexpr int TM = 2 * WM;
+    // this lane's two gains, loaded first so that their latency passes
+    // under the row sums
+    float g[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+      const int head = col / p.hd;
+      g[j] = col < p.n ? p.gain[(int64_t)head * p.gstride + (col - head * p.hd)] : 0.f;
+    }
     if (sum_scratch && MI % 2 == 0) {
       // Through LDS instead of 5 dependent lane shuffles per row: after one
       // barrier (other waves may still read their last chunk or have copies
@@ -228,13 +237,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
     if (vec_scratch) {
       // normalise in place, then the plain 16-byte store (same products in
       // the same order as below)
-      float g[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-        const int head = col / p.hd;
-        g[j] = col < p.n ? p.gain[(int64_t)head * p.gstride + (col - head * p.hd)] : 0.f;
-      }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -258,9 +260,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-          const int head = col / p.hd;
-          const float g = p.gain[(int64_t)head * p.gstride + (col - head * p.hd)];
-          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a] * scale * g;
+          if (r < m_rows && col < p.n) p.y[(int64_t)(base + r) * p.ldy + col] = acc[i][j][a] * scale * g[j];
         }
       }
   } else if constexpr (MODE == kGateUp) {
