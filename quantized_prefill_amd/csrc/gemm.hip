@@ -196,11 +196,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
   }
 
   // after the loop's last barrier the tiles are free: the norm's row sums
-  // (2 x 2 x 64 floats) and then one 32 x 40 transpose buffer per wave
+  // (2 x 2 x 64 floats), one 32 x 40 transpose buffer per wave, and 64 x 36
+  // floats per wave for the row reductions (sums of squares, maxima of |h|)
   float* const lds = (float*)&sm;
-  static_assert(sizeof(GemmSmem) >= (2 * 2 * 64 + 4 * 32 * 40) * 4, "epilogue scratch");
+  static_assert(sizeof(GemmSmem) >= (2 * 2 * 64 + 4 * 32 * 40 + 4 * 64 * 36) * 4, "epilogue scratch");
   gemm_epilogue<MODE, 2>(p, acc, base, m_rows, n0, wm, wn, lane, lds,
-                         true, p.vec_store ? lds + 2 * 2 * 64 + 32 * 40 * wave : nullptr);
+                         true, p.vec_store ? lds + 2 * 2 * 64 + 32 * 40 * wave : nullptr,
+                         MODE == kGateUp || MODE == kQkNorm ? lds + 2 * 2 * 64 + 4 * 32 * 40 + 64 * 36 * wave
+                                                            : nullptr);
 }
 
 template <int MODE>

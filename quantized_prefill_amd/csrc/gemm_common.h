@@ -267,6 +267,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
     // acc[i][0] = gate, acc[i][1] = up for output column n0 + 32 wn + lane%32
     const int col = n0 + 32 * wn + (lane & 31);
     float16v hv[MI][1];
+    // Row maxima of |h| over the wave's 32 columns: with sum_scratch (64 x 36
+    // floats of this wave's own LDS, MI == 2) the values are written
+    // row-major and lane l takes the maximum of row l with 16-byte reads;
+    // otherwise 5 lane shuffles per row value.
+    constexpr int SP = 36;
+    const bool via_lds = sum_scratch != nullptr && MI == 2;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -278,10 +284,28 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, float16v (&ac
         const bool ok = r < m_rows && col < p.n;
         if (ok && !vec_scratch) p.hbuf[(int64_t)(base + r) * p.n + col] = h;
         float mx = ok ? __builtin_fabsf(h) : 0.f;
+        if (via_lds) {
+          sum_scratch[(32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3)) * SP + (lane & 31)] = mx;
+        } else {
 #pragma unroll
-        for (int m = 1; m < 32; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
-        if ((lane & 31) == 0 && r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
+          for (int m = 1; m < 32; m <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+          if ((lane & 31) == 0 && r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
+        }
       }
+    if (via_lds) {
+      const float4v* rowp = (const float4v*)(sum_scratch + lane * SP);
+      float4v m4 = rowp[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) {
+        const float4v v4 = rowp[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m4[e] = __builtin_fmaxf(m4[e], v4[e]);
+      }
+      const float mx = __builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]));
+      const int r = WM * wm + lane;  // lane l holds row l of the wave's block
+      if (r < m_rows) atomicMax(p.rowmax + base + r, __builtin_bit_cast(uint32_t, mx));
+      asm volatile("" ::: "memory");
+    }
     if (vec_scratch) {
       const int r0 = base + WM * wm;
       store_tiles_vec<MI, 1>(hv, m_rows - WM * wm, n0 + 32 * wn, p.n, lane, vec_scratch,
