@@ -128,9 +128,11 @@ qp_status qp_prefill_gemm(int qtype, const void* w, int64_t n, int64_t k, const 
                           int64_t t, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 
 /*
- * qp_prefill_gemm with an optional workspace (the callers that give one let
- * a launch that would leave the GPU under-filled use all of it, the
- * stream-K-style split of the pages' shape-adaptive prefill):
+ * qp_prefill_gemm with an optional workspace, so that a launch whose shape
+ * would leave the GPU under-filled can use all of it (a shape-dependent
+ * choice of work split, as the per-format shape probe of "CUDA prefill VRAM
+ * loans and SM75 Q4/native-IQ opt-ins", section "Summary", makes one per
+ * weight format):
  *   workspace (device): qp_prefill_gemm_workspace_bytes(n, k, t) bytes,
  *     16-byte aligned, no initial contents needed; NULL (or a query of 0):
  *     exactly qp_prefill_gemm.
