@@ -57,6 +57,29 @@ def test_moe_small(orc, qtype):
     assert_close(y, ref, f"moe small {synth.NAMES[qtype]}")
 
 
+@pytest.mark.parametrize("qtype", [Q4_K, Q5_K, Q8_0, Q6_K, Q2_K, F16W], ids=["Q4_K", "Q5_K", "Q8_0", "Q6_K", "Q2_K",
+                                                                          "F16"])
+def test_moe_long_skewed_lists(orc, qtype):
+    """Long per-expert lists from skewed routing: one list of several tiles
+    (the last ragged), one empty expert; two calls give identical bits."""
+    t, ne, k, hidden, inter = 1024, 5, 2, 256, 512
+    wg = synth.quant_weights(qtype, ne * inter, hidden, 9650)
+    wu = synth.quant_weights(qtype, ne * inter, hidden, 9651)
+    wd = synth.quant_weights(qtype, ne * hidden, inter, 9652)
+    x = act_f16(t, hidden, 9653)
+    lg = synth.router_logits(t, ne, 9654)
+    lg[:, 0] += 1.5    # expert 0 takes most tokens
+    lg[:, 3] -= 100.0  # expert 3 never chosen
+    ids, wts = orc.route_topk(lg, k)
+    say(f"moe long lists {synth.NAMES[qtype]} counts {np.bincount(ids.reshape(-1), minlength=ne).tolist()}")
+    y = run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts)
+    tok = sample_tokens(t, 64, 9655)
+    ref = orc.moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts, tokens=tok)
+    assert_close(y[tok], ref, f"moe long lists {synth.NAMES[qtype]}")
+    y2 = run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts)
+    assert np.array_equal(y, y2), "routed FFN differs between two calls"
+
+
 def test_moe_invalid_ids_and_determinism(orc):
     """Pairs whose expert id is out of range add nothing; results repeat bit for bit."""
     t, ne, k, hidden, inter = 64, 4, 2, 256, 256
