@@ -74,6 +74,8 @@ class Oracle:
         L.or_route_topk.restype = i32
         L.or_moe.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i64, i64, vp, vp, vp, i64, vp]
         L.or_moe.restype = i32
+        L.or_attention.argtypes = [i32, vp, i64, vp, vp, i64, i64, i64, i64, i64, dbl, vp, i64, vp]
+        L.or_attention.restype = i32
         L.or_plant.restype = i32
         L.or_plant_count.restype = i32
         L.or_plant_name.argtypes = [i32]
@@ -192,6 +194,28 @@ class Oracle:
                             top_k, _p(ids), _p(weights), _p(tok), tok.size, _p(out))
         if rc != 0:
             raise ValueError("oracle moe rejected its arguments")
+        return out
+
+    # -- prompt attention --------------------------------------------------
+    def attention(self, kvtype, q, k_cache, v_cache, n_past, n_head, n_kv, head_dim, scale=None,
+                  tokens=None) -> np.ndarray:
+        """float64 [len(tokens), n_head * head_dim]; q is float32 [T, >= n_head*head_dim];
+        the caches are flat uint8 arrays of (n_past + T) * n_kv rows of head_dim weights."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        t = q.shape[0]
+        if scale is None:
+            scale = 1.0 / np.sqrt(head_dim)
+        kc = np.ascontiguousarray(k_cache, dtype=np.uint8).reshape(-1)
+        vc = np.ascontiguousarray(v_cache, dtype=np.uint8).reshape(-1)
+        need = (n_past + t) * n_kv * self.row_bytes(kvtype, head_dim)
+        if kc.size < need or vc.size < need:
+            raise ValueError(f"KV cache holds {min(kc.size, vc.size)} bytes, needs {need}")
+        tok = np.arange(t, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+        out = np.empty((tok.size, n_head * head_dim), dtype=np.float64)
+        rc = self._L.or_attention(kvtype, _p(q), q.shape[1], _p(kc), _p(vc), n_past, t, n_head, n_kv, head_dim,
+                                  float(scale), _p(tok), tok.size, _p(out))
+        if rc != 0:
+            raise ValueError("oracle attention rejected its arguments")
         return out
 
 

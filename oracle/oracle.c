@@ -19,7 +19,9 @@
  *   - "CUDA prefill VRAM loans and SM75 Q4/native-IQ opt-ins" (Strata PR),
  *     sections "Summary" and "Correctness and safety": routed experts run as a
  *     fused prefill path whose routing ids, expert selection, route weights
- *     and scatter order are those of the unfused path.
+ *     and scatter order are those of the unfused path.  Section "Summary"
+ *     and the table after it: prompt attention runs over a KV cache held
+ *     quantized (Q4_0 or INT8 per row), as a tensor-core path of its own.
  * The pages name the block types but do not print their bit layouts; the
  * layouts below are the GGUF/ggml on-disk convention, restated as formulas.
  *
@@ -78,14 +80,18 @@
 #define PLANT_Q5_NO_HIGH       24  /* Q5_K qh bit dropped */
 #define PLANT_Q5_HIGH_BIT      25  /* Q5_K qh bit chosen by the nibble half only, not the sub-block */
 #define PLANT_F16W_BYTES       26  /* F16 weights read big-endian */
-#define PLANT_COUNT            27
+#define PLANT_ATTN_NO_MASK     27  /* queries also attend to later keys */
+#define PLANT_ATTN_GQA         28  /* q head h reads kv head h % n_kv instead of h / group */
+#define PLANT_ATTN_NO_SCALE    29  /* scores not multiplied by the scale */
+#define PLANT_COUNT            30
 
 static const char* const plant_names[PLANT_COUNT] = {
     "none", "q8_unsigned", "q6_no_offset", "q6_no_high", "q4_scale_high",
     "scale_select", "d_for_dmin", "row_stride", "tail", "f16_rtz", "f16_scale",
     "q2_nibbles", "q4_nibble", "q6_shift", "gemm_transpose", "gemm_drop_k",
     "qkn_sum", "qkn_eps", "qkn_gain", "silu_sign", "moe_weight", "router_tie",
-    "router_renorm", "moe_up", "q5_no_high", "q5_high_bit", "f16w_bytes"};
+    "router_renorm", "moe_up", "q5_no_high", "q5_high_bit", "f16w_bytes",
+    "attn_no_mask", "attn_gqa", "attn_no_scale"};
 
 int or_plant(void) { return QP_PLANT; }
 int or_plant_count(void) { return PLANT_COUNT; }
@@ -661,5 +667,85 @@ int or_moe(int qtype, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
     free(xd);
     free(h);
   }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* prompt attention                                                          */
+
+/* Causal prompt attention of one chunk over a quantized KV cache, binary64
+ * ("CUDA prefill VRAM loans and SM75 Q4/native-IQ opt-ins", section
+ * "Summary" and the KV table after it: prompt attention over a KV cache
+ * stored as quantized rows).  The cache holds kv_len = n_past + t tokens;
+ * the row of token r and kv head g starts at byte (r*n_kv + g)*row_bytes(
+ * kvtype, head_dim) of kc (keys) and vc (values) and decodes as a weight row
+ * does.  Query i of the chunk (i < t) sits at position n_past + i and sees
+ * keys 0 .. n_past + i.  Query head h reads kv head h / (n_head / n_kv)
+ * (grouped-query attention).  For each sampled query i = tok[..] and head h:
+ *   s_r = scale * (q[i, h] . k[r, g])            r = 0 .. n_past + i
+ *   p_r = exp(s_r - max_r s_r) / sum_r exp(s_r - max_r s_r)
+ *   out[i, h] = sum_r p_r v[r, g]
+ * q is f32 with row stride ldq; head h is columns h*head_dim ..
+ * out is [ntok][n_head*head_dim]. */
+int or_attention(int kvtype, const float* q, int64_t ldq, const uint8_t* kc, const uint8_t* vc,
+                 int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv, int64_t head_dim,
+                 double scale, const int64_t* tok, int64_t ntok, double* out) {
+  if (or_block_size(kvtype) < 0 || n_past < 0 || t < 0 || n_head <= 0 || n_kv <= 0 ||
+      n_head % n_kv != 0 || head_dim <= 0 || head_dim % or_block_size(kvtype) != 0)
+    return -1;
+  for (int64_t i = 0; i < ntok; ++i)
+    if (tok[i] < 0 || tok[i] >= t) return -1;
+  const int64_t kv_len = n_past + t, group = n_head / n_kv;
+  const int64_t rb = or_row_bytes(kvtype, head_dim);
+#if QP_PLANT == PLANT_ATTN_NO_SCALE
+  scale = 1.0;
+#endif
+  /* decode the whole cache once (values in binary32, exact, as for weights) */
+  float* kf = (float*)malloc(sizeof(float) * (size_t)(kv_len * n_kv * head_dim + 1));
+  float* vf = (float*)malloc(sizeof(float) * (size_t)(kv_len * n_kv * head_dim + 1));
+  for (int64_t r = 0; r < kv_len * n_kv; ++r) {
+    dequant_row(kvtype, kc + r * rb, head_dim, kf + r * head_dim);
+    dequant_row(kvtype, vc + r * rb, head_dim, vf + r * head_dim);
+  }
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)kv_len);
+#pragma omp for collapse(2) schedule(dynamic)
+    for (int64_t i = 0; i < ntok; ++i) {
+      for (int64_t h = 0; h < n_head; ++h) {
+#if QP_PLANT == PLANT_ATTN_GQA
+        const int64_t g = h % n_kv;
+#else
+        const int64_t g = h / group;
+#endif
+#if QP_PLANT == PLANT_ATTN_NO_MASK
+        const int64_t last = kv_len - 1;
+#else
+        const int64_t last = n_past + tok[i];
+#endif
+        const float* qi = q + tok[i] * ldq + h * head_dim;
+        double mx = -INFINITY;
+        for (int64_t r = 0; r <= last; ++r) {
+          const float* kr = kf + (r * n_kv + g) * head_dim;
+          double dot = 0.0;
+          for (int64_t j = 0; j < head_dim; ++j) dot += (double)qi[j] * (double)kr[j];
+          s[r] = scale * dot;
+          if (s[r] > mx) mx = s[r];
+        }
+        double sum = 0.0;
+        for (int64_t r = 0; r <= last; ++r) { s[r] = exp(s[r] - mx); sum += s[r]; }
+        double* o = out + (i * n_head + h) * head_dim;
+        for (int64_t j = 0; j < head_dim; ++j) o[j] = 0.0;
+        for (int64_t r = 0; r <= last; ++r) {
+          const float* vr = vf + (r * n_kv + g) * head_dim;
+          const double p = s[r] / sum;
+          for (int64_t j = 0; j < head_dim; ++j) o[j] += p * (double)vr[j];
+        }
+      }
+    }
+    free(s);
+  }
+  free(kf);
+  free(vf);
   return 0;
 }

@@ -176,6 +176,17 @@ def router_logits(tokens: int, experts: int, seed: int) -> np.ndarray:
     return normal(seed, tokens * experts).astype(np.float32).reshape(tokens, experts)
 
 
+def kv_cache(kvtype: int, tokens: int, n_kv: int, head_dim: int, seed: int) -> np.ndarray:
+    """A KV cache of tokens x n_kv rows of head_dim values, flat uint8:
+    binary16 N(0, 1) draws, or Q8_0 blocks with scales in [1/64, 1/32] and
+    quants uniform in [-127, 127] (values within about +-4)."""
+    if kvtype == F16W:
+        return f16_bits(normal(seed, tokens * n_kv * head_dim)).view(np.uint8).reshape(-1)
+    if kvtype == Q8_0:
+        return quant_weights(Q8_0, tokens * n_kv, head_dim, seed, 1.0 / 64, 1.0 / 32)
+    raise ValueError(f"no KV cache recipe for type {kvtype}")
+
+
 # ---------------------------------------------------------------------------
 # Workloads.  Shapes are (out_features N, in_features K) per projection.
 

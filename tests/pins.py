@@ -525,4 +525,78 @@ def pin_moe_dense(o):
     assert np.array_equal(out_p, out[perm]), "token permutation"
 
 
+# ---------------------------------------------------------------------------
+# Prompt attention.  Caches are [token][kv head][head_dim] rows; the binary16
+# cache is built with numpy's conversion, the Q8_0 cache with enc_q8_0, so
+# every cache value is known exactly here.
+
+def _f16_cache(vals: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(vals, dtype=np.float16).view(np.uint8).reshape(-1)
+
+
+def _q8_cache(d_bits: int, q: np.ndarray) -> np.ndarray:
+    """Q8_0 cache of rows of 32 weights: one block per row, scale d_bits."""
+    q = np.asarray(q).reshape(-1, 32)
+    return np.concatenate([enc_q8_0(d_bits, row) for row in q])
+
+
+def pin_attention_zero_query_prefix_mean(o):
+    """q = 0 gives equal weights, so query i returns the mean of value rows
+    0 .. n_past + i (later rows must not count)."""
+    n_past, t, n_head, hd = 3, 5, 2, 32
+    kv = n_past + t
+    rng = np.random.default_rng(601)
+    v16 = rng.integers(-64, 64, size=(kv, 1, hd)) / 8.0
+    k16 = rng.standard_normal((kv, 1, hd))
+    q = np.zeros((t, n_head * hd), np.float32)
+    out = o.attention(F16W, q, _f16_cache(k16), _f16_cache(v16), n_past, n_head, 1, hd)
+    for i in range(t):
+        want = v16[:n_past + i + 1, 0].mean(axis=0)
+        for h in range(n_head):
+            assert np.allclose(out[i, h * hd:(h + 1) * hd], want, rtol=0, atol=1e-12), f"prefix mean q{i} h{h}"
+    # the same through a Q8_0 cache: values d * q with d = 1/4
+    qv = rng.integers(-127, 128, size=(kv, 32))
+    out = o.attention(Q8_0, q[:, :32], _q8_cache(h16(0.25), np.zeros((kv, 32))), _q8_cache(h16(0.25), qv),
+                      n_past, 1, 1, 32)
+    for i in range(t):
+        want = 0.25 * qv[:n_past + i + 1].mean(axis=0)
+        assert np.allclose(out[i], want, rtol=0, atol=1e-12), f"Q8_0 prefix mean q{i}"
+
+
+def pin_attention_gqa_constant_values(o):
+    """Values constant over tokens, c_g for kv head g: every query of head h
+    returns c_{h // (n_head / n_kv)} whatever the scores are."""
+    n_past, t, n_head, n_kv, hd = 2, 4, 6, 3, 32
+    kv = n_past + t
+    rng = np.random.default_rng(602)
+    c = rng.integers(-50, 50, size=(n_kv, hd)) / 4.0
+    v16 = np.broadcast_to(c, (kv, n_kv, hd))
+    k16 = rng.standard_normal((kv, n_kv, hd))
+    q = rng.standard_normal((t, n_head * hd)).astype(np.float32)
+    out = o.attention(F16W, q, _f16_cache(k16), _f16_cache(v16), n_past, n_head, n_kv, hd)
+    for h in range(n_head):
+        want = c[h // (n_head // n_kv)]
+        assert np.allclose(out[:, h * hd:(h + 1) * hd], want[None, :], rtol=0, atol=1e-12), f"GQA head {h}"
+
+
+def pin_attention_two_keys_logistic(o):
+    """One query over two keys: k0 = 0 and k1 = a*u with q = u gives scores 0
+    and scale*a*|u|^2, so the output is v0 + sigmoid(scale*a*|u|^2) (v1 - v0);
+    a single visible key returns its value row exactly."""
+    hd, a, scale = 32, 0.5, 0.375
+    u = np.zeros(hd)
+    u[[1, 5, 9, 30]] = [1.0, -2.0, 0.5, 1.5]
+    k16 = np.stack([np.zeros(hd), a * u])[:, None, :]
+    rng = np.random.default_rng(603)
+    v16 = (rng.integers(-32, 32, size=(2, 1, hd)) / 4.0)
+    q = u[None, :].astype(np.float32)
+    out = o.attention(F16W, q, _f16_cache(k16), _f16_cache(v16), 1, 1, 1, hd, scale=scale)
+    z = scale * a * float(u @ u)
+    sig = 0.5 * (1.0 + math.tanh(0.5 * z))
+    want = v16[0, 0] + sig * (v16[1, 0] - v16[0, 0])
+    assert np.allclose(out[0], want, rtol=1e-12, atol=1e-12), "two-key logistic"
+    one = o.attention(F16W, q, _f16_cache(k16), _f16_cache(v16), 0, 1, 1, hd, scale=scale)
+    assert np.array_equal(one[0], v16[0, 0]), "single key"
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
