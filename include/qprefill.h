@@ -252,6 +252,36 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
                                  float* out, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/*
+ * Causal prompt attention of one prefill chunk over a KV cache held as
+ * binary16 or Q8_0 rows ("CUDA prefill VRAM loans and SM75 Q4/native-IQ
+ * opt-ins", section "Summary" and the KV table after it: prompt attention as
+ * a tensor-core path over a quantized KV cache).  The cache holds
+ * kv_len = n_past + t tokens (earlier chunks, then this one); query i of the
+ * chunk sits at position n_past + i and sees keys 0 .. n_past + i.  Query
+ * head h reads kv head h / (n_head / n_kv_head).  For query i, head h:
+ *   s_r = scale * (q[i, h] . k[r, g]),  p = softmax_r(s),  out[i, h] = sum_r p_r v[r, g]
+ *   kv_type: QP_F16W (binary16 values) or QP_Q8_0 (one 34-byte block per 32
+ *            values: "INT8" cache rows).
+ *   q (device): t rows of f32, row stride ldq floats; head h is columns
+ *               h*head_dim .. (h+1)*head_dim-1 (the layout of the q
+ *               projection's output).
+ *   k_cache, v_cache (device): kv_len * n_kv_head rows of head_dim values in
+ *               kv_type, row (r * n_kv_head + g) for token r and kv head g.
+ *   out (device): t rows of f32, row stride ldo, head h at h*head_dim.
+ * Arithmetic: Q, K, V and the probabilities enter FP16 MFMA products
+ * (nearest-even binary16 of the f32 / exact cache values); scores, softmax
+ * and accumulation are f32.  Requires head_dim == 128, n_head a multiple of
+ * n_kv_head, n_head <= 1024, n_past + t < 2^31, ldq and ldo >= n_head*head_dim
+ * and multiples of 4, q and out 16-byte aligned, caches 16-byte (F16) or
+ * 2-byte (Q8_0) aligned, a finite scale.  t == 0 is a no-op.  out must not
+ * overlap q or the caches.  Errors: QP_ERR_UNSUPPORTED_TYPE for another
+ * kv_type, QP_ERR_INVALID_PARAMETER otherwise.
+ */
+qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                              int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
+                              float scale, float* out, int64_t ldo, hipStream_t stream);
+
 /* Static English name of a status ("QP_OK", ...). */
 const char* qp_status_string(qp_status s);
 

@@ -38,6 +38,7 @@ SIGNATURES = {
     "qp_grouped_expert_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "qp_grouped_expert_gemm": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP, _VP,
                                       _SZ, _VP]),
+    "qp_prompt_attention": (_INT, [_INT, _VP, _I64, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _F32C, _VP, _I64, _VP]),
     "qp_status_string": (C.c_char_p, [_INT]),
     "qp_last_error_detail": (C.c_char_p, []),
 }
@@ -251,4 +252,20 @@ def grouped_expert_gemm(qtype: int, w_gate, w_up, w_down, n_experts: int, hidden
                                        n_experts, hidden, inter, _dev(x, "x"), t, top_k, _dev(ids, "ids"),
                                        _dev(weights, "weights"), _dev(out, "out"), _dev(workspace, "workspace"),
                                        workspace.numel(), _stream()))
+    return out
+
+
+def prompt_attention(kv_type: int, q, k_cache, v_cache, n_past: int, n_head: int, n_kv_head: int,
+                     head_dim: int = 128, scale: float | None = None, out=None):
+    """Causal prompt attention of a chunk of q.shape[0] queries over a KV cache of
+    n_past + q.shape[0] tokens (flat byte tensors of binary16 or Q8_0 rows)."""
+    torch = _torch()
+    t = q.shape[0]
+    if scale is None:
+        scale = head_dim ** -0.5
+    if out is None:
+        out = torch.empty((t, n_head * head_dim), dtype=torch.float32, device=q.device)
+    check(lib().qp_prompt_attention(kv_type, _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
+                                    _dev(v_cache, "v_cache"), n_past, t, n_head, n_kv_head, head_dim, float(scale),
+                                    _dev(out, "out"), out.stride(0), _stream()))
     return out

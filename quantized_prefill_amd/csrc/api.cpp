@@ -4,6 +4,7 @@
 // batched prefill has no f32 dequant for IQ2_XXS, IQ3_S, IQ3_XXS, Q2_K",
 // sections "Cause" and title: an unsupported type is an InvalidParameter-style
 // error and the engine fails closed).
+#include <cmath>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -244,6 +245,31 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
   return from_hip(qp::launch_grouped_expert(qtype, w_gate, w_up, w_down, n_experts, hidden, inter, x, t, top_k, ids,
                                             weights, out, workspace, ws, stream),
                   "grouped expert launch");
+}
+
+qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                              int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
+                              float scale, float* out, int64_t ldo, hipStream_t stream) {
+  if (kv_type != QP_F16W && kv_type != QP_Q8_0)
+    return fail(QP_ERR_UNSUPPORTED_TYPE, "no prompt attention over a KV cache of ggml type %d", kv_type);
+  if (head_dim != 128) return fail(QP_ERR_INVALID_PARAMETER, "head_dim %lld (only 128)", (long long)head_dim);
+  if (n_head < 1 || n_head > 1024 || n_kv_head < 1 || n_head % n_kv_head != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "n_head=%lld n_kv_head=%lld", (long long)n_head, (long long)n_kv_head);
+  if (t < 0 || n_past < 0 || n_past + t > ((int64_t)1 << 31) - 1 - 256)
+    return fail(QP_ERR_INVALID_PARAMETER, "n_past=%lld t=%lld out of range", (long long)n_past, (long long)t);
+  const int64_t width = n_head * head_dim;
+  if (ldq < width || ldo < width || ldq % 4 != 0 || ldo % 4 != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "ldq=%lld ldo=%lld for %lld columns", (long long)ldq, (long long)ldo,
+                (long long)width);
+  if (!std::isfinite(scale)) return fail(QP_ERR_INVALID_PARAMETER, "scale is not finite");
+  if (t == 0) return ok();
+  if (!q || !k_cache || !v_cache || !out) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  const size_t cache_align = kv_type == QP_F16W ? 16 : 2;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, cache_align) || !aligned(v_cache, cache_align))
+    return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  return from_hip(qp::launch_attention(kv_type, q, ldq, k_cache, v_cache, n_past, t, n_head, n_kv_head, scale, out,
+                                       ldo, stream),
+                  "attention launch");
 }
 
 const char* qp_status_string(qp_status s) {

@@ -1,0 +1,300 @@
+// attention.hip -- causal prompt attention of one prefill chunk over a KV
+// cache held as binary16 or Q8_0 rows ("CUDA prefill VRAM loans and SM75
+// Q4/native-IQ opt-ins", section "Summary" and the KV table after it: prompt
+// attention as a tensor-core path over a quantized KV cache).
+//
+// One workgroup = 128 queries of one query head: 4 waves of 32 queries.  The
+// keys of the head's kv head stream through LDS in blocks of 64, double
+// buffered: K as rows (64 x 128), V transposed (128 x 64), both binary16,
+// decoded from the cache as they are staged.  Per wave and key block:
+//   S^T (64 keys x 32 queries) = K . Q^T    16 v_mfma_f32_32x32x16_f16
+//   online softmax over the keys            one lane owns one query column
+//   O^T (128 x 32) += V^T . P^T             16 v_mfma_f32_32x32x16_f16
+// Forming S transposed puts each query's scores in one lane (16 per 32-key
+// tile, plus the partner lane 32 apart), so the row maximum costs a single
+// cross-lane step, the rescale of O^T is a per-lane multiply, and the
+// probabilities feed the second product as its B operand straight from the
+// accumulator registers (the key order inside a 16-key step is the
+// accumulator's row order; V^T is read in that order).
+//
+// Numerics: Q is rounded to binary16 (nearest even), K and V are the exact
+// cache values rounded to binary16, scores and the softmax are f32
+// (exp2 of scale*log2(e)-scaled scores), P is rounded to binary16 for the
+// second product, O accumulates in f32 and is divided by the f32 row sum.
+#include "qp_device.h"
+#include "qp_internal.h"
+
+namespace qp {
+namespace {
+
+constexpr int kD = 128;              // head dim
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;     // queries per workgroup
+constexpr int kBK = 64;              // keys per staged block
+constexpr int kKP = kD + 8;          // K row pitch in halves: 16-lane reads hit distinct banks
+constexpr int kVP = kBK + 4;         // V^T row pitch in halves: 34 dwords, 32 rows on distinct bank pairs
+constexpr int kStage = kBK * kKP + kD * kVP;  // halves per stage
+
+struct AttnArgs {
+  const float* q;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  float* o;
+  int64_t ldq, ldo;
+  int n_past, t, kv_len;
+  int n_head, n_kv, group;
+  int nqt;     // query tiles of 128
+  int xcd;     // 1: the workgroups of one kv group go to one XCD
+  float c;     // scale * log2(e)
+};
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive cache values of one row (a chunk), raw, then as binary16.
+template <int KV> struct Chunk;
+
+template <> struct Chunk<kF16> {
+  static constexpr int64_t kRowBytes = 2 * kD;
+  u32x4 raw;
+  __device__ __forceinline__ void load(const uint8_t* row, int dc) { raw = *(const u32x4*)(row + 16 * dc); }
+  __device__ __forceinline__ void zero() { raw = (u32x4){0, 0, 0, 0}; }
+  __device__ __forceinline__ u32x4 halves() const { return raw; }
+};
+
+template <> struct Chunk<kQ8_0> {
+  static constexpr int64_t kRowBytes = 34 * (kD / 32);
+  uint32_t d, q0, q1;
+  __device__ __forceinline__ void load(const uint8_t* row, int dc) {
+    const uint16_t* b = (const uint16_t*)(row + 34 * (dc >> 2));  // rows and blocks start on even bytes
+    const uint16_t* qs = b + 1 + 4 * (dc & 3);
+    d = b[0];
+    q0 = (uint32_t)qs[0] | ((uint32_t)qs[1] << 16);
+    q1 = (uint32_t)qs[2] | ((uint32_t)qs[3] << 16);
+  }
+  __device__ __forceinline__ void zero() { d = q0 = q1 = 0; }
+  __device__ __forceinline__ u32x4 halves() const {
+    const float s = f16_to_f32(d);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = s * (float)(int8_t)(q0 >> (8 * e));
+      v[4 + e] = s * (float)(int8_t)(q1 >> (8 * e));
+    }
+    return (u32x4){pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
+  }
+};
+
+template <int KV>
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
+  using C = Chunk<KV>;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, hh = lane >> 5;
+
+  // workgroup -> (query tile, head); the longest tiles first.  With the XCD
+  // map, the group's query heads of one (tile, kv head) unit are dispatched
+  // back to back on one XCD (block b runs on XCD b % 8) and share its L2.
+  int unit, member;
+  const int b = blockIdx.x;
+  if (p.xcd) {
+    const int slot = b >> 3;
+    member = slot % p.group;
+    unit = (slot / p.group) * 8 + (b & 7);
+  } else {
+    unit = b / p.group;
+    member = b % p.group;
+  }
+  const int qt = p.nqt - 1 - unit / p.n_kv;
+  const int g = unit % p.n_kv;
+  const int head = g * p.group + member;
+  const int q0 = qt * kBM;
+  const int q0w = q0 + 32 * wave;
+  const bool wave_live = q0w < p.t;
+
+  // this wave's queries as the B operand of K . Q^T: query r, dims 16c + 8hh ..
+  half8 qf[8];
+  {
+    const int qi = q0w + r;
+    const float* qrow = p.q + (int64_t)qi * p.ldq + (int64_t)head * kD + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float4v a = {0, 0, 0, 0}, bq = {0, 0, 0, 0};
+      if (qi < p.t) {
+        a = *(const float4v*)(qrow + 16 * c);
+        bq = *(const float4v*)(qrow + 16 * c + 4);
+      }
+      const u32x4 h = {pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]), pack_f16x2(bq[0], bq[1]),
+                       pack_f16x2(bq[2], bq[3])};
+      qf[c] = __builtin_bit_cast(half8, h);
+    }
+  }
+
+  const int last_q = (q0 + kBM - 1 < p.t - 1) ? q0 + kBM - 1 : p.t - 1;
+  const int nkb = (p.n_past + last_q) / kBK + 1;
+  const int64_t row_stride = (int64_t)p.n_kv * C::kRowBytes;
+  const uint8_t* kbase = p.kc + (int64_t)g * C::kRowBytes;
+  const uint8_t* vbase = p.vc + (int64_t)g * C::kRowBytes;
+
+  // staging: chunk j of this thread is key (tid + 256 j) >> 4, dims 8 * (tid & 15) ..
+  C kch[4], vch[4];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = kb * kBK + ((tid + 256 * j) >> 4);
+      const int dc = tid & 15;
+      if (key < p.kv_len) {
+        kch[j].load(kbase + key * row_stride, dc);
+        vch[j].load(vbase + key * row_stride, dc);
+      } else {
+        kch[j].zero();
+        vch[j].zero();
+      }
+    }
+  };
+  auto store_block = [&](int buf) {
+    _Float16* ks = lds + buf * kStage;
+    _Float16* vt = ks + kBK * kKP;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = (tid + 256 * j) >> 4;
+      const int dc = tid & 15;
+      *(u32x4*)(ks + key * kKP + 8 * dc) = kch[j].halves();
+      const half8 v = __builtin_bit_cast(half8, vch[j].halves());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(8 * dc + e) * kVP + key] = v[e];
+    }
+  };
+
+  float16v o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) o[dt][a] = 0.0f;
+  float m_run = -1e30f;  // finite: a fully masked block leaves alpha = 1, p = 0
+  float l_part = 0.0f;   // this lane's share of the row sum (its 16 key rows per tile)
+  const int qpos_lo = p.n_past + q0w;
+  const int qpos = qpos_lo + r;
+
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) load_block(kb + 1);
+    const int key0 = kb * kBK;
+    if (wave_live && key0 <= qpos_lo + 31) {
+      const _Float16* ks = lds + (kb & 1) * kStage;
+      const _Float16* vt = ks + kBK * kKP;
+      float16v s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) s[kt][a] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const half8 ka = *(const half8*)(ks + (32 * kt + r) * kKP + 16 * c + 8 * hh);
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[c], s[kt], 0, 0, 0);
+        }
+      }
+      // scale into the log2 domain, mask keys after the query, block maximum
+      const bool diag = key0 + kBK - 1 > qpos_lo;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          float v = s[kt][a] * p.c;
+          if (diag && key0 + 32 * kt + 8 * (a >> 2) + 4 * hh + (a & 3) > qpos) v = -INFINITY;
+          s[kt][a] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) o[dt][a] *= alpha;
+      half8 pb[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + e] - m_new);
+          l_part += pv[e];
+        }
+        const u32x4 h = {pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
+                         pack_f16x2(pv[6], pv[7])};
+        pb[st] = __builtin_bit_cast(half8, h);
+      }
+      // k index 8hh + e of step st is key 16 st + 8 (e >> 2) + 4 hh + (e & 3)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const _Float16* vr = vt + (32 * dt + r) * kVP + 16 * st + 4 * hh;
+          const half4 lo = *(const half4*)vr;
+          const half4 hi = *(const half4*)(vr + 8);
+          const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[st], o[dt], 0, 0, 0);
+        }
+    }
+    if (kb + 1 < nkb) store_block((kb + 1) & 1);
+    __syncthreads();
+  }
+
+  const float l = l_part + __shfl_xor(l_part, 32, 64);
+  const int qi = q0w + r;
+  if (!wave_live || qi >= p.t) return;
+  const float inv = 1.0f / l;
+  float* orow = p.o + (int64_t)qi * p.ldo + (int64_t)head * kD + 4 * hh;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(float4v*)(orow + 32 * dt + 8 * i) = (float4v){o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv,
+                                                       o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv};
+}
+
+}  // namespace
+
+int64_t attention_row_bytes(int kv_type) {
+  switch (kv_type) {
+    case kF16: return Chunk<kF16>::kRowBytes;
+    case kQ8_0: return Chunk<kQ8_0>::kRowBytes;
+    default: return -1;
+  }
+}
+
+hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                            int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv, float scale, float* out,
+                            int64_t ldo, hipStream_t s) {
+  AttnArgs p;
+  p.q = q;
+  p.kc = (const uint8_t*)k_cache;
+  p.vc = (const uint8_t*)v_cache;
+  p.o = out;
+  p.ldq = ldq;
+  p.ldo = ldo;
+  p.n_past = (int)n_past;
+  p.t = (int)t;
+  p.kv_len = (int)(n_past + t);
+  p.n_head = (int)n_head;
+  p.n_kv = (int)n_kv;
+  p.group = (int)(n_head / n_kv);
+  p.nqt = (int)((t + kBM - 1) / kBM);
+  p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  const int64_t blocks = (int64_t)p.nqt * n_head;
+  p.xcd = blocks % (8 * p.group) == 0 ? 1 : 0;
+  if (kv_type == kF16)
+    hipLaunchKernelGGL(attention_kernel<kF16>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  else if (kv_type == kQ8_0)
+    hipLaunchKernelGGL(attention_kernel<kQ8_0>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace qp

@@ -50,6 +50,12 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
                                  int64_t top_k, const int32_t* ids, const float* weights, float* out,
                                  void* workspace, const MoeWorkspace& ws, hipStream_t s);
 
+// Causal prompt attention over a binary16 or Q8_0 KV cache, head_dim 128.
+int64_t attention_row_bytes(int kv_type);
+hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                            int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv, float scale, float* out,
+                            int64_t ldo, hipStream_t s);
+
 // geometry of the GEMM tiles (the MoE layout and the ABI checks use them)
 constexpr int kTileM = 128;
 constexpr int kTileN = 128;

@@ -121,3 +121,34 @@ def test_moe_rejections():
     bad = list(args)
     bad[0] = 3
     assert f(*bad, ws, None) == 2
+
+
+def test_attention_rejections():
+    L = qp.lib()
+    A = L.qp_prompt_attention
+    # kv_type, q, ldq, k, v, n_past, t, n_head, n_kv, head_dim, scale, out, ldo, stream
+    good = [qp.F16W, FAKE, 4096, FAKE, FAKE, 0, 8, 32, 8, 128, 0.088, FAKE, 4096, None]
+
+    def call(**kw):
+        a = list(good)
+        names = ["kv", "q", "ldq", "k", "v", "n_past", "t", "n_head", "n_kv", "hd", "scale", "out", "ldo", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return A(*a)
+
+    assert call(kv=qp.Q4_K) == 2
+    assert b"KV cache" in L.qp_last_error_detail()
+    assert call(hd=64) == 1
+    assert call(n_kv=5) == 1            # 32 heads do not split into 5 groups
+    assert call(n_head=0) == 1
+    assert call(t=-1) == 1
+    assert call(n_past=-3) == 1
+    assert call(n_past=(1 << 31)) == 1
+    assert call(ldq=4095) == 1          # below n_head * head_dim
+    assert call(ldo=4098) == 1          # not a multiple of 4
+    assert call(scale=float("inf")) == 1
+    assert call(t=0, q=None, k=None, v=None, out=None) == 0   # empty chunk: nothing to do
+    assert call(q=None) == 1
+    assert call(q=FAKE + 4) == 1        # q not 16-byte aligned
+    assert call(k=FAKE + 2) == 1        # binary16 cache not 16-byte aligned
+    assert call(out=FAKE + 8) == 1

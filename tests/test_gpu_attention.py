@@ -1,0 +1,104 @@
+"""Prompt attention over a binary16 or Q8_0 KV cache on the GPU against the oracle."""
+import numpy as np
+import pytest
+
+import synth
+import quantized_prefill_amd as qp
+from gpu_helpers import assert_close, sample_tokens, say, to_dev
+from synth import F16W, Q8_0
+
+pytestmark = pytest.mark.gpu
+
+HD = 128
+
+
+def queries(t: int, n_head: int, seed: int, ldq: int | None = None) -> np.ndarray:
+    """Query rows as the q projection leaves them after its head norm: N(0, 1)
+    values (RMS 1 per head), f32, optionally inside wider rows."""
+    q = synth.activations_f32(t, ldq or n_head * HD, seed)
+    return q
+
+
+def run_attention(kvtype, q, kc, vc, n_past, n_head, n_kv, scale=None, ldo=None):
+    import torch
+    qd = to_dev(q)
+    t = q.shape[0]
+    out = None
+    if ldo is not None:
+        out = torch.full((t, ldo), float("nan"), dtype=torch.float32, device="cuda")
+    y = qp.prompt_attention(kvtype, qd, to_dev(kc), to_dev(vc), n_past, n_head, n_kv, HD, scale, out=out)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+CASES = [
+    # t, n_past, n_head, n_kv : one tile, ragged tails, a prefix of earlier chunks, MHA and GQA
+    (1, 0, 4, 4),
+    (37, 0, 8, 2),
+    (128, 0, 4, 1),
+    (300, 0, 8, 2),
+    (200, 77, 8, 4),
+    (129, 1000, 2, 1),
+    (513, 64, 32, 8),
+]
+
+
+@pytest.mark.parametrize("kvtype", [F16W, Q8_0], ids=["F16", "Q8_0"])
+@pytest.mark.parametrize("t,n_past,n_head,n_kv", CASES)
+def test_attention_small(orc, kvtype, t, n_past, n_head, n_kv):
+    seed = 12000 + 7 * t + n_past + n_head
+    q = queries(t, n_head, seed)
+    kc = synth.kv_cache(kvtype, n_past + t, n_kv, HD, seed + 1)
+    vc = synth.kv_cache(kvtype, n_past + t, n_kv, HD, seed + 2)
+    y = run_attention(kvtype, q, kc, vc, n_past, n_head, n_kv)
+    ref = orc.attention(kvtype, q, kc, vc, n_past, n_head, n_kv, HD)
+    assert_close(y, ref, f"attention {synth.NAMES[kvtype]} t={t} past={n_past} heads={n_head}/{n_kv}")
+
+
+def test_attention_strides_scale_and_bounds(orc):
+    """Wider q and out rows, a non-default scale; columns past the heads stay untouched."""
+    t, n_head, n_kv, ldq, ldo = 150, 4, 2, 4 * HD + 64, 4 * HD + 32
+    q = queries(t, n_head, 12500, ldq)
+    kc = synth.kv_cache(Q8_0, t, n_kv, HD, 12501)
+    vc = synth.kv_cache(Q8_0, t, n_kv, HD, 12502)
+    y = run_attention(Q8_0, q, kc, vc, 0, n_head, n_kv, scale=0.05, ldo=ldo)
+    ref = orc.attention(Q8_0, q, kc, vc, 0, n_head, n_kv, HD, scale=0.05)
+    assert_close(y[:, :n_head * HD], ref, "attention strided")
+    assert np.all(np.isnan(y[:, n_head * HD:])), "wrote past the heads"
+
+
+def test_attention_sharp_scores(orc):
+    """A large scale makes the softmax nearly one-hot: the masking and the running
+    maximum decide the result."""
+    t, n_head, n_kv = 256, 4, 4
+    q = queries(t, n_head, 12600)
+    kc = synth.kv_cache(F16W, t, n_kv, HD, 12601)
+    vc = synth.kv_cache(F16W, t, n_kv, HD, 12602)
+    y = run_attention(F16W, q, kc, vc, 0, n_head, n_kv, scale=1.0)
+    ref = orc.attention(F16W, q, kc, vc, 0, n_head, n_kv, HD, scale=1.0)
+    assert_close(y, ref, "attention sharp")
+
+
+def test_attention_deterministic():
+    t, n_head, n_kv = 333, 8, 2
+    q = queries(t, n_head, 12700)
+    kc = synth.kv_cache(Q8_0, t, n_kv, HD, 12701)
+    vc = synth.kv_cache(Q8_0, t, n_kv, HD, 12702)
+    a = run_attention(Q8_0, q, kc, vc, 0, n_head, n_kv)
+    b = run_attention(Q8_0, q, kc, vc, 0, n_head, n_kv)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("kvtype", [F16W, Q8_0], ids=["F16", "Q8_0"])
+def test_attention_qwen3_8b_t2048(orc, kvtype):
+    """Qwen3-8B attention shape (32 query heads, 8 kv heads, head_dim 128) at
+    T = 2048, the launch the bench times; sampled queries against the oracle."""
+    t, n_head, n_kv = 2048, 32, 8
+    q = queries(t, n_head, 12800)
+    kc = synth.kv_cache(kvtype, t, n_kv, HD, 12801)
+    vc = synth.kv_cache(kvtype, t, n_kv, HD, 12802)
+    say(f"attention 8B t=2048 {synth.NAMES[kvtype]}")
+    y = run_attention(kvtype, q, kc, vc, 0, n_head, n_kv)
+    tok = sample_tokens(t, 24, 12803)
+    ref = orc.attention(kvtype, q, kc, vc, 0, n_head, n_kv, HD, tokens=tok)
+    assert_close(y[tok], ref, f"attention 8B {synth.NAMES[kvtype]}")
