@@ -11,7 +11,8 @@ sum of the projection launches' HIP-event durations); the dequant GB/s is
 reported beside it.  After the timed region the remaining workloads -- the
 Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the Q5_K
 Qwen3-8B layer at T = 2048 (projections one by one), the fused
-QK-norm projections at T = 8192 and the routed 128-expert FFN -- are timed
+QK-norm projections at T = 8192, the routed 128-expert FFN and causal prompt
+attention with Qwen3-8B heads over a binary16 or Q8_0 KV cache -- are timed
 and reported under "rows".
 """
 from __future__ import annotations
@@ -286,6 +287,32 @@ def other_rows(torch, synth, qp, iters):
     ms = time_fn(torch, moe, iters)
     flops = 2.0 * t * k * 3 * hidden * inter
     rows["moe_e128_top8_t4096"] = dict(tflops=flops / ms / 1e9, us=ms * 1e3)
+    del wg, wu, wd, x, lg, ids, wts, out, ws
+    rows.update(attention_rows(torch, synth, qp, iters))
+    return rows
+
+
+def attention_flops(t: int, n_past: int, n_head: int, head_dim: int) -> float:
+    """Algorithmic flops of causal prompt attention: query i sees n_past + i + 1
+    keys, each costing a head_dim dot product and a head_dim multiply-add of V."""
+    keys = t * n_past + t * (t + 1) / 2
+    return 4.0 * head_dim * n_head * keys
+
+
+def attention_rows(torch, synth, qp, iters):
+    """Causal prompt attention, Qwen3-8B heads (32 query, 8 kv, head_dim 128),
+    over a binary16 or Q8_0 KV cache."""
+    dev = torch.device("cuda")
+    rows = {}
+    for kvtype, t in ((synth.F16W, 2048), (synth.Q8_0, 2048), (synth.Q8_0, 8192)):
+        q = torch.from_numpy(synth.activations_f32(t, 32 * 128, synth.seed_for(5, t))).to(dev)
+        kc = torch.from_numpy(synth.kv_cache(kvtype, t, 8, 128, synth.seed_for(5, t + 1))).to(dev)
+        vc = torch.from_numpy(synth.kv_cache(kvtype, t, 8, 128, synth.seed_for(5, t + 2))).to(dev)
+        out = torch.empty((t, 32 * 128), device=dev)
+        ms = time_fn(torch, lambda: qp.prompt_attention(kvtype, q, kc, vc, 0, 32, 8, 128, out=out), iters)
+        name = f"attention_{synth.NAMES[kvtype].lower()}_kv_qwen3_8b_t{t}"
+        rows[name] = dict(tflops=attention_flops(t, 0, 32, 128) / ms / 1e9, us=ms * 1e3)
+        del q, kc, vc, out
     return rows
 
 

@@ -85,7 +85,7 @@ template <> struct Chunk<kQ8_0> {
 };
 
 template <int KV>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnArgs p) {
   using C = Chunk<KV>;
   __shared__ __attribute__((aligned(16))) _Float16 lds[2 * kStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -135,33 +135,41 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
   const uint8_t* kbase = p.kc + (int64_t)g * C::kRowBytes;
   const uint8_t* vbase = p.vc + (int64_t)g * C::kRowBytes;
 
-  // staging: chunk j of this thread is key (tid + 256 j) >> 4, dims 8 * (tid & 15) ..
+  // staging.  K chunk j of this thread: key (tid + 256 j) >> 4, dims
+  // 8 * (tid & 15) ..  (16 lanes read one row).  V chunk j: key
+  // 2 * (tid & 31) + (j & 1), dims 8 * ((tid >> 5) + 8 * (j >> 1)) .. : the
+  // two keys of a pair go to V^T as one 32-bit word per dim.
   C kch[4], vch[4];
   auto load_block = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = kb * kBK + ((tid + 256 * j) >> 4);
-      const int dc = tid & 15;
-      if (key < p.kv_len) {
-        kch[j].load(kbase + key * row_stride, dc);
-        vch[j].load(vbase + key * row_stride, dc);
-      } else {
+      if (key < p.kv_len)
+        kch[j].load(kbase + key * row_stride, tid & 15);
+      else
         kch[j].zero();
+      const int vkey = kb * kBK + 2 * (tid & 31) + (j & 1);
+      if (vkey < p.kv_len)
+        vch[j].load(vbase + vkey * row_stride, (tid >> 5) + 8 * (j >> 1));
+      else
         vch[j].zero();
-      }
     }
   };
   auto store_block = [&](int buf) {
     _Float16* ks = lds + buf * kStage;
     _Float16* vt = ks + kBK * kKP;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = (tid + 256 * j) >> 4;
-      const int dc = tid & 15;
-      *(u32x4*)(ks + key * kKP + 8 * dc) = kch[j].halves();
-      const half8 v = __builtin_bit_cast(half8, vch[j].halves());
+    for (int j = 0; j < 4; ++j) *(u32x4*)(ks + ((tid + 256 * j) >> 4) * kKP + 8 * (tid & 15)) = kch[j].halves();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(8 * dc + e) * kVP + key] = v[e];
+    for (int pr = 0; pr < 2; ++pr) {
+      const u32x4 a = vch[2 * pr].halves(), b = vch[2 * pr + 1].halves();
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+      uint32_t* col = (uint32_t*)(vt + 8 * ((tid >> 5) + 8 * pr) * kVP + 2 * (tid & 31));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        col[(2 * e) * (kVP / 2)] = (av[e] & 0xFFFFu) | (bv[e] << 16);
+        col[(2 * e + 1) * (kVP / 2)] = (av[e] >> 16) | (bv[e] & 0xFFFF0000u);
+      }
     }
   };
 
@@ -210,12 +218,14 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
       l_part *= alpha;
+      if (__any(m_new != m_run)) {  // the maximum moved for some query of the wave
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) o[dt][a] *= alpha;
+          for (int a = 0; a < 16; ++a) o[dt][a] *= alpha;
+      }
+      m_run = m_new;
       half8 pb[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
