@@ -46,6 +46,7 @@
 #endif
 
 #define OR_F16 1
+#define OR_Q4_0 2
 #define OR_Q8_0 8
 #define OR_Q2_K 10
 #define OR_Q4_K 12
@@ -83,7 +84,9 @@
 #define PLANT_ATTN_NO_MASK     27  /* queries also attend to later keys */
 #define PLANT_ATTN_GQA         28  /* q head h reads kv head h % n_kv instead of h / group */
 #define PLANT_ATTN_NO_SCALE    29  /* scores not multiplied by the scale */
-#define PLANT_COUNT            30
+#define PLANT_Q4_0_HALVES      30  /* Q4_0: values 0..15 from high nibbles, 16..31 from low */
+#define PLANT_Q4_0_OFFSET      31  /* Q4_0 quant without the -8 */
+#define PLANT_COUNT            32
 
 static const char* const plant_names[PLANT_COUNT] = {
     "none", "q8_unsigned", "q6_no_offset", "q6_no_high", "q4_scale_high",
@@ -91,7 +94,7 @@ static const char* const plant_names[PLANT_COUNT] = {
     "q2_nibbles", "q4_nibble", "q6_shift", "gemm_transpose", "gemm_drop_k",
     "qkn_sum", "qkn_eps", "qkn_gain", "silu_sign", "moe_weight", "router_tie",
     "router_renorm", "moe_up", "q5_no_high", "q5_high_bit", "f16w_bytes",
-    "attn_no_mask", "attn_gqa", "attn_no_scale"};
+    "attn_no_mask", "attn_gqa", "attn_no_scale", "q4_0_halves", "q4_0_offset"};
 
 int or_plant(void) { return QP_PLANT; }
 int or_plant_count(void) { return PLANT_COUNT; }
@@ -173,7 +176,7 @@ void or_float_to_half_array(const float* src, uint16_t* dst, int64_t n) {
 int64_t or_block_size(int qtype) {
   switch (qtype) {
     case OR_F16: return 1;
-    case OR_Q8_0: return 32;
+    case OR_Q8_0: case OR_Q4_0: return 32;
     case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: case OR_Q2_K: return 256;
     default: return -1;
   }
@@ -183,6 +186,7 @@ int64_t or_type_size(int qtype) {
   switch (qtype) {
     case OR_F16: return 2;
     case OR_Q8_0: return 34;
+    case OR_Q4_0: return 18;
     case OR_Q4_K: return 144;
     case OR_Q5_K: return 176;
     case OR_Q6_K: return 210;
@@ -235,6 +239,24 @@ static float q8_0_value(const uint8_t* b, int i) {
   d = 1.0f;
 #endif
   return d * q;
+}
+
+/* Q4_0 (18 bytes: binary16 d, then 16 bytes of 4-bit quants): value i is
+ * d * (q - 8), where q is the low nibble of byte 2 + i for i < 16 and the
+ * high nibble of byte 2 + i - 16 for i >= 16.  The pages name Q4_0 as a KV
+ * cache format; the layout is the GGUF one. */
+static float q4_0_value(const uint8_t* b, int i) {
+  float d = f16_at(b);
+#if QP_PLANT == PLANT_Q4_0_HALVES
+  int q = i < 16 ? (b[2 + i] >> 4) : (b[2 + i - 16] & 0x0F);
+#else
+  int q = i < 16 ? (b[2 + i] & 0x0F) : (b[2 + i - 16] >> 4);
+#endif
+#if QP_PLANT == PLANT_Q4_0_OFFSET
+  return d * (float)q;
+#else
+  return d * (float)(q - 8);
+#endif
 }
 
 /* Q4_K 6-bit (scale, min) of sub-block j from the 12 packed bytes s[0..11]:
@@ -402,6 +424,7 @@ static float block_value(int qtype, const uint8_t* b, int i) {
   switch (qtype) {
     case OR_F16: return f16w_value(b);
     case OR_Q8_0: return q8_0_value(b, i);
+    case OR_Q4_0: return q4_0_value(b, i);
     case OR_Q4_K: return q4_k_value(b, i);
     case OR_Q5_K: return q5_k_value(b, i);
     case OR_Q6_K: return q6_k_value(b, i);

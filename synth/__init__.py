@@ -48,8 +48,9 @@ MASK64 = (1 << 64) - 1
 
 # ggml type ids
 F16W, Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 1, 8, 10, 12, 13, 14
-BLOCK = {F16W: (1, 2), Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84)}
-NAMES = {F16W: "F16", Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K", Q2_K: "Q2_K"}
+Q4_0 = 2  # a KV cache format here, not a weight type
+BLOCK = {F16W: (1, 2), Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84)}
+NAMES = {F16W: "F16", Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K", Q2_K: "Q2_K"}
 BY_NAME = {v: k for k, v in NAMES.items()}
 
 BASE_SEED = 0x9E3779B9
@@ -144,6 +145,8 @@ def quant_weights(qtype: int, rows: int, cols: int, seed: int,
         q = np.floor(uniform(substream(seed, 2), nb * 32) * 255.0).astype(np.int64) - 127
         blocks[:, 2:34] = q.astype(np.int8).view(np.uint8).reshape(nb, 32)
         _put_f16(blocks, 0, d)
+    elif qtype == Q4_0:
+        _put_f16(blocks, 0, d)
     elif qtype in (Q4_K, Q5_K):
         dmin = f16_bits(uniform_range(substream(seed, 3), nb, scale_lo, scale_hi))
         _put_f16(blocks, 0, d)
@@ -178,12 +181,15 @@ def router_logits(tokens: int, experts: int, seed: int) -> np.ndarray:
 
 def kv_cache(kvtype: int, tokens: int, n_kv: int, head_dim: int, seed: int) -> np.ndarray:
     """A KV cache of tokens x n_kv rows of head_dim values, flat uint8:
-    binary16 N(0, 1) draws, or Q8_0 blocks with scales in [1/64, 1/32] and
-    quants uniform in [-127, 127] (values within about +-4)."""
+    binary16 N(0, 1) draws; Q8_0 blocks with scales in [1/64, 1/32] and
+    quants uniform in [-127, 127] (values within about +-4); or Q4_0 blocks
+    with scales in [1/4, 1/2] and uniform 4-bit quants (values within +-4)."""
     if kvtype == F16W:
         return f16_bits(normal(seed, tokens * n_kv * head_dim)).view(np.uint8).reshape(-1)
     if kvtype == Q8_0:
         return quant_weights(Q8_0, tokens * n_kv, head_dim, seed, 1.0 / 64, 1.0 / 32)
+    if kvtype == Q4_0:
+        return quant_weights(Q4_0, tokens * n_kv, head_dim, seed, 0.25, 0.5)
     raise ValueError(f"no KV cache recipe for type {kvtype}")
 
 

@@ -23,7 +23,7 @@ import os
 import numpy as np
 
 import synth
-from synth import F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
+from synth import F16W, Q4_0, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "hand_blocks.json")
@@ -54,6 +54,16 @@ def enc_q8_0(d_bits: int, q: np.ndarray) -> np.ndarray:
     b = np.zeros(34, np.uint8)
     _put16(b, 0, d_bits)
     b[2:] = np.asarray(q, dtype=np.int64).astype(np.int8).view(np.uint8)
+    return b
+
+
+def enc_q4_0(d_bits: int, q: np.ndarray) -> np.ndarray:
+    """Q4_0 block from 32 quants in [0, 15]: quant j < 16 is the low nibble of
+    byte 2 + j, quant j >= 16 the high nibble of byte 2 + j - 16."""
+    q = np.asarray(q, dtype=np.int64)
+    b = np.zeros(18, np.uint8)
+    _put16(b, 0, d_bits)
+    b[2:] = (q[:16] | (q[16:] << 4)).astype(np.uint8)
     return b
 
 
@@ -173,6 +183,22 @@ def pin_sweep_q8_0(o):
         got = o.dequant_f32(Q8_0, raw, 1, 256)[0]
         want = _closed_form_f32(d_bits, None, np.ones(256), q, None)
         assert np.array_equal(f32_bits(got), f32_bits(want)), f"Q8_0 sweep d={d_bits:#06x}"
+
+
+def pin_sweep_q4_0(o):
+    """Every quant 0..15 at every position (a cyclic shift per block, so a
+    position's low and high nibble partners differ), for several scales:
+    value = d * (q - 8), exact in binary32."""
+    ds = [0x3400, 0x2E66, 0x0001, 0x8400, 0x7BFF, 0x0000, 0x8000, 0x3C00]
+    blocks, want = [], []
+    for d in ds:
+        for shift in range(16):
+            q = (np.arange(32) * 5 + shift + (np.arange(32) >= 16) * 3) % 16
+            blocks.append(enc_q4_0(d, q))
+            want.append(h16_value(d) * (q - 8.0))
+    raw = np.concatenate(blocks)
+    got = o.dequant_f32(Q4_0, raw, len(blocks), 32)
+    assert np.array_equal(f32_bits(got), f32_bits(np.array(want, dtype=np.float64))), "Q4_0 sweep"
 
 
 def pin_sweep_q4_k(o):
@@ -561,6 +587,14 @@ def pin_attention_zero_query_prefix_mean(o):
     for i in range(t):
         want = 0.25 * qv[:n_past + i + 1].mean(axis=0)
         assert np.allclose(out[i], want, rtol=0, atol=1e-12), f"Q8_0 prefix mean q{i}"
+    # and through a Q4_0 cache: values d * (q - 8) with d = 1/2
+    q4 = rng.integers(0, 16, size=(kv, 32))
+    kc4 = np.concatenate([enc_q4_0(h16(0.5), row) for row in rng.integers(0, 16, size=(kv, 32))])
+    vc4 = np.concatenate([enc_q4_0(h16(0.5), row) for row in q4])
+    out = o.attention(Q4_0, q[:, :32], kc4, vc4, n_past, 1, 1, 32)
+    for i in range(t):
+        want = 0.5 * (q4[:n_past + i + 1] - 8.0).mean(axis=0)
+        assert np.allclose(out[i], want, rtol=0, atol=1e-12), f"Q4_0 prefix mean q{i}"
 
 
 def pin_attention_gqa_constant_values(o):

@@ -54,7 +54,8 @@ def test_float_to_half_exhaustive(orc):
 
 
 def test_geometry(orc):
-    assert [orc.block_size(t) for t in (1, 8, 12, 13, 14, 10)] == [1, 32, 256, 256, 256, 256]
-    assert [orc.type_size(t) for t in (1, 8, 12, 13, 14, 10)] == [2, 34, 144, 176, 210, 84]
+    assert [orc.block_size(t) for t in (1, 2, 8, 12, 13, 14, 10)] == [1, 32, 32, 256, 256, 256, 256]
+    assert [orc.type_size(t) for t in (1, 2, 8, 12, 13, 14, 10)] == [2, 18, 34, 144, 176, 210, 84]
     assert orc.row_bytes(14, 4173) == 17 * 210
-    assert orc.block_size(2) == -1
+    assert orc.row_bytes(2, 128) == 4 * 18
+    assert orc.block_size(3) == -1
