@@ -12,7 +12,7 @@ reported beside it.  After the timed region the remaining workloads -- the
 Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the Q5_K
 Qwen3-8B layer at T = 2048 (projections one by one), the fused
 QK-norm projections at T = 8192, the routed 128-expert FFN and causal prompt
-attention with Qwen3-8B heads over a binary16 or Q8_0 KV cache -- are timed
+attention with Qwen3-8B heads over a binary16, Q8_0 or Q4_0 KV cache -- are timed
 and reported under "rows".
 """
 from __future__ import annotations
@@ -301,10 +301,11 @@ def attention_flops(t: int, n_past: int, n_head: int, head_dim: int) -> float:
 
 def attention_rows(torch, synth, qp, iters):
     """Causal prompt attention, Qwen3-8B heads (32 query, 8 kv, head_dim 128),
-    over a binary16 or Q8_0 KV cache."""
+    over a binary16, Q8_0 or Q4_0 KV cache."""
     dev = torch.device("cuda")
     rows = {}
-    for kvtype, t in ((synth.F16W, 2048), (synth.Q8_0, 2048), (synth.Q8_0, 8192)):
+    for kvtype, t in ((synth.F16W, 2048), (synth.Q8_0, 2048), (synth.Q4_0, 2048), (synth.Q8_0, 8192),
+                      (synth.Q4_0, 8192)):
         q = torch.from_numpy(synth.activations_f32(t, 32 * 128, synth.seed_for(5, t))).to(dev)
         kc = torch.from_numpy(synth.kv_cache(kvtype, t, 8, 128, synth.seed_for(5, t + 1))).to(dev)
         vc = torch.from_numpy(synth.kv_cache(kvtype, t, 8, 128, synth.seed_for(5, t + 2))).to(dev)

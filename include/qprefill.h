@@ -69,7 +69,7 @@ typedef enum {
   QP_ERR_DEVICE = 4               /* the HIP runtime reported an error at launch */
 } qp_status;
 
-typedef enum { QP_F16W = 1, QP_Q8_0 = 8, QP_Q2_K = 10, QP_Q4_K = 12, QP_Q5_K = 13, QP_Q6_K = 14 } qp_qtype;
+typedef enum { QP_F16W = 1, QP_Q4_0 = 2, QP_Q8_0 = 8, QP_Q2_K = 10, QP_Q4_K = 12, QP_Q5_K = 13, QP_Q6_K = 14 } qp_qtype;
 
 typedef enum { QP_F32 = 0, QP_F16 = 1 } qp_dtype;
 
@@ -254,15 +254,19 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
 
 /*
  * Causal prompt attention of one prefill chunk over a KV cache held as
- * binary16 or Q8_0 rows ("CUDA prefill VRAM loans and SM75 Q4/native-IQ
+ * binary16, Q8_0 or Q4_0 rows ("CUDA prefill VRAM loans and SM75 Q4/native-IQ
  * opt-ins", section "Summary" and the KV table after it: prompt attention as
  * a tensor-core path over a quantized KV cache).  The cache holds
  * kv_len = n_past + t tokens (earlier chunks, then this one); query i of the
  * chunk sits at position n_past + i and sees keys 0 .. n_past + i.  Query
  * head h reads kv head h / (n_head / n_kv_head).  For query i, head h:
  *   s_r = scale * (q[i, h] . k[r, g]),  p = softmax_r(s),  out[i, h] = sum_r p_r v[r, g]
- *   kv_type: QP_F16W (binary16 values) or QP_Q8_0 (one 34-byte block per 32
- *            values: "INT8" cache rows).
+ *   kv_type: QP_F16W (binary16 values), QP_Q8_0 (one 34-byte block per 32
+ *            values: "INT8" cache rows) or QP_Q4_0 (one 18-byte block per 32
+ *            values: binary16 d, then 16 bytes whose low nibbles are values
+ *            0..15 and high nibbles values 16..31, each d * (nibble - 8)).
+ *            QP_Q4_0 is a KV cache format only: the weight entry points
+ *            reject it.
  *   q (device): t rows of f32, row stride ldq floats; head h is columns
  *               h*head_dim .. (h+1)*head_dim-1 (the layout of the q
  *               projection's output).
@@ -274,7 +278,7 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
  * and accumulation are f32.  Requires head_dim == 128, n_head a multiple of
  * n_kv_head, n_head <= 1024, n_past + t < 2^31, ldq and ldo >= n_head*head_dim
  * and multiples of 4, q and out 16-byte aligned, caches 16-byte (F16) or
- * 2-byte (Q8_0) aligned, a finite scale.  t == 0 is a no-op.  out must not
+ * 2-byte (Q8_0, Q4_0) aligned, a finite scale.  t == 0 is a no-op.  out must not
  * overlap q or the caches.  Errors: QP_ERR_UNSUPPORTED_TYPE for another
  * kv_type, QP_ERR_INVALID_PARAMETER otherwise.
  */

@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqprefill.so")
 
 F16W, Q8_0, Q2_K, Q4_K, Q5_K, Q6_K = 1, 8, 10, 12, 13, 14
+Q4_0 = 2  # KV cache format of prompt_attention only
 F32, F16 = 0, 1
 
 STATUS = {0: "QP_OK", 1: "QP_ERR_INVALID_PARAMETER", 2: "QP_ERR_UNSUPPORTED_TYPE",
@@ -258,7 +259,7 @@ def grouped_expert_gemm(qtype: int, w_gate, w_up, w_down, n_experts: int, hidden
 def prompt_attention(kv_type: int, q, k_cache, v_cache, n_past: int, n_head: int, n_kv_head: int,
                      head_dim: int = 128, scale: float | None = None, out=None):
     """Causal prompt attention of a chunk of q.shape[0] queries over a KV cache of
-    n_past + q.shape[0] tokens (flat byte tensors of binary16 or Q8_0 rows)."""
+    n_past + q.shape[0] tokens (flat byte tensors of binary16, Q8_0 or Q4_0 rows)."""
     torch = _torch()
     t = q.shape[0]
     if scale is None:

@@ -250,7 +250,7 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
 qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
                               int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
                               float scale, float* out, int64_t ldo, hipStream_t stream) {
-  if (kv_type != QP_F16W && kv_type != QP_Q8_0)
+  if (kv_type != QP_F16W && kv_type != QP_Q8_0 && kv_type != QP_Q4_0)
     return fail(QP_ERR_UNSUPPORTED_TYPE, "no prompt attention over a KV cache of ggml type %d", kv_type);
   if (head_dim != 128) return fail(QP_ERR_INVALID_PARAMETER, "head_dim %lld (only 128)", (long long)head_dim);
   if (n_head < 1 || n_head > 1024 || n_kv_head < 1 || n_head % n_kv_head != 0)

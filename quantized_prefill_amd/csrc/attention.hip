@@ -1,5 +1,5 @@
 // attention.hip -- causal prompt attention of one prefill chunk over a KV
-// cache held as binary16 or Q8_0 rows ("CUDA prefill VRAM loans and SM75
+// cache held as binary16, Q8_0 or Q4_0 rows ("CUDA prefill VRAM loans and SM75
 // Q4/native-IQ opt-ins", section "Summary" and the KV table after it: prompt
 // attention as a tensor-core path over a quantized KV cache).
 //
@@ -27,6 +27,7 @@
 namespace qp {
 namespace {
 
+constexpr int kQ4_0 = 2;             // ggml type id; a KV cache format here, not a weight type
 constexpr int kD = 128;              // head dim
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;     // queries per workgroup
@@ -79,6 +80,35 @@ template <> struct Chunk<kQ8_0> {
     for (int e = 0; e < 4; ++e) {
       v[e] = s * (float)(int8_t)(q0 >> (8 * e));
       v[4 + e] = s * (float)(int8_t)(q1 >> (8 * e));
+    }
+    return (u32x4){pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
+  }
+};
+
+// Q4_0: 18-byte blocks (binary16 d, 16 bytes of nibbles); value j of a block
+// is d * (q - 8) with q the low nibble of byte j (j < 16) or the high nibble
+// of byte j - 16.  Chunk dc holds values 8 (dc & 3) .. of block dc >> 2: the
+// low nibbles of bytes 8 (dc & 1) .. for dc & 3 < 2, else their high nibbles.
+template <> struct Chunk<kQ4_0> {
+  static constexpr int64_t kRowBytes = 18 * (kD / 32);
+  uint32_t d, q0, q1, hi;
+  __device__ __forceinline__ void load(const uint8_t* row, int dc) {
+    const uint16_t* b = (const uint16_t*)(row + 18 * (dc >> 2));  // rows and blocks start on even bytes
+    const uint16_t* qs = b + 1 + 4 * (dc & 1);
+    d = b[0];
+    q0 = (uint32_t)qs[0] | ((uint32_t)qs[1] << 16);
+    q1 = (uint32_t)qs[2] | ((uint32_t)qs[3] << 16);
+    hi = (dc & 2) ? 4u : 0u;
+  }
+  __device__ __forceinline__ void zero() { d = q0 = q1 = hi = 0; }
+  __device__ __forceinline__ u32x4 halves() const {
+    const float s = f16_to_f32(d);
+    const uint32_t n0 = (q0 >> hi) & 0x0F0F0F0Fu, n1 = (q1 >> hi) & 0x0F0F0F0Fu;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = s * (float)((int)((n0 >> (8 * e)) & 0xFu) - 8);
+      v[4 + e] = s * (float)((int)((n1 >> (8 * e)) & 0xFu) - 8);
     }
     return (u32x4){pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
   }
@@ -274,6 +304,7 @@ int64_t attention_row_bytes(int kv_type) {
   switch (kv_type) {
     case kF16: return Chunk<kF16>::kRowBytes;
     case kQ8_0: return Chunk<kQ8_0>::kRowBytes;
+    case kQ4_0: return Chunk<kQ4_0>::kRowBytes;
     default: return -1;
   }
 }
@@ -302,6 +333,8 @@ hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void
     hipLaunchKernelGGL(attention_kernel<kF16>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
   else if (kv_type == kQ8_0)
     hipLaunchKernelGGL(attention_kernel<kQ8_0>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  else if (kv_type == kQ4_0)
+    hipLaunchKernelGGL(attention_kernel<kQ4_0>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

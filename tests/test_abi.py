@@ -51,7 +51,7 @@ def test_status_strings():
 
 def test_dequant_rejections():
     L = qp.lib()
-    assert L.qp_dequant_f32(2, FAKE, 4, 256, FAKE, None) == 2          # IQ4_NL-style id: unsupported
+    assert L.qp_dequant_f32(2, FAKE, 4, 256, FAKE, None) == 2          # Q4_0: a KV cache format only
     assert b"no dequant kernel" in L.qp_last_error_detail()
     assert L.qp_dequant_f32(qp.Q4_K, FAKE, -1, 256, FAKE, None) == 1
     assert L.qp_dequant_f32(qp.Q4_K, FAKE, 4, 0, FAKE, None) == 1
@@ -151,4 +151,5 @@ def test_attention_rejections():
     assert call(q=None) == 1
     assert call(q=FAKE + 4) == 1        # q not 16-byte aligned
     assert call(k=FAKE + 2) == 1        # binary16 cache not 16-byte aligned
+    assert call(kv=qp.Q4_0, k=FAKE + 1) == 1   # Q4_0 cache on an odd byte
     assert call(out=FAKE + 8) == 1

@@ -1,11 +1,11 @@
-"""Prompt attention over a binary16 or Q8_0 KV cache on the GPU against the oracle."""
+"""Prompt attention over a binary16, Q8_0 or Q4_0 KV cache on the GPU against the oracle."""
 import numpy as np
 import pytest
 
 import synth
 import quantized_prefill_amd as qp
 from gpu_helpers import assert_close, sample_tokens, say, to_dev
-from synth import F16W, Q8_0
+from synth import F16W, Q4_0, Q8_0
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("kvtype", [F16W, Q8_0], ids=["F16", "Q8_0"])
+@pytest.mark.parametrize("kvtype", [F16W, Q8_0, Q4_0], ids=["F16", "Q8_0", "Q4_0"])
 @pytest.mark.parametrize("t,n_past,n_head,n_kv", CASES)
 def test_attention_small(orc, kvtype, t, n_past, n_head, n_kv):
     seed = 12000 + 7 * t + n_past + n_head
@@ -89,7 +89,7 @@ def test_attention_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("kvtype", [F16W, Q8_0], ids=["F16", "Q8_0"])
+@pytest.mark.parametrize("kvtype", [F16W, Q8_0, Q4_0], ids=["F16", "Q8_0", "Q4_0"])
 def test_attention_qwen3_8b_t2048(orc, kvtype):
     """Qwen3-8B attention shape (32 query heads, 8 kv heads, head_dim 128) at
     T = 2048, the launch the bench times; sampled queries against the oracle."""
