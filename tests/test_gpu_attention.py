@@ -40,6 +40,8 @@ CASES = [
     (200, 77, 8, 4),
     (129, 1000, 2, 1),
     (513, 64, 32, 8),
+    (1, 4095, 32, 8),     # one query after a long prefix: 64 key blocks, one tile
+    (64, 8000, 8, 8),     # a short chunk at the end of a long context
 ]
 
 
