@@ -276,9 +276,11 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
  * Arithmetic: Q, K, V and the probabilities enter FP16 MFMA products
  * (nearest-even binary16 of the f32 / exact cache values); scores, softmax
  * and accumulation are f32.  Requires head_dim == 128, n_head a multiple of
- * n_kv_head, n_head <= 1024, n_past + t < 2^31, ldq and ldo >= n_head*head_dim
+ * n_kv_head, n_head <= 1024, n_past + t < 2^31, ceil(t/128) * n_head < 2^24
+ * (one workgroup per 128 queries and head), ldq and ldo >= n_head*head_dim
  * and multiples of 4, q and out 16-byte aligned, caches 16-byte (F16) or
- * 2-byte (Q8_0, Q4_0) aligned, a finite scale.  t == 0 is a no-op.  out must not
+ * 2-byte (Q8_0, Q4_0) aligned, a finite scale (scale * |q . k| must stay
+ * within f32 range).  t == 0 is a no-op.  out must not
  * overlap q or the caches.  Errors: QP_ERR_UNSUPPORTED_TYPE for another
  * kv_type, QP_ERR_INVALID_PARAMETER otherwise.
  */

@@ -257,6 +257,8 @@ qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const vo
     return fail(QP_ERR_INVALID_PARAMETER, "n_head=%lld n_kv_head=%lld", (long long)n_head, (long long)n_kv_head);
   if (t < 0 || n_past < 0 || n_past + t > ((int64_t)1 << 31) - 1 - 256)
     return fail(QP_ERR_INVALID_PARAMETER, "n_past=%lld t=%lld out of range", (long long)n_past, (long long)t);
+  if (((t + 127) / 128) * n_head > ((int64_t)1 << 24) - 1)  // 256-thread workgroups: under 2^32 threads
+    return fail(QP_ERR_INVALID_PARAMETER, "t=%lld with %lld heads: grid too large", (long long)t, (long long)n_head);
   const int64_t width = n_head * head_dim;
   if (ldq < width || ldo < width || ldq % 4 != 0 || ldo % 4 != 0)
     return fail(QP_ERR_INVALID_PARAMETER, "ldq=%lld ldo=%lld for %lld columns", (long long)ldq, (long long)ldo,

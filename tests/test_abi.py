@@ -144,6 +144,8 @@ def test_attention_rejections():
     assert call(t=-1) == 1
     assert call(n_past=-3) == 1
     assert call(n_past=(1 << 31)) == 1
+    assert call(t=(1 << 30), n_head=1024, n_kv=8, ldq=1 << 17, ldo=1 << 17) == 1   # grid beyond 2^32 threads
+    assert b"grid too large" in L.qp_last_error_detail()
     assert call(ldq=4095) == 1          # below n_head * head_dim
     assert call(ldo=4098) == 1          # not a multiple of 4
     assert call(scale=float("inf")) == 1
