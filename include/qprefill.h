@@ -24,7 +24,8 @@
  *   - Pointers marked (device) are device memory of the current HIP device;
  *     (host) are host memory.  The caller owns every buffer.  The library
  *     never allocates, frees or synchronizes; the caller-supplied workspace
- *     is the only scratch memory.
+ *     is the only scratch memory, except for qp_prefill_gemm_noalloc, whose
+ *     partial sums go to a fixed static device array of the library.
  *   - Work is enqueued on `stream` (NULL = the null stream) and is
  *     asynchronous: a QP_OK return means "validated and launched".
  *   - Arguments are validated before anything is launched.  On any error
@@ -153,6 +154,27 @@ qp_status qp_prefill_gemm_ws(int qtype, const void* w, int64_t n, int64_t k, con
  * current device (parts * t * n floats, rounded up to 256); 0 when it would
  * not split, or for sizes out of range. */
 size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t);
+
+/*
+ * qp_prefill_gemm_ws for callers that cannot allocate (code under HIP graph
+ * capture, serving loops without an allocator, harnesses that forbid
+ * hipMalloc): the same split and the same kernels, with the partial sums in a
+ * static device array of QP_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  The caller passes inputs and
+ * outputs only; the call allocates and frees nothing.  Results are bit for
+ * bit those of qp_prefill_gemm_ws with a workspace.
+ * On a GPU of up to 256 compute units every split fits the scratch; a split
+ * that would need more (qp_prefill_gemm_workspace_bytes above
+ * QP_NOALLOC_SCRATCH_BYTES) is rejected with QP_ERR_WORKSPACE_TOO_SMALL.
+ * The first call on a device looks up that device's copy of the array.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents (every partial sum is written before it is read, so nothing needs
+ * clearing): calls that overlap on one GPU, on any streams, race.
+ * Errors: those of qp_prefill_gemm_ws.
+ */
+#define QP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+qp_status qp_prefill_gemm_noalloc(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype,
+                                  int64_t t, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 
 /*
  * Prefill projection with the per-head RMSNorm of QK-norm models fused into

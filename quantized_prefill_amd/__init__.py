@@ -30,6 +30,7 @@ SIGNATURES = {
     "qp_prefill_gemm": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP]),
     "qp_prefill_gemm_ws": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP, _SZ, _VP]),
     "qp_prefill_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "qp_prefill_gemm_noalloc": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP]),
     "qp_prefill_gemm_qknorm": (_INT, [_INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64, _F32C, _VP, _I64,
                                       _VP]),
     "qp_prefill_gemm_qkv": (_INT, [_INT, _VP, _I64, _VP, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64,
@@ -161,6 +162,30 @@ def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None, workspace=None):
     check(lib().qp_prefill_gemm_ws(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0), out.data_ptr(),
                                    out.stride(0), _dev(ws, "workspace") if ws is not None else None,
                                    ws.numel() if ws is not None else 0, _stream()))
+    return out
+
+
+# bytes of the library's static scratch behind prefill_gemm_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def prefill_gemm_noalloc(qtype: int, w, n: int, k: int, x, out):
+    """y = x . W^T through qp_prefill_gemm_noalloc: the K split of prefill_gemm
+    with its partial sums in the library's static device scratch, so the call
+    allocates nothing (out must be given).  Calls on one GPU share that
+    scratch and must not overlap."""
+    torch = _torch()
+    if x.dtype == torch.float16:
+        xd = F16
+    elif x.dtype == torch.float32:
+        xd = F32
+    else:
+        raise TypeError("x must be float16 or float32")
+    if not x.is_cuda or x.stride(1) != 1 or not out.is_cuda or out.stride(1) != 1:
+        raise ValueError("x and out must be GPU tensors with unit column stride")
+    t = x.shape[0]
+    check(lib().qp_prefill_gemm_noalloc(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0),
+                                        out.data_ptr(), out.stride(0), _stream()))
     return out
 
 

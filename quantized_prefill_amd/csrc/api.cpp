@@ -133,6 +133,20 @@ qp_status qp_prefill_gemm_ws(int qtype, const void* w, int64_t n, int64_t k, con
                   "gemm launch");
 }
 
+qp_status qp_prefill_gemm_noalloc(int qtype, const void* w, int64_t n, int64_t k, const void* x, int x_dtype,
+                                  int64_t t, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+  static_assert(QP_NOALLOC_SCRATCH_BYTES == qp::kNoAllocScratchBytes, "header states the scratch size");
+  if (x_dtype != QP_F16 && x_dtype != QP_F32) return fail(QP_ERR_INVALID_PARAMETER, "x_dtype must be QP_F16 or QP_F32");
+  qp_status st = gemm_checks(qtype, w, n, k, x, t, ldx, x_dtype == QP_F32 ? 4 : 2, y, ldy);
+  if (st != QP_OK || t == 0) return st;
+  const size_t need = qp_prefill_gemm_workspace_bytes(n, k, t);
+  if (need > qp::kNoAllocScratchBytes)
+    return fail(QP_ERR_WORKSPACE_TOO_SMALL, "this split needs %zu bytes of partial sums, above the %zu-byte static scratch",
+                need, qp::kNoAllocScratchBytes);
+  return from_hip(qp::launch_gemm_noalloc(qtype, w, n, k, x, x_dtype == QP_F32, t, ldx, y, ldy, stream),
+                  "gemm_noalloc launch");
+}
+
 size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   if (n <= 0 || k <= 0 || t < 0 || n > kMaxDim || k > kMaxDim || t > kMaxDim) return 0;
   const int parts = qp::gemm_ksplit_parts(n, k, t);

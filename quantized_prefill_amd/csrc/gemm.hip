@@ -29,6 +29,7 @@
 // column l%32), k = 8*(l/32) + e; result register a of lane l holds
 // D[8*(a/4) + 4*(l/32) + a%4][l%32].
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "gemm_common.h"
@@ -318,6 +319,49 @@ hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, con
   }
   dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
   return x_f32 ? launch_mode<kPlainF32>(qtype, grid, p, s) : launch_mode<kPlainF16>(qtype, grid, p, s);
+}
+
+// ---------------------------------------------------------------------------
+// The K split without a caller workspace, for callers that cannot allocate:
+// the partial sums go to `scratch`, a static device array that every GPU the
+// library runs on holds until the process ends.  A split launch has
+// tiles * parts < 2 * CUs (parts is the smallest power of two that reaches
+// one workgroup per CU) and at most 128 x 128 outputs per tile, so on a GPU
+// of up to 256 CUs its partial sums take under 512 * 16384 floats = 32 MiB.
+// In host code `scratch` names a host-side stand-in: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_noalloc(int qtype, const void* w, int64_t n, int64_t k, const void* x, bool x_f32, int64_t t,
+                               int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+  void* ptr = nullptr;
+  hipError_t e = noalloc_scratch(&ptr);
+  if (e != hipSuccess) return e;
+  return launch_gemm_split(qtype, w, n, k, x, x_f32, t, ldx, y, ldy, (float*)ptr,
+                           (int64_t)(kNoAllocScratchBytes / sizeof(float)), s);
 }
 
 hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,

@@ -155,3 +155,14 @@ def test_attention_rejections():
     assert call(k=FAKE + 2) == 1        # binary16 cache not 16-byte aligned
     assert call(kv=qp.Q4_0, k=FAKE + 1) == 1   # Q4_0 cache on an odd byte
     assert call(out=FAKE + 8) == 1
+
+
+def test_noalloc_rejections():
+    """The allocation-free projection validates like qp_prefill_gemm, before
+    anything is launched (t == 0 is a no-op that touches no device)."""
+    L = qp.lib()
+    assert L.qp_prefill_gemm_noalloc(2, FAKE, 64, 256, FAKE, qp.F16, 8, 256, FAKE, 64, None) == 2
+    assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 300, FAKE, qp.F16, 8, 304, FAKE, 64, None) == 1
+    assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 256, FAKE, 7, 8, 256, FAKE, 64, None) == 1
+    assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 256, FAKE + 8, qp.F16, 8, 256, FAKE, 64, None) == 1
+    assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 0, 256, FAKE, 64, None) == 0
