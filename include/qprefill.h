@@ -177,6 +177,24 @@ qp_status qp_prefill_gemm_noalloc(int qtype, const void* w, int64_t n, int64_t k
                                   int64_t t, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 
 /*
+ * The two input projections of a feed-forward layer over one chunk ("What
+ * changes": batched prefill of a chunk of prompt tokens in FP16, one product
+ * per projection):
+ *   y_gate = the qp_prefill_gemm result for (w_gate, n)
+ *   y_up   = the qp_prefill_gemm result for (w_up, n)
+ * over the same binary16 x (T x K, row stride ldx), with one qtype, n and k.
+ * Where the two projections' tiles together fill the GPU this is a single
+ * launch; otherwise it is the two calls.  Each output matches its separate
+ * call within the GEMM tolerance (the summation order may differ), and every
+ * call with the same inputs gives the same bits.  The outputs must not
+ * overlap each other or x.  Requirements and errors are those of
+ * qp_prefill_gemm with x_dtype QP_F16, for each projection.
+ */
+qp_status qp_prefill_gemm_gate_up(int qtype, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                                  const uint16_t* x, int64_t t, int64_t ldx, float* y_gate, int64_t ldy_gate,
+                                  float* y_up, int64_t ldy_up, hipStream_t stream);
+
+/*
  * Prefill projection with the per-head RMSNorm of QK-norm models fused into
  * the epilogue ("What changes": per-head QK norm):  with Y = X . W^T as in
  * qp_prefill_gemm, for each token t and head h (columns h*head_dim ..

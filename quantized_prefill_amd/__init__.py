@@ -31,6 +31,7 @@ SIGNATURES = {
     "qp_prefill_gemm_ws": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP, _SZ, _VP]),
     "qp_prefill_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qp_prefill_gemm_noalloc": (_INT, [_INT, _VP, _I64, _I64, _VP, _INT, _I64, _I64, _VP, _I64, _VP]),
+    "qp_prefill_gemm_gate_up": (_INT, [_INT, _VP, _VP, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _VP, _I64, _VP]),
     "qp_prefill_gemm_qknorm": (_INT, [_INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64, _F32C, _VP, _I64,
                                       _VP]),
     "qp_prefill_gemm_qkv": (_INT, [_INT, _VP, _I64, _VP, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _VP, _I64,
@@ -187,6 +188,24 @@ def prefill_gemm_noalloc(qtype: int, w, n: int, k: int, x, out):
     check(lib().qp_prefill_gemm_noalloc(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0),
                                         out.data_ptr(), out.stride(0), _stream()))
     return out
+
+
+def prefill_gemm_gate_up(qtype: int, w_gate, w_up, n: int, k: int, x, out_gate=None, out_up=None):
+    """The gate and up projections (each [T, n] f32) of one float16 x in one call."""
+    torch = _torch()
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor with unit column stride")
+    t = x.shape[0]
+    if out_gate is None:
+        out_gate = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    if out_up is None:
+        out_up = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    check(lib().qp_prefill_gemm_gate_up(qtype, _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), n, k, x.data_ptr(), t,
+                                        x.stride(0), out_gate.data_ptr(), out_gate.stride(0), out_up.data_ptr(),
+                                        out_up.stride(0), _stream()))
+    return out_gate, out_up
 
 
 def prefill_gemm_qknorm(qtype: int, w, n: int, k: int, x, head_dim: int, gain, gain_head_stride: int = 0,

@@ -154,6 +154,17 @@ size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   return (size_t)((parts * t * n * 4 + 255) / 256 * 256);
 }
 
+qp_status qp_prefill_gemm_gate_up(int qtype, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                                  const uint16_t* x, int64_t t, int64_t ldx, float* y_gate, int64_t ldy_gate,
+                                  float* y_up, int64_t ldy_up, hipStream_t stream) {
+  qp_status st = gemm_checks(qtype, w_gate, n, k, x, t, ldx, 2, y_gate, ldy_gate);
+  if (st != QP_OK) return st;
+  st = gemm_checks(qtype, w_up, n, k, x, t, ldx, 2, y_up, ldy_up);
+  if (st != QP_OK || t == 0) return st;
+  return from_hip(qp::launch_gemm_gate_up(qtype, w_gate, w_up, n, k, x, t, ldx, y_gate, ldy_gate, y_up, ldy_up, stream),
+                  "gemm_gate_up launch");
+}
+
 qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,
                                  int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
                                  float eps, float* y, int64_t ldy, hipStream_t stream) {

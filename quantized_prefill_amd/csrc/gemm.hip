@@ -246,6 +246,20 @@ static bool use_tall_tiles(int qtype, int64_t n, int64_t k, int64_t t, int64_t l
   return t >= 512 && tiles >= 256 && tall_strides_ok(ldx, ldy) && tall_weights_ok(qtype, k);
 }
 
+// The kernel with weights decoded into registers (256 x 256 tiles) where its
+// tiles fill the GPU in whole rounds (or at least two): its tiles do twice
+// the work of the 256 x 128 tall tile, so a partly filled last round costs
+// twice as much.
+static bool wide_fills(int64_t tiles) {
+  const int cus = cu_count();
+  return tiles >= cus && (tiles % cus == 0 || tiles >= 2 * cus);
+}
+static bool use_wide_tiles(int qtype, int mode, int64_t n, int64_t t, int64_t ldx, int64_t ldy) {
+  if (!wide_supported(qtype, mode) || !tall_strides_ok(ldx, ldy)) return false;
+  const int64_t cols = (n + wide_cols() - 1) / wide_cols();
+  return wide_fills(cols * ((t + 255) / 256));
+}
+
 // Sum of a plain projection's K parts, in part order:
 // y[r, c] = (..((p_0 + p_1) + p_2) ..) + p_{S-1}, partials dense (row stride n)
 // and part_stride floats apart.  One thread per 4 columns of a row.
@@ -296,6 +310,7 @@ hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, con
   p.y = y;
   p.ldy = ldy;
   p.vec_store = ldy % 4 == 0;
+  if (!x_f32 && use_wide_tiles(qtype, kPlainF16, n, t, ldx, ldy)) return launch_gemm_wide(qtype, kPlainF16, 8, p, s);
   if (!x_f32 && use_tall_tiles(qtype, n, k, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
@@ -388,6 +403,41 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
   }
   dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + BM - 1) / BM));
   return launch_mode<kQkNorm>(qtype, grid, p, s);
+}
+
+// The gate and up projections of a feed-forward layer over one X: one
+// launch of the wide kernel with two segments where its tiles fill the GPU,
+// else the two projections one after the other.
+hipError_t launch_gemm_gate_up(int qtype, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                               const uint16_t* x, int64_t t, int64_t ldx, float* y_gate, int64_t ldy_gate, float* y_up,
+                               int64_t ldy_up, hipStream_t s) {
+  const int64_t cols = (n + wide_cols() - 1) / wide_cols();
+  if (!wide_supported(qtype, kMulti) || !tall_strides_ok(ldx, ldy_gate) || !tall_strides_ok(ldx, ldy_up) ||
+      !wide_fills(2 * cols * ((t + 255) / 256))) {
+    hipError_t e = launch_gemm(qtype, w_gate, n, k, x, false, t, ldx, y_gate, ldy_gate, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm(qtype, w_up, n, k, x, false, t, ldx, y_up, ldy_up, s);
+  }
+  GemmParams p = {};
+  p.rb = row_bytes_of(qtype, k);
+  p.k = (int)k;
+  p.x = x;
+  p.ldx = ldx;
+  p.t = (int)t;
+  p.seg.nseg = 2;
+  const void* w[2] = {w_gate, w_up};
+  float* y[2] = {y_gate, y_up};
+  const int64_t ldy[2] = {ldy_gate, ldy_up};
+  for (int i = 0; i < 2; ++i) {
+    p.seg.tile0[i] = (int)(i * cols);
+    p.seg.w[i] = (const uint8_t*)w[i];
+    p.seg.n[i] = (int)n;
+    p.seg.k[i] = (int)k;
+    p.seg.y[i] = y[i];
+    p.seg.ldy[i] = ldy[i];
+  }
+  for (int i = 2; i <= kMaxSeg; ++i) p.seg.tile0[i] = (int)(2 * cols);
+  return launch_gemm_wide(qtype, kMulti, 8, p, s);
 }
 
 // Sums of the two K halves of split projections (k and v of the fused

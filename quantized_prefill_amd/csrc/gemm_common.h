@@ -366,4 +366,11 @@ static inline int64_t row_bytes_of(int qtype, int64_t cols) {
 // The 256-token tile kernel (gemm_tall.hip) for the plain f16 and QK-norm modes.
 hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p, hipStream_t s);
 
+// The kernel with in-register weight decode (gemm_wide.hip): tiles of
+// 32 * mi tokens x wide_cols() features, mi = 8 or 4; plain f16 or kMulti
+// (segments of whole column tiles over one X).
+bool wide_supported(int qtype, int mode);
+int wide_cols();
+hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s);
+
 }  // namespace qp

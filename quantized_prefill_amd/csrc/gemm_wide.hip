@@ -1,0 +1,632 @@
+// gemm_wide.hip -- the dequant-on-load projection for large prefill chunks
+//   Y[t, n] = sum_k X[t, k] * W[n, k]
+// ("QK-norm models take the FP16 batched prefill", section "What changes":
+// chunked batched prefill in FP16; the QK norm is per head).
+//
+// One wave per SIMD.  A workgroup of 4 waves owns a tile of BMW tokens x
+// BNW output features; wave w owns all BMW tokens of features
+// 32*NJ*w .. 32*NJ*w + 32*NJ - 1, i.e. MI x NJ MFMA tiles of 32 x 32
+// (v_mfma_f32_32x32x16_f16, f32 accumulators).  Each wave decodes the
+// weights of its own features straight into the MFMA B-operand registers, so
+// a weight is decoded once per tile and never goes through LDS as binary16.
+// Measured on MI355X: one wave per SIMD issuing independent MFMAs keeps the
+// matrix unit 97% busy with 2 independent VALU ops between MFMAs and 94%
+// with 4, so the decode arithmetic (2.5-3 VALU per weight, about 3 per MFMA
+// at 256 tokens) issues beside the MFMAs of the same wave.
+//
+// K order.  K advances in chunks of 64 weights (4 MFMA k-steps of 16).
+// Inside a chunk, k-step s takes, for lanes 0-31 (g = 0) and 32-63 (g = 1),
+// the 8 weights of piece 4(s%2) + 2g + s/2 (pieces of 8).  A lane (row n,
+// half g) therefore covers the two 16-weight runs [32r + 16g, 32r + 16g + 16)
+// of the chunk (r = s%2), which in every K-quant layout are 16 consecutive
+// code bytes of one scale group; the activations of a k-step are read from
+// the same pieces.  The sum over K is the same; only its order differs.
+//
+// Weights.  Raw block bytes of the tile's rows are staged into LDS 128
+// weights (a "step", two chunks) at a time by direct global-to-LDS dword
+// loads, R rows per wave instruction (lane L copies dword L % RSD of row
+// L / RSD, so consecutive rows sit RSD dwords apart, RSD odd), from a
+// wave-uniform scalar offset stepping 4R rows: contiguous runs of a row per
+// instruction keep the address unit cheap.  Two staging buffers: step t is
+// issued two chunks before its bytes are read.
+// Activations.  256-row x 64 tiles go straight from global memory into an
+// LDS ring (16-byte direct loads); LDS rows keep 8 pieces of 16 B, piece p
+// of row r in slot p ^ ((r >> 1) & 7), so a fragment read of 16 rows hits
+// 16 distinct 16-byte bank groups.
+#include <type_traits>
+
+#include "gemm_common.h"
+
+namespace qp {
+
+namespace wide {
+
+constexpr int NW = 8;               // waves per workgroup, two per SIMD
+constexpr int NTW = 64 * NW;
+constexpr int kLds = 160 * 1024;
+
+// Staging of one step (128 weights) of one row.
+//   NDW dwords are copied (from the dword holding the first byte of each
+//   field run), RSD >= NDW is the LDS pitch (odd).  off(d, h) is the byte
+//   offset from the dword-aligned block start of staged dword d for step
+//   half h of a 256-weight block (before subtracting the block's start
+//   misalignment, 0 or 2).
+template <int QT> struct Stage;
+
+// Q6_K half h: ql[64h, +64) (17 dwords), qh[32h, +32) (9), the 8 scales of
+// the half (3), d (1).
+template <> struct Stage<kQ6_K> {
+  static constexpr int NDW = 30, RSD = 31, TS = 210;
+  static __device__ __forceinline__ uint32_t off(int d, int h) {
+    return d < 17 ? 64 * h + 4 * d : d < 26 ? 128 + 32 * h + 4 * (d - 17) : d < 29 ? 192 + 8 * h + 4 * (d - 26) : 208;
+  }
+};
+// Q2_K half h (blocks keep 4-byte alignment): the 8 scale bytes (2 dwords),
+// qs[32h, +32) (8), d and dmin (1).
+template <> struct Stage<kQ2_K> {
+  static constexpr int NDW = 11, RSD = 11, TS = 84;
+  static __device__ __forceinline__ uint32_t off(int d, int h) {
+    return d < 2 ? 8 * h + 4 * d : d < 10 ? 16 + 32 * h + 4 * (d - 2) : 80;
+  }
+};
+// Q4_K half h (16-byte aligned blocks): d, dmin and the 12 scale bytes (4
+// dwords), qs[64h, +64) (16).
+template <> struct Stage<kQ4_K> {
+  static constexpr int NDW = 20, RSD = 21, TS = 144;
+  static __device__ __forceinline__ uint32_t off(int d, int h) { return d < 4 ? 4 * d : 16 + 64 * h + 4 * (d - 4); }
+};
+// Q5_K half h: header (4 dwords), qh[32] (8: every weight of the block has
+// its fifth bit there), qs[64h, +64) (16).
+template <> struct Stage<kQ5_K> {
+  static constexpr int NDW = 28, RSD = 29, TS = 176;
+  static __device__ __forceinline__ uint32_t off(int d, int h) {
+    return d < 12 ? 4 * d : 48 + 64 * h + 4 * (d - 12);
+  }
+};
+
+// One decode unit: 16 weights (run r of chunk O of a step) of one row, the
+// lane's k-steps r and r + 2.  read() fetches the unit's staged dwords (NU
+// of them); scale() derives the unit's factors; half<H>() decodes code
+// dwords 2H, 2H + 1 (8 weights) into the B operand of k-step r + 2H:
+//   b[s][q]: k-step s, dword q (two binary16 weights).
+struct UnitScale {
+  uint32_t x, y;  // per type: two f32 factors, or two packed binary16 tables
+};
+
+template <int QT> struct Dec;
+
+template <> struct Dec<kQ6_K> {
+  static constexpr int NU = 13;
+  // ql run r: staged dwords 8r + 4g .. + 4; qh: 17 + 4g .. + 4; the chunk's
+  // scales 26 + O .. 27 + O; d 29 (each run starts delta bytes into its dword)
+  template <int O, int r>
+  static __device__ __forceinline__ void read(const uint32_t* row, int g, uint32_t (&u)[NU]) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) u[i] = row[8 * r + 4 * g + i];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) u[5 + i] = row[17 + 4 * g + i];
+    u[10] = row[26 + O];
+    u[11] = row[27 + O];
+    u[12] = row[29];
+  }
+  // a = d * sc (exact in f32) and -(1024 + 32) a
+  template <int O, int r>
+  static __device__ __forceinline__ UnitScale scale(const uint32_t (&u)[NU], uint32_t delta, int g) {
+    const float d = f16_to_f32((u[12] >> (8 * delta)) & 0xFFFFu);
+    const uint32_t scw = __builtin_amdgcn_alignbyte(u[11], u[10], delta);  // the chunk's 4 scales
+    const float a = __fmul_rn(d, (float)(int)(int8_t)((scw >> (8 * (g + 2 * r))) & 0xFFu));
+    return {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, -__fmul_rn(a, 1056.f))};
+  }
+  // A byte permute makes two codes c into the binary16 numbers 1024 + c, and a
+  // mixed-precision fma a (1024 + c) - 1056 a = a (c - 32) writes each result
+  // into its half of the output word: every term is exact in f32, so the only
+  // rounding is the one to binary16.
+  template <int O, int r, int H>
+  static __device__ __forceinline__ void half(const uint32_t (&u)[NU], uint32_t delta, const UnitScale& sc,
+                                              uint32_t (&b)[4][4]) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    constexpr int c6 = 2 * O + r;  // which 2-bit field of qh
+    const float a = __builtin_bit_cast(float, sc.x), cc = __builtin_bit_cast(float, sc.y);
+#pragma unroll
+    for (int k = 2 * H; k < 2 * H + 2; ++k) {
+      const uint32_t ql = __builtin_amdgcn_alignbyte(u[k + 1], u[k], delta);
+      const uint32_t qh = __builtin_amdgcn_alignbyte(u[5 + k + 1], u[5 + k], delta);
+      const uint32_t lo = (O ? ql >> 4 : ql) & 0x0F0F0F0Fu;
+      // the 2-bit field c6 of each qh byte moved to bits 4..5
+      const uint32_t hs = c6 < 2 ? qh << (4 - 2 * c6) : (c6 == 2 ? qh : qh >> 2);
+      const uint32_t code = (hs & 0x30303030u) | lo;
+      const h2 x01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, code, 0x07010700u));
+      const h2 x23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, code, 0x07030702u));
+      const h2 r01 = {(_Float16)__builtin_fmaf(a, (float)x01[0], cc), (_Float16)__builtin_fmaf(a, (float)x01[1], cc)};
+      const h2 r23 = {(_Float16)__builtin_fmaf(a, (float)x23[0], cc), (_Float16)__builtin_fmaf(a, (float)x23[1], cc)};
+      b[r + 2 * H][2 * (k & 1)] = __builtin_bit_cast(uint32_t, r01);
+      b[r + 2 * H][2 * (k & 1) + 1] = __builtin_bit_cast(uint32_t, r23);
+    }
+  }
+};
+
+// Q2_K: the 4 values of a scale group, RNE16(fma(A, q, -B)) for q = 0..3,
+// as two packed words; each weight picks its value by byte permute
+// (selector bytes 2q, 2q + 1 of its binary16).
+template <> struct Dec<kQ2_K> {
+  static constexpr int NU = 6;
+  // qs: staged dwords 2 + 4g .. + 3 (aligned); the chunk's scales O; d, dmin 10
+  template <int O, int r>
+  static __device__ __forceinline__ void read(const uint32_t* row, int g, uint32_t (&u)[NU]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = row[2 + 4 * g + i];
+    u[4] = row[O];
+    u[5] = row[10];
+  }
+  template <int O, int r>
+  static __device__ __forceinline__ UnitScale scale(const uint32_t (&u)[NU], uint32_t, int g) {
+    const float d = f16_to_f32(u[5] & 0xFFFFu), dmin = f16_to_f32(u[5] >> 16);
+    const uint32_t s = (u[4] >> (8 * (2 * r + g))) & 0xFFu;
+    const float a = __fmul_rn(d, (float)(s & 15u));
+    const float bb = __fmul_rn(dmin, (float)(s >> 4));
+    return {pack_f16x2(__builtin_fmaf(a, 0.f, -bb), __builtin_fmaf(a, 1.f, -bb)),
+            pack_f16x2(__builtin_fmaf(a, 2.f, -bb), __builtin_fmaf(a, 3.f, -bb))};
+  }
+  template <int O, int r, int H>
+  static __device__ __forceinline__ void half(const uint32_t (&u)[NU], uint32_t, const UnitScale& sc,
+                                              uint32_t (&b)[4][4]) {
+    constexpr int j2 = 2 * O + r;  // 2-bit field of qs
+#pragma unroll
+    for (int k = 2 * H; k < 2 * H + 2; ++k) {
+      // 2q in each byte, then 2q and 2q + 1 interleaved as selectors
+      const uint32_t e = (j2 == 0 ? u[k] << 1 : u[k] >> (2 * j2 - 1)) & 0x06060606u;
+      const uint32_t od = e | 0x01010101u;
+      const uint32_t s01 = __builtin_amdgcn_perm(od, e, 0x05010400u);
+      const uint32_t s23 = __builtin_amdgcn_perm(od, e, 0x07030602u);
+      b[r + 2 * H][2 * (k & 1)] = __builtin_amdgcn_perm(sc.y, sc.x, s01);
+      b[r + 2 * H][2 * (k & 1) + 1] = __builtin_amdgcn_perm(sc.y, sc.x, s23);
+    }
+  }
+};
+
+// Q4_K / Q5_K: value = RNE16((d*sc)*q - dmin*m) with the products exact in
+// f32 and one rounding at the fused subtraction, then nearest-even binary16.
+__device__ __forceinline__ void kquant_values(uint32_t code, float a, float bb, uint32_t& w01, uint32_t& w23) {
+  const float v0 = __builtin_fmaf(a, (float)(code & 0xFFu), -bb);
+  const float v1 = __builtin_fmaf(a, (float)((code >> 8) & 0xFFu), -bb);
+  const float v2 = __builtin_fmaf(a, (float)((code >> 16) & 0xFFu), -bb);
+  const float v3 = __builtin_fmaf(a, (float)(code >> 24), -bb);
+  w01 = pack_f16x2(v0, v1);
+  w23 = pack_f16x2(v2, v3);
+}
+
+template <> struct Dec<kQ4_K> {
+  static constexpr int NU = 8;
+  // header 0..3; qs of chunk O: staged dwords 4 + 8O + 4g .. + 3 (both runs:
+  // low nibbles for r = 0, high for r = 1)
+  template <int O, int r>
+  static __device__ __forceinline__ void read(const uint32_t* row, int g, uint32_t (&u)[NU]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = row[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[4 + i] = row[4 + 8 * O + 4 * g + i];
+  }
+  template <int O, int r>
+  static __device__ __forceinline__ UnitScale scale(const uint32_t (&u)[NU], uint32_t h, int) {
+    const float d = f16_to_f32(u[0] & 0xFFFFu), dmin = f16_to_f32(u[0] >> 16);
+    uint32_t sc, m;
+    q4k_scale_min(u[1], u[2], u[3], 4 * h + 2 * O + r, sc, m);
+    return {__builtin_bit_cast(uint32_t, __fmul_rn(d, (float)sc)), __builtin_bit_cast(uint32_t, __fmul_rn(dmin, (float)m))};
+  }
+  template <int O, int r, int H>
+  static __device__ __forceinline__ void half(const uint32_t (&u)[NU], uint32_t, const UnitScale& sc,
+                                              uint32_t (&b)[4][4]) {
+#pragma unroll
+    for (int k = 2 * H; k < 2 * H + 2; ++k) {
+      const uint32_t code = (u[4 + k] >> (4 * r)) & 0x0F0F0F0Fu;
+      kquant_values(code, __builtin_bit_cast(float, sc.x), __builtin_bit_cast(float, sc.y), b[r + 2 * H][2 * (k & 1)],
+                    b[r + 2 * H][2 * (k & 1) + 1]);
+    }
+  }
+};
+
+template <> struct Dec<kQ5_K> {
+  static constexpr int NU = 12;
+  // header 0..3; qh bytes 16g .. + 15: staged dwords 4 + 4g; qs of chunk O: 12 + 8O + 4g
+  template <int O, int r>
+  static __device__ __forceinline__ void read(const uint32_t* row, int g, uint32_t (&u)[NU]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = row[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[4 + i] = row[4 + 4 * g + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[8 + i] = row[12 + 8 * O + 4 * g + i];
+  }
+  template <int O, int r>
+  static __device__ __forceinline__ UnitScale scale(const uint32_t (&u)[NU], uint32_t h, int) {
+    const float d = f16_to_f32(u[0] & 0xFFFFu), dmin = f16_to_f32(u[0] >> 16);
+    uint32_t sc, m;
+    q4k_scale_min(u[1], u[2], u[3], 4 * h + 2 * O + r, sc, m);
+    return {__builtin_bit_cast(uint32_t, __fmul_rn(d, (float)sc)), __builtin_bit_cast(uint32_t, __fmul_rn(dmin, (float)m))};
+  }
+  // the fifth bit of weight l is bit j = 4h + 2O + r of qh byte l
+  template <int O, int r, int H>
+  static __device__ __forceinline__ void half(const uint32_t (&u)[NU], uint32_t h, const UnitScale& sc,
+                                              uint32_t (&b)[4][4]) {
+    const uint32_t j = 4 * h + 2 * O + r;
+#pragma unroll
+    for (int k = 2 * H; k < 2 * H + 2; ++k) {
+      const uint32_t code = ((u[8 + k] >> (4 * r)) & 0x0F0F0F0Fu) | (((u[4 + k] >> j) & 0x01010101u) << 4);
+      kquant_values(code, __builtin_bit_cast(float, sc.x), __builtin_bit_cast(float, sc.y), b[r + 2 * H][2 * (k & 1)],
+                    b[r + 2 * H][2 * (k & 1) + 1]);
+    }
+  }
+};
+
+// LDS offset (halfs) of 16-byte piece `piece` of activation row `row`
+__device__ __forceinline__ int xswz(int row, int piece) { return (row * 8 + (piece ^ ((row >> 1) & 7))) * 8; }
+
+// s_waitcnt vmcnt(N), the other counters unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int QT, int MI>
+struct Cfg {
+  static constexpr int BMW = 32 * MI, BNW = 32 * NW;
+  static constexpr int RSD = Stage<QT>::RSD;
+  static constexpr int R = 64 / RSD;                       // rows per staging instruction
+  static constexpr int NG = (BNW + R - 1) / R;             // groups of R rows per tile
+  static constexpr int NI = (NG + NW - 1) / NW;            // staging instructions per wave and step
+  static constexpr int XTILE = BMW * 64;                   // halfs per activation chunk
+  static constexpr int RAWB = BNW * RSD + 64;              // dwords per staging buffer (64 of padding)
+  static constexpr int XB = 3;
+  static constexpr int XL = BMW * 8 / 64 / NW;             // activation loads per wave and chunk (16 B per lane)
+  static_assert((NG - 1) * R * RSD + 64 <= RAWB, "the padding takes the last group's spare lanes");
+  static_assert(XB * XTILE * 2 + 2 * RAWB * 4 <= kLds, "LDS budget");
+  static_assert(XL * NW * 64 == BMW * 8, "whole activation loads per wave");
+};
+
+template <int QT, int MI>
+struct Smem {
+  using C = Cfg<QT, MI>;
+  _Float16 x[C::XB][C::XTILE];
+  uint32_t raw[2][C::RAWB];
+};
+
+}  // namespace wide
+
+using namespace wide;
+
+// Main loop and epilogue of one tile; FULL: every row of the tile is inside
+// the weight tensor (staging addresses from a per-lane constant and a
+// per-instruction scalar offset).
+//
+// Wave w owns features 32 w .. 32 w + 31 of the tile.  Its B operands sit in
+// one set of four k-step slots; slot x is refilled for the next chunk in the
+// k-step after the MFMAs that last read it.  A chunk's decode has two units
+// (runs r = 0, 1; unit r fills k-steps r and r + 2, as halves H = 0, 1).
+// Schedule of chunk c:
+//   k-step 0: read the staged bytes of unit 0 of chunk c + 1; slot 3 <- unit
+//             1, half 1 of chunk c
+//   k-step 1: slot 0 <- unit 0, half 0 of chunk c + 1; read the staged bytes
+//             of unit 1 of chunk c + 1
+//   k-step 2: slot 1 <- unit 1, half 0 of chunk c + 1
+//   wait for the activations of chunk c + 1 (and, for odd c, the staging of
+//   the step after next); barrier
+//   k-step 3: load activation chunk c + 3 into the buffer chunk c used;
+//             slot 2 <- unit 0, half 1 of chunk c + 1
+// In every k-step the MI MFMAs issue with one activation fragment read after
+// each, for the same M block of the next k-step (k-step 0 of chunk c + 1
+// after k-step 3: its activations are in place once the barrier passed).
+// Staging of step t + 2 (into the buffer step t used) is issued in four
+// parts, at k-step 3 of chunk 2t and k-steps 0..2 of chunk 2t + 1: every
+// read of step t happens before the barrier of chunk 2t, and step t + 2 is
+// first read after the barrier of chunk 2t + 2.  Indices past the end are
+// clamped to the last chunk or step (the loads and decodes then repeat valid
+// data that nothing uses), so the loop body has no branches.
+template <int QT, int MODE, int MI, bool FULL>
+__device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm, int n0, int m0) {
+  using C = Cfg<QT, MI>;
+  using S = Stage<QT>;
+  using D = Dec<QT>;
+  constexpr int BMW = C::BMW, BNW = C::BNW, XB = C::XB, RSD = C::RSD, R = C::R, NI = C::NI, XL = C::XL;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int m_rows = min(BMW, p.t - m0);
+  const int nch = p.k / BK;     // chunks of 64 (a multiple of 4)
+  const int nsteps = nch / 2;   // staging steps of 128
+  const int64_t rb = p.rb;
+  const uint32_t rb3 = (uint32_t)(rb & 3);
+
+  // ---- activation copy: load q of wave w puts lane l at tile row
+  // w * BMW / NW + 8 q + l / 8, slot l % 8
+  const _Float16* xtile = (const _Float16*)p.x + (int64_t)m0 * p.ldx;
+  uint32_t xoff[XL];
+#pragma unroll
+  for (int q = 0; q < XL; ++q) {
+    const int row = w * (BMW / NW) + 8 * q + (lane >> 3);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    xoff[q] = (uint32_t)(2 * (min(row, m_rows - 1) * p.ldx + 8 * piece));
+  }
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)xtile, (short)0, -1, 0x00020000);
+  auto load_x = [&](int c) __attribute__((always_inline)) {
+    c = min(c, nch - 1);  // past the end: the last chunk again (keeps the load count uniform)
+    _Float16* dst = sm.x[c % XB] + w * (BMW / NW) * 64;
+#pragma unroll
+    for (int q = 0; q < XL; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (__attribute__((address_space(3))) void*)(dst + 8 * q * 64), 16,
+                                               (int)xoff[q], 128 * c, 0, 0);
+  };
+
+  // ---- weight staging: row n of the tile at LDS dword RSD * n (RSD odd).
+  // Instruction q of wave w stages group grp = NW q + w of R rows (past the
+  // last group: the last group again, the same bytes to the same place); lane
+  // L loads the dword that belongs at group dword L, i.e. dword L % RSD of row
+  // grp R + L / RSD.  Every lane loads, so no branch splits the loop: lanes
+  // past the group's R rows write the first dwords of the next rows, exactly
+  // what those rows' own loads write there, and a lane on a row's padding
+  // dword writes a copy of the row's last staged dword there.  In the last
+  // group the lanes past the tile's rows copy its last row instead, into the
+  // 64 dwords of padding after the buffer (rows past the tile need not exist).
+  const int sgr = lane / RSD, sd = min(lane % RSD, S::NDW - 1);
+  const int sgr_last = min(sgr, BNW - 1 - (C::NG - 1) * R);
+  const uint8_t* wtile = p.w + (int64_t)n0 * rb;
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)wtile, (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrsrc_part =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wtile, (short)0, FULL ? -1 : (int)((int64_t)(p.n - n0) * rb), 0x00020000);
+  // FULL: the dword-aligned start of the lane's run splits into a per-lane
+  // part and a per-instruction part (rows 2 apart start at the same offset
+  // within a dword, and R is even wherever rb % 4 != 0), for block offsets 0
+  // and 2 mod 4 and the two step halves
+  auto lane_off = [&](int gr, uint32_t& v00, uint32_t& va, uint32_t& vh) __attribute__((always_inline)) {
+    v00 = (((uint32_t)(gr * rb)) & ~3u) + S::off(sd, 0);
+    va = ((((uint32_t)(gr * rb) + 2u) & ~3u) - (((uint32_t)(gr * rb)) & ~3u));  // 0 or 4
+    vh = S::off(sd, 1) - S::off(sd, 0);
+  };
+  uint32_t vo00, vo_a, vo_h, vl00, vl_a, vl_h;
+  lane_off(sgr, vo00, vo_a, vo_h);
+  lane_off(sgr_last, vl00, vl_a, vl_h);
+  // part [Q0, Q1) of the loads of step st (clamped to the last step) into buffer buf
+  auto stage_part = [&](int st, int buf, auto q0c, auto q1c) __attribute__((always_inline)) {
+    constexpr int Q0 = decltype(q0c)::value, Q1 = decltype(q1c)::value;
+    st = min(st, nsteps - 1);
+    const int u = st >> 1, h = st & 1;
+    const uint32_t boff = (uint32_t)u * S::TS;
+    uint32_t* dst = sm.raw[buf];
+    if constexpr (FULL) {
+      const uint32_t ab = (boff >> 1) & 1u;
+      const uint32_t v0 = vo00 + ab * vo_a + (uint32_t)h * vo_h;
+      const uint32_t vl = vl00 + ab * vl_a + (uint32_t)h * vl_h;
+#pragma unroll
+      for (int q = Q0; q < Q1; ++q) {
+        const int grp = min(NW * q + w, C::NG - 1);
+        const bool last = NW * q + NW - 1 >= C::NG - 1 && grp == C::NG - 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (__attribute__((address_space(3))) void*)(dst + grp * R * RSD), 4,
+                                                 (int)(last ? vl : v0), (int)((int64_t)grp * R * rb + (boff & ~3u)), 0, 0);
+      }
+    } else {
+      // the tile's last rows lie past the tensor: the whole offset goes in
+      // the range-checked per-lane offset, and loads at or past the tensor's
+      // end (wrsrc_part's record count) return zeros, which only rows past
+      // the tensor receive (their outputs are not stored)
+      const uint32_t v0 = ((((uint32_t)(sgr * rb) + boff) & ~3u) + S::off(sd, h));
+#pragma unroll
+      for (int q = Q0; q < Q1; ++q) {
+        const int grp = min(NW * q + w, C::NG - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc_part,
+                                                 (__attribute__((address_space(3))) void*)(dst + grp * R * RSD), 4,
+                                                 (int)(v0 + (uint32_t)(grp * R * rb)), 0, 0, 0);
+      }
+    }
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, NI / 4>;
+  using P2 = std::integral_constant<int, NI / 2>;
+  using P3 = std::integral_constant<int, 3 * NI / 4>;
+  using P4 = std::integral_constant<int, NI>;
+
+  // ---- decode side: the lane's row is tile row 32 w + l % 32
+  const int nrow = 32 * w + (lane & 31);
+  const uint32_t rdelta = (uint32_t)((FULL ? nrow : min(nrow, p.n - 1 - n0)) & 1) * rb3;  // 2: row starts 2 bytes into a dword
+  // staged bytes of unit (O, r) of step st (clamped)
+  auto read_unit = [&](int st, auto oc, auto rc, uint32_t (&u)[D::NU]) __attribute__((always_inline)) {
+    st = min(st, nsteps - 1);
+    D::template read<decltype(oc)::value, decltype(rc)::value>(sm.raw[st & 1] + nrow * RSD, g, u);
+  };
+  // Q6_K: misalignment of the block start; Q4_K / Q5_K: the step's half
+  auto dec_arg = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    st = min(st, nsteps - 1);
+    if constexpr (QT == kQ6_K)
+      return (rdelta + (uint32_t)(st >> 1) * S::TS) & 3;
+    else
+      return (uint32_t)(st & 1);
+  };
+
+  float16v acc[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i] = (float16v){};
+  // activation fragment of k-step s: row 32 i + l % 32, piece 4 (s % 2) + 2 g + s / 2;
+  // rows 32 apart share the slot order
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = 2 * xswz(lane & 31, 4 * (s & 1) + 2 * g + (s >> 1));
+  auto a_ptr = [&](int c, int s) __attribute__((always_inline)) -> const char* {
+    return (const char*)sm.x[min(c, nch - 1) % XB] + aoff[s];
+  };
+
+  uint32_t b[4][4];
+  half8 a[MI];
+  uint32_t u0[D::NU], u1[D::NU];
+  UnitScale s0, s1;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // ---- prologue: steps 0 and 1 staged, activation chunks 0 .. 2; chunk 0's
+  // slots 0..2 decoded (slot 3 in the loop's first k-step)
+  stage_part(0, 0, P0{}, P4{});
+  stage_part(1, 1, P0{}, P4{});
+  load_x(0);
+  load_x(1);
+  load_x(2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  {
+    const char* ap = a_ptr(0, 0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[i] = *(const half8*)(ap + 32 * 64 * 2 * i);
+  }
+  read_unit(0, I0{}, I0{}, u0);
+  read_unit(0, I0{}, I1{}, u1);
+  s0 = D::template scale<0, 0>(u0, dec_arg(0), g);
+  s1 = D::template scale<0, 1>(u1, dec_arg(0), g);
+  D::template half<0, 0, 0>(u0, dec_arg(0), s0, b);
+  D::template half<0, 1, 0>(u1, dec_arg(0), s1, b);
+  D::template half<0, 0, 1>(u0, dec_arg(0), s0, b);
+
+  // k-step s of chunk c: MFMA i, then the read of M block i of the next
+  // fragment (k-step s + 1, or k-step 0 of chunk c + 1)
+  auto mfmas = [&](int c, int s) __attribute__((always_inline)) {
+    const char* ap = s < 3 ? a_ptr(c, s + 1) : a_ptr(c + 1, 0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], __builtin_bit_cast(half8, b[s]), acc[i], 0, 0, 0);
+      a[i] = *(const half8*)(ap + 32 * 64 * 2 * i);
+    }
+  };
+  // per MFMA: the fragment read after it, a share of the VALU and of the global loads
+  auto interleave = [&](auto nvc, auto nmc) __attribute__((always_inline)) {
+    constexpr int NV = decltype(nvc)::value, NM = decltype(nmc)::value;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, (NM + MI - 1) / MI, 0);  // global load
+      __builtin_amdgcn_sched_group_barrier(0x002, (NV + MI - 1) / MI, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using V0 = std::integral_constant<int, 40>;
+
+  // chunk c = 2 st + O
+  auto chunk = [&](int st, auto oc) __attribute__((always_inline)) {
+    constexpr int O = decltype(oc)::value;
+    constexpr int ON = 1 - O;  // chunk c + 1 within its step
+    const int c = 2 * st + O;
+    const int sn = O ? st + 1 : st;  // step of chunk c + 1
+    using ONc = std::integral_constant<int, ON>;
+    const uint32_t da = dec_arg(st), dn = dec_arg(sn);
+    // k-step 0
+    if constexpr (O == 1) stage_part(st + 2, st & 1, P1{}, P2{});
+    mfmas(c, 0);
+    D::template half<O, 1, 1>(u1, da, s1, b);  // slot 3, this chunk
+    read_unit(sn, ONc{}, I0{}, u0);
+    interleave(V0{}, std::integral_constant<int, O == 1 ? P2::value - P1::value : 0>{});
+    // k-step 1
+    if constexpr (O == 1) stage_part(st + 2, st & 1, P2{}, P3{});
+    mfmas(c, 1);
+    s0 = D::template scale<ON, 0>(u0, dn, g);
+    D::template half<ON, 0, 0>(u0, dn, s0, b);  // slot 0, next chunk
+    read_unit(sn, ONc{}, I1{}, u1);
+    interleave(V0{}, std::integral_constant<int, O == 1 ? P3::value - P2::value : 0>{});
+    // k-step 2
+    if constexpr (O == 1) stage_part(st + 2, st & 1, P3{}, P4{});
+    mfmas(c, 2);
+    s1 = D::template scale<ON, 1>(u1, dn, g);
+    D::template half<ON, 1, 0>(u1, dn, s1, b);  // slot 1, next chunk
+    interleave(V0{}, std::integral_constant<int, O == 1 ? P4::value - P3::value : 0>{});
+    // activations of chunk c + 1 (and for odd c the staging of step st + 2) have landed
+    if constexpr (O == 1)
+      wait_vm<XL + NI>();
+    else
+      wait_vm<XL>();
+    lds_barrier();
+    // k-step 3
+    load_x(c + 3);  // its buffer held chunk c
+    if constexpr (O == 0) stage_part(st + 2, st & 1, P0{}, P1{});  // its buffer held step st
+    mfmas(c, 3);
+    D::template half<ON, 0, 1>(u0, dn, s0, b);  // slot 2, next chunk
+    interleave(V0{}, std::integral_constant<int, XL + (O == 0 ? P1::value : 0)>{});
+  };
+
+  for (int st = 0; st < nsteps; ++st) {
+    chunk(st, I0{});
+    chunk(st, I1{});
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
+  lds_barrier();
+
+  // ---- epilogue: 16-byte stores through a per-wave LDS transpose
+  float* scr = (float*)sm.x + 32 * 40 * w;
+  float16v accs[MI][1];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) accs[i][0] = acc[i];
+  store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
+                         [&](int r) __attribute__((always_inline)) { return p.y + (int64_t)(m0 + r) * p.ldy; });
+}
+
+// Grid: (column tiles, token tiles).  kMulti: projections over one X, each
+// a segment of whole column tiles (its own weights, rows and output).
+template <int QT, int MODE, int MI>
+__global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
+  __shared__ __attribute__((aligned(16))) Smem<QT, MI> sm;
+  GemmParams p = pk;
+  int tile_x = blockIdx.x;
+  if constexpr (MODE == kMulti) {
+    int sg = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
+    tile_x -= pk.seg.tile0[sg];
+    p.w = pk.seg.w[sg];
+    p.n = pk.seg.n[sg];
+    p.y = pk.seg.y[sg];
+    p.ldy = pk.seg.ldy[sg];
+  }
+  const int n0 = tile_x * Cfg<QT, MI>::BNW;
+  const int m0 = blockIdx.y * Cfg<QT, MI>::BMW;
+  if (n0 + Cfg<QT, MI>::BNW <= p.n)
+    wide_tile<QT, MODE, MI, true>(p, sm, n0, m0);
+  else
+    wide_tile<QT, MODE, MI, false>(p, sm, n0, m0);
+}
+
+bool wide_supported(int qtype, int mode) {
+  return (qtype == kQ6_K || qtype == kQ2_K || qtype == kQ4_K || qtype == kQ5_K) && (mode == kPlainF16 || mode == kMulti);
+}
+
+int wide_cols() { return 32 * NW; }
+
+template <int QT, int MODE, int MI>
+static void launch_wide_t(const GemmParams& p, uint32_t col_tiles, hipStream_t s) {
+  constexpr int BMW = 32 * MI;
+  const dim3 grid(col_tiles, (uint32_t)((p.t + BMW - 1) / BMW));
+  hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), grid, dim3(NTW), 0, s, p);
+}
+
+// Tiles of 32 * mi tokens x 256 features (mi = 8 or 4); kMulti: p.seg
+// holds the segments and col_tiles their total.
+hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s) {
+  if (mode != kPlainF16 && mode != kMulti) return hipErrorInvalidValue;
+  const uint32_t cols = mode == kMulti ? (uint32_t)p.seg.tile0[p.seg.nseg] : (uint32_t)((p.n + 255) / 256);
+#define QP_WIDE_T(QT)                                                                              \
+  if (mode == kMulti) {                                                                            \
+    if (mi == 8) launch_wide_t<QT, kMulti, 8>(p, cols, s); else launch_wide_t<QT, kMulti, 4>(p, cols, s); \
+  } else {                                                                                         \
+    if (mi == 8) launch_wide_t<QT, kPlainF16, 8>(p, cols, s); else launch_wide_t<QT, kPlainF16, 4>(p, cols, s); \
+  }
+  switch (qtype) {
+    case kQ6_K: QP_WIDE_T(kQ6_K) break;
+    case kQ2_K: QP_WIDE_T(kQ2_K) break;
+    case kQ4_K: QP_WIDE_T(kQ4_K) break;
+    case kQ5_K: QP_WIDE_T(kQ5_K) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QP_WIDE_T
+  return hipGetLastError();
+}
+
+}  // namespace qp

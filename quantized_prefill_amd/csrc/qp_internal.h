@@ -29,6 +29,11 @@ hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, co
                               int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
                               float eps, float* y, int64_t ldy, hipStream_t s);
 
+// gate and up projections of one X (same n and k)
+hipError_t launch_gemm_gate_up(int qtype, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                               const uint16_t* x, int64_t t, int64_t ldx, float* y_gate, int64_t ldy_gate, float* y_up,
+                               int64_t ldy_up, hipStream_t s);
+
 // q, k (per-head RMSNorm) and v (plain) projections of one X; n[i] == 0 skips
 // one.  partial: room for qkv_split_partial_floats() floats that lets k and v
 // run as two K halves (null: never split).

@@ -59,6 +59,20 @@ def sample_tokens(t: int, n: int, seed: int) -> np.ndarray:
     return np.array(sorted(idx), dtype=np.int64)
 
 
+def tile_rows(t: int, tile: int, extra: int, seed: int) -> np.ndarray:
+    """The first and last token row of every `tile`-row tile of a launch,
+    plus `extra` seeded others."""
+    idx = set()
+    for b in range(0, t, tile):
+        idx.add(b)
+        idx.add(min(b + tile - 1, t - 1))
+    rng = np.random.default_rng(seed)
+    target = len(idx) + extra
+    while len(idx) < min(target, t):
+        idx.add(int(rng.integers(0, t)))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
 @functools.lru_cache(maxsize=None)
 def weights(qtype: int, rows: int, cols: int, seed: int) -> np.ndarray:
     return synth.quant_weights(qtype, rows, cols, seed)

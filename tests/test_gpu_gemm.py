@@ -5,7 +5,7 @@ import pytest
 
 import synth
 import quantized_prefill_amd as qp
-from gpu_helpers import assert_close, act_f16, sample_tokens, say, to_dev, weights
+from gpu_helpers import assert_close, act_f16, sample_tokens, say, tile_rows, to_dev, weights
 from synth import F16W, Q8_0, Q4_K, Q5_K, Q6_K, Q2_K
 
 pytestmark = pytest.mark.gpu
@@ -136,7 +136,7 @@ def test_workload_projections(orc, name, qtype, n, k, t, wseed, xseed):
     raw = weights(qtype, n, k, wseed)
     x = act_f16(t, k, xseed)
     y = run_gemm(qtype, raw, n, k, x)
-    tok = sample_tokens(t, 12, 9000 + n)
+    tok = tile_rows(t, 256, 8, 9000 + n)  # first and last row of every 256-token tile, and others
     ref = orc.prefill_gemm(qtype, raw, n, k, x, tokens=tok)
     assert_close(y[tok], ref, name)
     weights.cache_clear()
@@ -169,7 +169,7 @@ def test_qknorm_workload(orc):
     K (Q6_K 4096 -> 8 heads), per-head RMSNorm with eps 1e-6."""
     t, hidden, hd = 8192, 4096, 128
     x = act_f16(t, hidden, synth.seed_for(3, 0))
-    tok = sample_tokens(t, 12, 9100)
+    tok = tile_rows(t, 256, 8, 9100)
     for name, qtype, n, wseed, gseed in (("q", Q4_K, 4096, synth.seed_for(3, 1), synth.seed_for(3, 3)),
                                          ("k", Q6_K, 1024, synth.seed_for(3, 2), synth.seed_for(3, 4))):
         say(f"qknorm workload {name} n={n}")
@@ -261,7 +261,7 @@ def test_qkv_workload(orc, qtype):
     ns = [p[1] for p in names]
     gains = [synth.gains(hd, synth.seed_for(2, 600 + j)) for j in range(2)]
     say(f"qkv workload {synth.NAMES[qtype]} t={t} n={ns}")
-    tok = sample_tokens(t, 10, 9200)
+    tok = tile_rows(t, 256, 8, 9200)
     yq, _, _ = check_qkv(orc, qtype, ws, ns, k, x, hd, gains, [0, 0], tok, f"qkv {synth.NAMES[qtype]}")
     y_sep = run_qknorm(qtype, ws[0], ns[0], k, x, hd, gains[0], 0, 1e-6)
     assert np.array_equal(yq, y_sep), "fused q differs from the separate QK-norm launch"

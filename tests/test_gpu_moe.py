@@ -119,6 +119,6 @@ def test_moe_workload(orc):
     assert np.allclose(w, rw, rtol=2e-6)
     say("moe workload: grouped expert GEMM")
     y = run_moe(Q4_K, wg, wu, wd, ne, hidden, inter, x, ids, w)
-    tok = sample_tokens(t, 10, 9800)
+    tok = sample_tokens(t, 64, 9800)
     ref = orc.moe(Q4_K, wg, wu, wd, ne, hidden, inter, x, rid, rw, tokens=tok)
     assert_close(y[tok], ref, "moe workload")
