@@ -93,6 +93,18 @@ struct UnitScale {
   uint32_t x, y;  // per type: two f32 factors, or two packed binary16 tables
 };
 
+// RNE16(fma(a, x, c)) for each binary16 half of x, packed as x is: one
+// v_fma_mixlo_f16 and one v_fma_mixhi_f16 (the compiler would otherwise round
+// through f32 pairs and a separate pack)
+__device__ __forceinline__ uint32_t fma_mix_pair(float a, uint32_t x, float c) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=&v"(r)
+      : "v"(a), "v"(x), "v"(c));
+  return r;
+}
+
 template <int QT> struct Dec;
 
 template <> struct Dec<kQ6_K> {
@@ -109,38 +121,40 @@ template <> struct Dec<kQ6_K> {
     u[11] = row[27 + O];
     u[12] = row[29];
   }
-  // a = d * sc (exact in f32) and -(1024 + 32) a
+  // a = d * sc times 2^24 and -32 d sc (both exact in f32)
   template <int O, int r>
   static __device__ __forceinline__ UnitScale scale(const uint32_t (&u)[NU], uint32_t delta, int g) {
     const float d = f16_to_f32((u[12] >> (8 * delta)) & 0xFFFFu);
     const uint32_t scw = __builtin_amdgcn_alignbyte(u[11], u[10], delta);  // the chunk's 4 scales
     const float a = __fmul_rn(d, (float)(int)(int8_t)((scw >> (8 * (g + 2 * r))) & 0xFFu));
-    return {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, -__fmul_rn(a, 1056.f))};
+    return {__builtin_bit_cast(uint32_t, __fmul_rn(a, 16777216.f)), __builtin_bit_cast(uint32_t, __fmul_rn(a, -32.f))};
   }
-  // A byte permute makes two codes c into the binary16 numbers 1024 + c, and a
-  // mixed-precision fma a (1024 + c) - 1056 a = a (c - 32) writes each result
-  // into its half of the output word: every term is exact in f32, so the only
-  // rounding is the one to binary16.
+  // 6-bit codes of the four weights in staged dword j of the run (bits 0..5 of each byte)
+  template <int O, int r>
+  static __device__ __forceinline__ uint32_t codes(const uint32_t (&u)[NU], int j) {
+    constexpr int c6 = 2 * O + r;  // which 2-bit field of qh
+    const uint32_t ql = u[j], qh = u[5 + j];
+    const uint32_t lo = (O ? ql >> 4 : ql) & 0x0F0F0F0Fu;
+    // the 2-bit field c6 of each qh byte moved to bits 4..5
+    const uint32_t hs = c6 < 2 ? qh << (4 - 2 * c6) : (c6 == 2 ? qh : qh >> 2);
+    return (hs & 0x30303030u) | lo;
+  }
+  // A byte permute puts each code c alone in the low byte of a binary16, the
+  // subnormal c 2^-24, starting delta bytes into the run; a mixed-precision fma
+  // (a 2^24) (c 2^-24) - 32 a = a (c - 32) is exact in f32 (at most 8 + 11 + 6
+  // significant bits), so the only rounding is the one to binary16.
   template <int O, int r, int H>
   static __device__ __forceinline__ void half(const uint32_t (&u)[NU], uint32_t delta, const UnitScale& sc,
                                               uint32_t (&b)[4][4]) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    constexpr int c6 = 2 * O + r;  // which 2-bit field of qh
     const float a = __builtin_bit_cast(float, sc.x), cc = __builtin_bit_cast(float, sc.y);
+    const uint32_t sel01 = 0x0C010C00u + delta * 0x00010001u, sel23 = 0x0C030C02u + delta * 0x00010001u;
+    uint32_t cw[3];
 #pragma unroll
-    for (int k = 2 * H; k < 2 * H + 2; ++k) {
-      const uint32_t ql = __builtin_amdgcn_alignbyte(u[k + 1], u[k], delta);
-      const uint32_t qh = __builtin_amdgcn_alignbyte(u[5 + k + 1], u[5 + k], delta);
-      const uint32_t lo = (O ? ql >> 4 : ql) & 0x0F0F0F0Fu;
-      // the 2-bit field c6 of each qh byte moved to bits 4..5
-      const uint32_t hs = c6 < 2 ? qh << (4 - 2 * c6) : (c6 == 2 ? qh : qh >> 2);
-      const uint32_t code = (hs & 0x30303030u) | lo;
-      const h2 x01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, code, 0x07010700u));
-      const h2 x23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, code, 0x07030702u));
-      const h2 r01 = {(_Float16)__builtin_fmaf(a, (float)x01[0], cc), (_Float16)__builtin_fmaf(a, (float)x01[1], cc)};
-      const h2 r23 = {(_Float16)__builtin_fmaf(a, (float)x23[0], cc), (_Float16)__builtin_fmaf(a, (float)x23[1], cc)};
-      b[r + 2 * H][2 * (k & 1)] = __builtin_bit_cast(uint32_t, r01);
-      b[r + 2 * H][2 * (k & 1) + 1] = __builtin_bit_cast(uint32_t, r23);
+    for (int j = 0; j < 3; ++j) cw[j] = codes<O, r>(u, 2 * H + j);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      b[r + 2 * H][2 * k] = fma_mix_pair(a, __builtin_amdgcn_perm(cw[k + 1], cw[k], sel01), cc);
+      b[r + 2 * H][2 * k + 1] = fma_mix_pair(a, __builtin_amdgcn_perm(cw[k + 1], cw[k], sel23), cc);
     }
   }
 };
@@ -186,13 +200,14 @@ template <> struct Dec<kQ2_K> {
 
 // Q4_K / Q5_K: value = RNE16((d*sc)*q - dmin*m) with the products exact in
 // f32 and one rounding at the fused subtraction, then nearest-even binary16.
+// A byte permute makes each code q the subnormal binary16 q 2^-24, and the
+// mixed-precision fma takes a = d sc 2^24, so a q 2^-24 is the exact product.
 __device__ __forceinline__ void kquant_values(uint32_t code, float a, float bb, uint32_t& w01, uint32_t& w23) {
-  const float v0 = __builtin_fmaf(a, (float)(code & 0xFFu), -bb);
-  const float v1 = __builtin_fmaf(a, (float)((code >> 8) & 0xFFu), -bb);
-  const float v2 = __builtin_fmaf(a, (float)((code >> 16) & 0xFFu), -bb);
-  const float v3 = __builtin_fmaf(a, (float)(code >> 24), -bb);
-  w01 = pack_f16x2(v0, v1);
-  w23 = pack_f16x2(v2, v3);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 x01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0u, code, 0x0C010C00u));
+  const h2 x23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0u, code, 0x0C030C02u));
+  w01 = pack_f16x2(__builtin_fmaf(a, (float)x01[0], -bb), __builtin_fmaf(a, (float)x01[1], -bb));
+  w23 = pack_f16x2(__builtin_fmaf(a, (float)x23[0], -bb), __builtin_fmaf(a, (float)x23[1], -bb));
 }
 
 template <> struct Dec<kQ4_K> {
@@ -211,7 +226,8 @@ template <> struct Dec<kQ4_K> {
     const float d = f16_to_f32(u[0] & 0xFFFFu), dmin = f16_to_f32(u[0] >> 16);
     uint32_t sc, m;
     q4k_scale_min(u[1], u[2], u[3], 4 * h + 2 * O + r, sc, m);
-    return {__builtin_bit_cast(uint32_t, __fmul_rn(d, (float)sc)), __builtin_bit_cast(uint32_t, __fmul_rn(dmin, (float)m))};
+    return {__builtin_bit_cast(uint32_t, __fmul_rn(__fmul_rn(d, (float)sc), 16777216.f)),
+            __builtin_bit_cast(uint32_t, __fmul_rn(dmin, (float)m))};
   }
   template <int O, int r, int H>
   static __device__ __forceinline__ void half(const uint32_t (&u)[NU], uint32_t, const UnitScale& sc,
@@ -242,7 +258,8 @@ template <> struct Dec<kQ5_K> {
     const float d = f16_to_f32(u[0] & 0xFFFFu), dmin = f16_to_f32(u[0] >> 16);
     uint32_t sc, m;
     q4k_scale_min(u[1], u[2], u[3], 4 * h + 2 * O + r, sc, m);
-    return {__builtin_bit_cast(uint32_t, __fmul_rn(d, (float)sc)), __builtin_bit_cast(uint32_t, __fmul_rn(dmin, (float)m))};
+    return {__builtin_bit_cast(uint32_t, __fmul_rn(__fmul_rn(d, (float)sc), 16777216.f)),
+            __builtin_bit_cast(uint32_t, __fmul_rn(dmin, (float)m))};
   }
   // the fifth bit of weight l is bit j = 4h + 2O + r of qh byte l
   template <int O, int r, int H>
