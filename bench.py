@@ -8,7 +8,11 @@ epilogue) and v in one call over their shared X, then o, gate, up and down.
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 `value` is the projection TFLOP/s (sum of algorithmic flops over the
 sum of the projection launches' HIP-event durations); the dequant GB/s is
-reported beside it.  After the timed region the remaining workloads -- the
+reported beside it, per (type, output dtype) and in total, from a timed
+region of the 28 dequants alone, and as measured inside the layer step.
+Every dequant writes its own destination (2.3 GB of outputs per pass, far
+past the 256 MB last-level cache), so no output is rewritten inside the
+cache.  After the timed region the remaining workloads -- the
 Q8_0 1024 x 1024 projection, the Q4_K Qwen3-1.7B layer at T = 512, the Q5_K
 Qwen3-8B layer at T = 2048 (projections one by one), the fused
 QK-norm projections at T = 8192, the routed 128-expert FFN and causal prompt
@@ -125,17 +129,33 @@ def build_8b(torch, synth, qp):
                               y=torch.empty((t, n), dtype=torch.float32, device=dev)))
     gains = {name: torch.from_numpy(synth.gains(128, synth.seed_for(2, 600 + j))).to(dev)
              for j, name in enumerate(("q", "k"))}
-    maxw = max(p["n"] * p["k"] for p in projs)
-    d32 = torch.empty(maxw, dtype=torch.float32, device=dev)
-    d16 = torch.empty(maxw, dtype=torch.float16, device=dev)
-    return dict(t=t, hidden=hidden, xs=xs, projs=projs, gains=gains, d32=d32, d16=d16, qtypes=(synth.Q6_K, synth.Q2_K))
+    # one f32 and one f16 destination per projection and type
+    for p in projs:
+        p["d32"] = torch.empty((p["n"], p["k"]), dtype=torch.float32, device=dev)
+        p["d16"] = torch.empty((p["n"], p["k"]), dtype=torch.float16, device=dev)
+    return dict(t=t, hidden=hidden, xs=xs, projs=projs, gains=gains, qtypes=(synth.Q6_K, synth.Q2_K))
 
 
-def step_8b(L, qp, timer):
+def dequant_group(qp, L, qt, f16):
+    """The f32 (or f16) dequant of the seven projections of one type, back to back."""
     for p in L["projs"]:
-        n, k = p["n"], p["k"]
-        timer.run("dequant_f32", lambda p=p: qp.dequant_f32(p["qtype"], p["w"], n, k, out=L["d32"][:n * k].view(n, k)))
-        timer.run("dequant_f16", lambda p=p: qp.dequant_f16(p["qtype"], p["w"], n, k, out=L["d16"][:n * k].view(n, k)))
+        if p["qtype"] == qt:
+            if f16:
+                qp.dequant_f16(qt, p["w"], p["n"], p["k"], out=p["d16"])
+            else:
+                qp.dequant_f32(qt, p["w"], p["n"], p["k"], out=p["d32"])
+
+
+def dequant_pass(L, qp, synth, timer):
+    """The 28 dequants of the layer, one event pair per (type, dtype) group of 7."""
+    for qt in L["qtypes"]:
+        for f16 in (False, True):
+            timer.run(f"dequant:{synth.NAMES[qt]}:{'f16' if f16 else 'f32'}",
+                      lambda qt=qt, f16=f16: dequant_group(qp, L, qt, f16))
+
+
+def step_8b(L, qp, synth, timer):
+    dequant_pass(L, qp, synth, timer)
     for qt in L["qtypes"]:
         pr = {p["name"]: p for p in L["projs"] if p["qtype"] == qt}
         q, k, v = pr["q"], pr["k"], pr["v"]
@@ -156,11 +176,17 @@ def gemm_flops_8b(L):
     return sum(2.0 * L["t"] * p["n"] * p["k"] for p in L["projs"])
 
 
-def dequant_bytes_8b(L, synth):
+def dequant_bytes_8b(L, synth, qt=None, f16=None):
+    """Algorithmic bytes of the layer's dequants (the weights read once per
+    launch, every output written once), optionally of one type or dtype."""
     tot = 0.0
     for p in L["projs"]:
+        if qt is not None and p["qtype"] != qt:
+            continue
         read = p["n"] * synth.row_bytes(p["qtype"], p["k"])
-        tot += 2 * read + p["n"] * p["k"] * (4 + 2)
+        for is16 in (False, True):
+            if f16 is None or f16 == is16:
+                tot += read + p["n"] * p["k"] * (2 if is16 else 4)
     return tot
 
 
@@ -170,10 +196,9 @@ def dequant_graph_gbps(torch, qp, L, synth, replays=10):
     the per-launch event pairs and host dispatch between them.  Reported beside
     the per-launch figure, never instead of it."""
     def deq():
-        for p in L["projs"]:
-            n, k = p["n"], p["k"]
-            qp.dequant_f32(p["qtype"], p["w"], n, k, out=L["d32"][:n * k].view(n, k))
-            qp.dequant_f16(p["qtype"], p["w"], n, k, out=L["d16"][:n * k].view(n, k))
+        for qt in L["qtypes"]:
+            for f16 in (False, True):
+                dequant_group(qp, L, qt, f16)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -210,13 +235,38 @@ def time_fn(torch, fn, iters):
     return s.elapsed_time(e) / iters  # ms
 
 
-def other_rows(torch, synth, qp, iters):
-    """The other workloads, each timed on its own after the main region."""
+ROW_GROUPS = ("q8_0", "q4_k_1p7b", "q5_k_8b", "qknorm", "moe", "attention")
+
+
+def other_rows(torch, synth, qp, iters, which=ROW_GROUPS):
+    """The other workloads, each timed on its own after the main region
+    (`which`: the groups of ROW_GROUPS to run)."""
     dev = torch.device("cuda")
+    rows = {}
+    if "q8_0" in which:
+        rows.update(_rows_q8_0(torch, synth, qp, iters, dev))
+    if "q4_k_1p7b" in which:
+        rows.update(_rows_q4_k_1p7b(torch, synth, qp, iters, dev))
+    if "q5_k_8b" in which:
+        rows.update(_rows_q5_k_8b(torch, synth, qp, iters, dev))
+    if "qknorm" in which:
+        rows.update(_rows_qknorm(torch, synth, qp, iters, dev))
+    if "moe" in which:
+        rows.update(_rows_moe(torch, synth, qp, iters, dev))
+    if "attention" in which:
+        rows.update(attention_rows(torch, synth, qp, iters))
+    return rows
+
+
+def _dev(torch, dev, a):
+    return torch.from_numpy(a).to(dev)
+
+
+def _rows_q8_0(torch, synth, qp, iters, dev):
     rows = {}
 
     def d(a):
-        return torch.from_numpy(a).to(dev)
+        return _dev(torch, dev, a)
 
     # Q8_0 1024 x 1024, T = 64, f32 activations
     w = d(synth.quant_weights(synth.Q8_0, 1024, 1024, synth.seed_for(0, 0)))
@@ -227,6 +277,15 @@ def other_rows(torch, synth, qp, iters):
     msd = time_fn(torch, lambda: qp.dequant_f32(synth.Q8_0, w, 1024, 1024, out=o32), iters)
     rows["q8_0_1024_t64"] = dict(gemm_tflops=2 * 64 * 1024 * 1024 / ms / 1e9, gemm_us=ms * 1e3,
                                  dequant_f32_gbps=(1024 * 1088 + 1024 * 1024 * 4) / msd / 1e6)
+    return rows
+
+
+def _rows_q4_k_1p7b(torch, synth, qp, iters, dev):
+    rows = {}
+
+    def d(a):
+        return _dev(torch, dev, a)
+
     # Q4_K, Qwen3-1.7B layer at T = 512
     flops, tms, dbytes, dms = 0.0, 0.0, 0.0, 0.0
     for i, (name, n, k) in enumerate(synth.PROJ_1_7B):
@@ -240,6 +299,15 @@ def other_rows(torch, synth, qp, iters):
         dbytes += n * synth.row_bytes(synth.Q4_K, k) + 4.0 * n * k
     rows["q4_k_qwen3_1p7b_t512"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
                                         dequant_f32_gbps=dbytes / dms / 1e6)
+    return rows
+
+
+def _rows_q5_k_8b(torch, synth, qp, iters, dev):
+    rows = {}
+
+    def d(a):
+        return _dev(torch, dev, a)
+
     # Q5_K, Qwen3-8B layer at T = 2048 (the seven projections, each on its own)
     flops, tms, dbytes, dms = 0.0, 0.0, 0.0, 0.0
     x8 = {}
@@ -257,6 +325,15 @@ def other_rows(torch, synth, qp, iters):
     rows["q5_k_qwen3_8b_t2048"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
                                        dequant_f32_gbps=dbytes / dms / 1e6)
     del x8
+    return rows
+
+
+def _rows_qknorm(torch, synth, qp, iters, dev):
+    rows = {}
+
+    def d(a):
+        return _dev(torch, dev, a)
+
     # fused QK norm, T = 8192
     t = 8192
     x = d(synth.activations_f16(t, 4096, synth.seed_for(3, 0))).view(torch.float16)
@@ -270,6 +347,15 @@ def other_rows(torch, synth, qp, iters):
         flops += 2.0 * t * n * 4096
     rows["qknorm_qwen3_8b_t8192"] = dict(tflops=flops / tms / 1e9, us=tms * 1e3)
     del x, y
+    return rows
+
+
+def _rows_moe(torch, synth, qp, iters, dev):
+    rows = {}
+
+    def d(a):
+        return _dev(torch, dev, a)
+
     # routed experts: 128 experts, top-8, T = 4096, router included
     t, ne, k, hidden, inter = 4096, 128, 8, 2048, 768
     wg = d(synth.quant_weights(synth.Q4_K, ne * inter, hidden, synth.seed_for(4, 2)))
@@ -290,7 +376,6 @@ def other_rows(torch, synth, qp, iters):
     flops = 2.0 * t * k * 3 * hidden * inter
     rows["moe_e128_top8_t4096"] = dict(tflops=flops / ms / 1e9, us=ms * 1e3)
     del wg, wu, wd, x, lg, ids, wts, out, ws
-    rows.update(attention_rows(torch, synth, qp, iters))
     return rows
 
 
@@ -319,36 +404,84 @@ def attention_rows(torch, synth, qp, iters):
     return rows
 
 
+def cpu_info():
+    """(CPU model name, logical CPUs) of the host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model or "unknown", os.cpu_count()
+
+
 def cpu_baseline(synth, budget_s: float):
-    """The oracle (binary64 GEMM over its own exact dequant) on the host cores,
-    on a bounded sample of the same workload: the first few token rows of
-    each 8B projection, growing until about budget_s seconds of CPU work."""
+    """The oracle (binary64 GEMM over its own exact dequant, and its f32
+    dequant) on the host cores, all threads and one thread, each on a bounded
+    sample of the same workload sized to a share of budget_s seconds."""
+    import numpy as np
     import oracle
     orc = oracle.get()
+    model, nproc = cpu_info()
+    threads_all = orc.num_threads()
     projs = []
     for qt in (synth.Q6_K, synth.Q2_K):
         for i, (name, n, k) in enumerate(synth.PROJ_8B):
-            projs.append((qt, n, k, synth.quant_weights(qt, n, k, synth.seed_for(2, 10 * qt + i))))
-    xs = {k: synth.activations_f16(1, k, synth.seed_for(2, 500 + k // 256)) for k in {p[2] for p in projs}}
-    def run(ntok):
-        flops = 0.0
-        t0 = time.perf_counter()
-        for qt, n, k, raw in projs:
-            orc.prefill_gemm(qt, raw, n, k, xs[k][:ntok])
-            flops += 2.0 * ntok * n * k
-        return flops, time.perf_counter() - t0
+            projs.append((qt, name, n, k, synth.quant_weights(qt, n, k, synth.seed_for(2, 10 * qt + i))))
 
-    flops, dt = run(1)
-    ntok = 1
-    # grow the sample until it takes about half the budget or more (the
-    # per-token cost falls as the dequant of each weight is shared)
-    while dt < 0.5 * budget_s and ntok < 512:
-        ntok = int(max(ntok + 1, min(512, ntok * budget_s / max(dt, 1e-3))))
-        xs = {k: synth.activations_f16(ntok, k, synth.seed_for(2, 500 + k // 256)) for k in xs}
+    def gemm_rate(sel, share):
+        """Grow the token count until the sample takes about `share` seconds
+        (the per-token cost falls as the dequant of each weight is shared)."""
+        xs = {}
+
+        def run(ntok):
+            for k in {p[3] for p in sel}:
+                xs[k] = synth.activations_f16(ntok, k, synth.seed_for(2, 500 + k // 256))
+            flops = 0.0
+            t0 = time.perf_counter()
+            for qt, _, n, k, raw in sel:
+                orc.prefill_gemm(qt, raw, n, k, xs[k])
+                flops += 2.0 * ntok * n * k
+            return flops, time.perf_counter() - t0
+
+        ntok = 1
         flops, dt = run(ntok)
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=orc.num_threads(), kind="oracle",
-                sample=f"first {ntok} token rows of each of the 14 Qwen3-8B projections (Q6_K and Q2_K), "
-                       f"binary64 dot products over the oracle's f32 dequant; {dt:.1f} s")
+        while dt < 0.5 * share and ntok < 512:
+            ntok = int(max(ntok + 1, min(512, ntok * share / max(dt, 1e-3))))
+            flops, dt = run(ntok)
+        return flops / dt / 1e9, ntok, dt
+
+    def dequant_rate(sel):
+        nbytes, dt = 0.0, 0.0
+        for qt, _, n, k, raw in sel:
+            t0 = time.perf_counter()
+            out = orc.dequant_f32(qt, raw, n, k)
+            dt += time.perf_counter() - t0
+            nbytes += raw.size + out.nbytes
+            del out
+        return nbytes / dt / 1e9, dt
+
+    gate = [p for p in projs if p[1] == "gate"]            # 12288 x 4096, Q6_K and Q2_K
+    small = [p for p in projs if p[1] in ("k", "v")]      # 1024 x 4096, both types
+    orc.set_num_threads(threads_all)
+    g_all, n_all, t_all = gemm_rate(projs, 0.45 * budget_s)
+    d_all, td_all = dequant_rate(gate)
+    orc.set_num_threads(1)
+    g_one, n_one, t_one = gemm_rate(small, 0.25 * budget_s)
+    d_one, td_one = dequant_rate(small)
+    orc.set_num_threads(threads_all)
+    return dict(value=g_all / 1e3, unit="TFLOP/s", cores=threads_all, kind="oracle",
+                sample=(f"GEMM: first {n_all} token rows of each of the 14 Qwen3-8B projections (Q6_K and Q2_K) on "
+                        f"{threads_all} threads ({t_all:.1f} s), first {n_one} rows of the k and v projections "
+                        f"on 1 thread ({t_one:.1f} s), binary64 dot products over the oracle's f32 dequant; "
+                        f"dequant to f32: the two 12288 x 4096 gate tensors on {threads_all} threads "
+                        f"({td_all:.1f} s), the four 1024 x 4096 k/v tensors on 1 thread ({td_one:.1f} s)"),
+                cpu_model=model, nproc=nproc, threads_all=threads_all,
+                gemm_gflops_all_threads=round(g_all, 3), gemm_gflops_1_thread=round(g_one, 3),
+                dequant_f32_gbps_all_threads=round(d_all, 3), dequant_f32_gbps_1_thread=round(d_one, 3))
 
 
 def two_pass_row(torch, synth, qp, L, iters):
@@ -394,6 +527,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
+    ap.add_argument("--rows", default=",".join(ROW_GROUPS),
+                    help="comma-separated groups of the other workloads to run: " + ", ".join(ROW_GROUPS))
+    ap.add_argument("--no-two-pass", action="store_true", help="skip the f16-cache comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -421,14 +557,14 @@ def main():
     torch.cuda.synchronize()
     timer = Timer()
     for _ in range(args.warmup):
-        step_8b(L, qp, timer)
+        step_8b(L, qp, synth, timer)
     torch.cuda.synchronize()
     timer.reset()
     print("bench: timed steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step_8b(L, qp, timer)
+        step_8b(L, qp, synth, timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timer.collect()
@@ -436,10 +572,35 @@ def main():
     dom_ms = timer.total["gemm_dom"] / timer.count["gemm_dom"]   # average launch
     dom_flops = sum(2.0 * L["t"] * p["n"] * p["k"] for p in L["projs"] if p["dom"])  # one launch covers them
     gemm_ms = (timer.total["gemm"] + timer.total["gemm_dom"]) / args.steps
-    deq_ms = (timer.total["dequant_f32"] + timer.total["dequant_f16"]) / args.steps
+    deq_cats = [c for c in timer.total if c.startswith("dequant:")]
+    deq_layer_ms = sum(timer.total[c] for c in deq_cats) / args.steps
+    # the dequants again in a timed region of their own: inside the layer step
+    # each follows the previous step's projections, whose outputs (up to
+    # 200 MB of Y) are still dirty in the last-level cache and get written
+    # back while the dequant streams its own outputs
+    print("bench: dequant region", file=sys.stderr, flush=True)
+    dtimer = Timer()
+    for _ in range(2):
+        dequant_pass(L, qp, synth, dtimer)
+    torch.cuda.synchronize()
+    dtimer.reset()
+    for _ in range(args.steps):
+        dequant_pass(L, qp, synth, dtimer)
+    torch.cuda.synchronize()
+    dtimer.collect()
+    deq_ms = sum(dtimer.total.values()) / args.steps
+    deq_rows = {}
+    for c in sorted(dtimer.total):
+        _, tname, dt = c.split(":")
+        qt = synth.BY_NAME[tname]
+        ms = dtimer.total[c] / dtimer.count[c]
+        nbytes = dequant_bytes_8b(L, synth, qt, dt == "f16")
+        deq_rows[f"{tname}_{dt}"] = {"gbps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
+                                     "us": round(ms * 1e3, 2), "mbytes": round(nbytes / 1e6, 1), "launches": 7}
     flops = gemm_flops_8b(L)
     tflops = flops / gemm_ms / 1e9
     dq_gbps = dequant_bytes_8b(L, synth) / deq_ms / 1e6
+    dq_layer_gbps = dequant_bytes_8b(L, synth) / deq_layer_ms / 1e6
     traffic = recorded_traffic()
     res = {
         "metric": METRIC,
@@ -461,6 +622,8 @@ def main():
         "dequant_gbps": round(dq_gbps, 1),
         "dequant_hbm_frac": round(dq_gbps / PEAK_HBM_GBPS, 4),
         "dequant_ms_per_step": round(deq_ms, 4),
+        "dequant_by_type": deq_rows,
+        "dequant_in_layer_gbps": round(dq_layer_gbps, 1),
         "roofline": {
             "kernel": DOMINANT,
             "bound": "mfma",
@@ -477,15 +640,22 @@ def main():
     dq_graph = dequant_graph_gbps(torch, qp, L, synth)
     res["dequant_graph_gbps"] = round(dq_graph, 1)
     res["dequant_graph_hbm_frac"] = round(dq_graph / PEAK_HBM_GBPS, 4)
-    if not args.no_rows:
+    two_pass = None
+    if not args.no_rows and not args.no_two_pass:
         print("bench: f16-cache comparator", file=sys.stderr, flush=True)
         two_pass = two_pass_row(torch, synth, qp, L, 10)
     del L
     torch.cuda.empty_cache()
     if not args.no_rows:
         print("bench: other workloads", file=sys.stderr, flush=True)
-        rows = other_rows(torch, synth, qp, 10)
-        rows["two_pass_f16_cache_q6_k_qwen3_8b_t2048"] = two_pass
+        which = [g for g in args.rows.split(",") if g]
+        unknown = set(which) - set(ROW_GROUPS)
+        if unknown:
+            print(f"bench.py: unknown row groups {sorted(unknown)}", file=sys.stderr)
+            sys.exit(2)
+        rows = other_rows(torch, synth, qp, 10, which)
+        if two_pass is not None:
+            rows["two_pass_f16_cache_q6_k_qwen3_8b_t2048"] = two_pass
         res["rows"] = {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in rows.items()}
     if not args.no_cpu:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)

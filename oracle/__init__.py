@@ -81,6 +81,8 @@ class Oracle:
         L.or_plant_name.argtypes = [i32]
         L.or_plant_name.restype = C.c_char_p
         L.or_num_threads.restype = i32
+        L.or_set_num_threads.argtypes = [i32]
+        L.or_set_num_threads.restype = None
 
     # -- small helpers -----------------------------------------------------
     @property
@@ -92,6 +94,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self._L.or_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the oracle's parallel loops from now on (timing only)."""
+        self._L.or_set_num_threads(int(n))
 
     def block_size(self, qtype: int) -> int:
         return self._L.or_block_size(qtype)

@@ -108,6 +108,15 @@ int or_num_threads(void) {
 #endif
 }
 
+/* Threads of the parallel loops from now on (n >= 1); timing only. */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* binary16 <-> binary32                                                     */
 

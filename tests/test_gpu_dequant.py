@@ -15,37 +15,40 @@ pytestmark = pytest.mark.gpu
 QTYPES = [Q8_0, Q4_K, Q5_K, Q6_K, Q2_K]
 
 
-def gpu_dequant(qtype, raw: np.ndarray, rows: int, cols: int, f16: bool):
-    """Dequant through the C ABI into a guarded buffer; returns (values, guards_intact)."""
+def gpu_dequant(qtype, raw: np.ndarray, rows: int, cols: int, f16: bool, dst_off: int = 0):
+    """Dequant through the C ABI into a guarded buffer; returns (values, guards_intact).
+    dst_off elements before the output move it off 16-byte alignment (the
+    kernels' fallback paths)."""
     import torch
     assert raw.size == rows * synth.row_bytes(qtype, cols), "weight buffer does not match rows x row_bytes"
     w = to_dev(raw)
     n = rows * cols
+    g0 = GUARD + dst_off
     if f16:
-        buf = torch.full((n + 2 * GUARD,), NAN16, dtype=torch.int16, device="cuda")
+        buf = torch.full((n + 2 * g0,), NAN16, dtype=torch.int16, device="cuda")
         esz = 2
     else:
-        buf = torch.full((n + 2 * GUARD,), NAN32, dtype=torch.int32, device="cuda")
+        buf = torch.full((n + 2 * g0,), NAN32, dtype=torch.int32, device="cuda")
         esz = 4
     before = buf.cpu().numpy().copy()
     fn = qp.lib().qp_dequant_f16 if f16 else qp.lib().qp_dequant_f32
-    qp.check(fn(qtype, w.data_ptr(), rows, cols, buf.data_ptr() + GUARD * esz,
+    qp.check(fn(qtype, w.data_ptr(), rows, cols, buf.data_ptr() + g0 * esz,
                 torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     after = buf.cpu().numpy()
-    intact = np.array_equal(after[:GUARD], before[:GUARD]) and np.array_equal(after[GUARD + n:], before[GUARD + n:])
-    vals = after[GUARD:GUARD + n]
+    intact = np.array_equal(after[:g0], before[:g0]) and np.array_equal(after[g0 + n:], before[g0 + n:])
+    vals = after[g0:g0 + n]
     return (vals.view(np.uint16) if f16 else vals.view(np.uint32)).reshape(rows, cols), intact
 
 
-def check_bits(orc, qtype, raw, rows, cols, what):
+def check_bits(orc, qtype, raw, rows, cols, what, dst_off=0):
     want32 = orc.dequant_f32(qtype, raw, rows, cols).view(np.uint32)
-    got32, ok32 = gpu_dequant(qtype, raw, rows, cols, False)
+    got32, ok32 = gpu_dequant(qtype, raw, rows, cols, False, dst_off)
     assert ok32, f"{what}: f32 dequant wrote outside rows x cols"
     bad = np.flatnonzero(got32.reshape(-1) != want32.reshape(-1))
     assert bad.size == 0, f"{what}: f32 mismatch at {bad[:5]} got {got32.reshape(-1)[bad[:5]]} want {want32.reshape(-1)[bad[:5]]}"
     want16 = orc.dequant_f16_bits(qtype, raw, rows, cols)
-    got16, ok16 = gpu_dequant(qtype, raw, rows, cols, True)
+    got16, ok16 = gpu_dequant(qtype, raw, rows, cols, True, dst_off)
     assert ok16, f"{what}: f16 dequant wrote outside rows x cols"
     bad = np.flatnonzero(got16.reshape(-1) != want16.reshape(-1))
     assert bad.size == 0, f"{what}: f16 mismatch at {bad[:5]}"
@@ -102,6 +105,26 @@ def test_extra_partial_row_8b(orc, qtype):
     for rows in (1, 3):
         raw = weights(qtype, rows, 4096 + 77, 7100 + rows)
         check_bits(orc, qtype, raw, rows, 4096 + 77, f"4173-wide rows={rows}")
+
+
+@pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
+def test_dense_boundaries(orc, qtype):
+    """Dense tensors whose weight count ends inside a wave's or a workgroup's
+    share of the flat kernel (1, 4096 / QK - 1, 4096 / QK, 4096 / QK + 1 and
+    3 (4096 / QK) + 5 blocks), as one row and as one block per row; and
+    outputs off 16-byte alignment (the per-unit kernel)."""
+    qk = synth.BLOCK[qtype][0]
+    nbg = 4096 // qk
+    for nb in (1, nbg - 1, nbg, nbg + 1, 3 * nbg + 5):
+        for rows in sorted({1, nb}):
+            cols = nb * qk // rows
+            raw = weights(qtype, rows, cols, 7500 + nb + rows)
+            say(f"dequant groups {synth.NAMES[qtype]} rows={rows} cols={cols}")
+            check_bits(orc, qtype, raw, rows, cols, f"{nb} blocks as {rows} rows")
+    raw = weights(qtype, 3, 5 * qk, 7600)
+    for dst_off in (1, 3):
+        say(f"dequant output offset {synth.NAMES[qtype]} +{dst_off}")
+        check_bits(orc, qtype, raw, 3, 5 * qk, f"dst +{dst_off} elements", dst_off)
 
 
 def test_edge_sizes(orc):
