@@ -16,9 +16,10 @@
  *     (each row)": the dequant is bit-exact with the CPU oracle, including a
  *     partial last block, and writes nothing outside its output.
  *   - "CUDA prefill VRAM loans and SM75 Q4/native-IQ opt-ins" (Strata PR),
- *     "Summary" and "Correctness and safety": routed experts run as a fused
- *     prefill path whose routing ids, expert selection, route weights and
- *     scatter order are those of the unfused path.
+ *     "Summary" and "Correctness and safety": the routed experts get a fused
+ *     prefill path that picks the same experts for each token, weighs them
+ *     the same and adds their outputs up in the same order as the unfused
+ *     path does.
  *
  * Conventions for every entry point:
  *   - Pointers marked (device) are device memory of the current HIP device;
@@ -74,14 +75,18 @@ typedef enum { QP_F16W = 1, QP_Q4_0 = 2, QP_Q8_0 = 8, QP_Q2_K = 10, QP_Q4_K = 12
 
 typedef enum { QP_F32 = 0, QP_F16 = 1 } qp_dtype;
 
-/* Weights per block: 1 (F16), 32 (Q8_0) or 256 (K types); -1 for an unsupported type. */
+/* Weights per block of a GGUF block type ("Qwen3.5 batched prefill has no f32
+ * dequant ...", "Cause": the dequant covers the model's block types): 1
+ * (F16), 32 (Q8_0, Q4_0) or 256 (K types); -1 for an unsupported type. */
 int64_t qp_block_size(int qtype);
 
-/* Bytes per block: 2, 34, 144, 176, 210, 84; -1 for an unsupported type. */
+/* Bytes per block (same passage): 2, 34 (Q8_0), 18 (Q4_0), 144, 176, 210,
+ * 84; -1 for an unsupported type. */
 int64_t qp_type_size(int qtype);
 
-/* Bytes of one row of `cols` weights: ceil(cols / QK) * type_size.
- * -1 for an unsupported type or cols <= 0. */
+/* Bytes of one row of `cols` weights (same passage; a row ends in a partial
+ * block when cols % QK != 0, "Acceptance (each row)"): ceil(cols / QK) *
+ * type_size.  -1 for an unsupported type or cols <= 0. */
 int64_t qp_row_bytes(int qtype, int64_t cols);
 
 /*
@@ -152,7 +157,8 @@ qp_status qp_prefill_gemm_ws(int qtype, const void* w, int64_t n, int64_t k, con
 
 /* Bytes of the workspace qp_prefill_gemm_ws uses for these sizes on the
  * current device (parts * t * n floats, rounded up to 256); 0 when it would
- * not split, or for sizes out of range. */
+ * not split, or for sizes out of range (the shape-dependent split of the
+ * Strata PR's "Summary", as for qp_prefill_gemm_ws). */
 size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t);
 
 /*
@@ -204,7 +210,11 @@ qp_status qp_prefill_gemm_gate_up(int qtype, const void* w_gate, const void* w_u
  *   gain (device): f32; gain_head_stride 0 shares one head_dim vector
  *                  across heads, head_dim gives each head its own.
  *   x (device): binary16 activations (as qp_prefill_gemm with QP_F16).
- * Requires head_dim in {64, 128}, n % head_dim == 0, finite eps > 0.
+ * Requires head_dim in {64, 128, 256}, n % head_dim == 0, finite eps > 0.
+ * Heads of 64 and 128 columns are normalised in the projection's epilogue;
+ * a head of 256 columns spans two output tiles, so the projection stores Y
+ * and a second pass normalises each head of the stored rows in place (the
+ * same arithmetic).
  */
 qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x,
                                  int64_t t, int64_t ldx, int64_t head_dim, const float* gain,
@@ -219,8 +229,9 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
  *   y_v = the qp_prefill_gemm result for (w_v, n_v) with binary16 x
  * over the same x (T x K binary16, row stride ldx), with one qtype, k,
  * head_dim and eps.  When the three projections' output tiles together fill
- * the GPU this is a single launch (k and v alone often do not: 1024 outputs
- * at T = 2048 make 64 tiles); otherwise it is the three calls.  Results match
+ * the GPU and head_dim <= 128 this is a single launch (k and v alone often do
+ * not fill it: 1024 outputs at T = 2048 make 64 tiles); otherwise it is the
+ * three calls.  Results match
  * the separate calls within the GEMM tolerance (summation order may differ);
  * y_q matches its separate call bit for bit, and every call with the same
  * inputs gives the same bits.
@@ -245,13 +256,14 @@ qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const voi
                               hipStream_t stream);
 
 /* Bytes of the optional workspace of qp_prefill_gemm_qkv (partial sums of k
- * and v: 2 * t * (n_k + n_v) floats, rounded up to 256); 0 for sizes out of
- * range. */
+ * and v: 2 * t * (n_k + n_v) floats, rounded up to 256; the work split of the
+ * Strata PR's "Summary"); 0 for sizes out of range. */
 size_t qp_prefill_gemm_qkv_workspace_bytes(int64_t n_q, int64_t n_k, int64_t n_v, int64_t t);
 
 /*
- * Router of a routed-expert layer ("Correctness and safety": routing ids,
- * expert selection and route weights):  for each token t,
+ * Router of a routed-expert layer (Strata PR, "Correctness and safety": the
+ * fused path must choose and weigh the experts exactly as the unfused one):
+ * for each token t,
  * p = softmax(logits[t, :]) over n_experts; the top_k experts by logit,
  * largest first, ties to the lower expert index; weight = p of each chosen
  * expert (renorm != 0 divides the chosen weights by their sum).
@@ -262,14 +274,17 @@ size_t qp_prefill_gemm_qkv_workspace_bytes(int64_t n_q, int64_t n_k, int64_t n_v
 qp_status qp_moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k,
                             int renorm, int32_t* ids, float* weights, hipStream_t stream);
 
-/* Workspace bytes qp_grouped_expert_gemm needs for these sizes (0 on a bad size). */
+/* Workspace bytes qp_grouped_expert_gemm needs for these sizes (0 on a bad
+ * size): the token lists of the Strata PR's fused expert path ("Summary"),
+ * the h rows between the passes and the per-pair outputs. */
 size_t qp_grouped_expert_workspace_bytes(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden,
                                          int64_t inter);
 
 /*
- * Routed expert FFN over per-expert token lists ("Summary": fused routed-
- * expert prefill; "Correctness and safety": same selection, weights and
- * scatter order):  for token t and slot s with expert e = ids[t, s]:
+ * Routed expert FFN over per-expert token lists (Strata PR, "Summary": fused
+ * routed-expert prefill; "Correctness and safety": the experts chosen, their
+ * weights and the order of the sum stay those of the unfused path):  for
+ * token t and slot s with expert e = ids[t, s]:
  *   g = x[t] . Wg_e^T, u = x[t] . Wu_e^T           (inter values each)
  *   h = SiLU(g) * u = g / (1 + exp(-g)) * u
  *   out[t, :] = sum over s = 0..top_k-1, in slot order, of weights[t, s] * (h . Wd_e^T)
@@ -278,19 +293,41 @@ size_t qp_grouped_expert_workspace_bytes(int64_t t, int64_t top_k, int64_t n_exp
  *   w_down (device): n_experts tensors of hidden x inter (stride hidden * row_bytes(inter)).
  *   x (device): t x hidden binary16, row stride hidden.
  *   ids, weights (device): t x top_k int32 / f32.  A pair whose id is out of
- *                          [0, n_experts) contributes nothing.
+ *                          [0, n_experts) contributes nothing and is counted
+ *                          in the workspace header (the aprender issue's
+ *                          "Cause": bad input is reported, never absorbed;
+ *                          qp_grouped_expert_dropped_pairs reads the count).
  *   out (device): t x hidden f32, row stride hidden.
  *   workspace (device): >= qp_grouped_expert_workspace_bytes(...), 256-byte
  *                       aligned; its contents on entry do not matter.
  * Token lists are built on the device (count, scan, stable fill by pair
  * index), so the result is deterministic.  Requires hidden % 256 == 0 and
- * inter % 256 == 0, 1 <= top_k <= n_experts.
+ * inter % 256 == 0, 1 <= top_k <= n_experts.  The workspace header (its
+ * first 256 bytes) holds at QP_MOE_DROPPED_PAIRS_OFFSET the uint32 count of
+ * dropped pairs of the call; a call with t == 0 launches nothing and leaves
+ * it as it was.
  */
 qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up, const void* w_down,
                                  int64_t n_experts, int64_t hidden, int64_t inter, const uint16_t* x,
                                  int64_t t, int64_t top_k, const int32_t* ids, const float* weights,
                                  float* out, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/*
+ * Reader of the dropped-pair count of the last qp_grouped_expert_gemm call
+ * that used `workspace` (the aprender issue, "Cause": an engine fails closed
+ * on input it cannot serve; the count lets the caller do so for expert ids
+ * out of range):
+ *   workspace (device): that call's workspace, 256-byte aligned.
+ *   count (host or device): one uint32_t, written by a copy enqueued on
+ *     `stream` after the work already there; valid once the stream has
+ *     reached it (pinned host memory or device memory keep the call
+ *     asynchronous; for pageable host memory HIP completes the copy first).
+ * Errors: QP_ERR_INVALID_PARAMETER for NULL or misaligned pointers,
+ * QP_ERR_DEVICE if the copy cannot be enqueued.
+ */
+#define QP_MOE_DROPPED_PAIRS_OFFSET 0
+qp_status qp_grouped_expert_dropped_pairs(const void* workspace, uint32_t* count, hipStream_t stream);
 
 /*
  * Causal prompt attention of one prefill chunk over a KV cache held as
@@ -315,24 +352,28 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
  *   out (device): t rows of f32, row stride ldo, head h at h*head_dim.
  * Arithmetic: Q, K, V and the probabilities enter FP16 MFMA products
  * (nearest-even binary16 of the f32 / exact cache values); scores, softmax
- * and accumulation are f32.  Requires head_dim == 128, n_head a multiple of
- * n_kv_head, n_head <= 1024, n_past + t < 2^31, ceil(t/128) * n_head < 2^24
- * (one workgroup per 128 queries and head), ldq and ldo >= n_head*head_dim
- * and multiples of 4, q and out 16-byte aligned, caches 16-byte (F16) or
- * 2-byte (Q8_0, Q4_0) aligned, a finite scale (scale * |q . k| must stay
- * within f32 range).  t == 0 is a no-op.  out must not
- * overlap q or the caches.  Errors: QP_ERR_UNSUPPORTED_TYPE for another
+ * and accumulation are f32.  scale: a finite number; 0 selects the usual
+ * 1 / sqrt(head_dim) (rounded to f32 from the binary64 value).  The running
+ * maximum of the online softmax starts at -inf, so any finite scaled scores
+ * are handled (scores that overflow f32 give inf or NaN).  Requires
+ * head_dim == 128, n_head a multiple of n_kv_head, n_head <= 1024,
+ * n_past + t < 2^31, ceil(t/128) * n_head < 2^24 (one workgroup per 128
+ * queries and head), ldq and ldo >= n_head*head_dim and multiples of 4, q
+ * and out 16-byte aligned, caches 16-byte (F16) or 2-byte (Q8_0, Q4_0)
+ * aligned.  t == 0 is a no-op.  out must not overlap q or the caches.  Errors: QP_ERR_UNSUPPORTED_TYPE for another
  * kv_type, QP_ERR_INVALID_PARAMETER otherwise.
  */
 qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
                               int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
                               float scale, float* out, int64_t ldo, hipStream_t stream);
 
-/* Static English name of a status ("QP_OK", ...). */
+/* Static English name of a status ("QP_OK", ...): the error kinds of the
+ * aprender issue's "Cause" (an unsupported type is an InvalidParameter-style
+ * error and the call fails closed). */
 const char* qp_status_string(qp_status s);
 
 /* Detail of the last error returned on the calling thread (host memory owned
- * by the library, valid until the next call on this thread). */
+ * by the library, valid until the next call on this thread); same passage. */
 const char* qp_last_error_detail(void);
 
 #ifdef __cplusplus

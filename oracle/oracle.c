@@ -86,7 +86,8 @@
 #define PLANT_ATTN_NO_SCALE    29  /* scores not multiplied by the scale */
 #define PLANT_Q4_0_HALVES      30  /* Q4_0: values 0..15 from high nibbles, 16..31 from low */
 #define PLANT_Q4_0_OFFSET      31  /* Q4_0 quant without the -8 */
-#define PLANT_COUNT            32
+#define PLANT_ATTN_MAX_FLOOR   32  /* softmax maximum taken from a finite floor of -1e30 */
+#define PLANT_COUNT            33
 
 static const char* const plant_names[PLANT_COUNT] = {
     "none", "q8_unsigned", "q6_no_offset", "q6_no_high", "q4_scale_high",
@@ -94,7 +95,7 @@ static const char* const plant_names[PLANT_COUNT] = {
     "q2_nibbles", "q4_nibble", "q6_shift", "gemm_transpose", "gemm_drop_k",
     "qkn_sum", "qkn_eps", "qkn_gain", "silu_sign", "moe_weight", "router_tie",
     "router_renorm", "moe_up", "q5_no_high", "q5_high_bit", "f16w_bytes",
-    "attn_no_mask", "attn_gqa", "attn_no_scale", "q4_0_halves", "q4_0_offset"};
+    "attn_no_mask", "attn_gqa", "attn_no_scale", "q4_0_halves", "q4_0_offset", "attn_max_floor"};
 
 int or_plant(void) { return QP_PLANT; }
 int or_plant_count(void) { return PLANT_COUNT; }
@@ -756,7 +757,11 @@ int or_attention(int kvtype, const float* q, int64_t ldq, const uint8_t* kc, con
         const int64_t last = n_past + tok[i];
 #endif
         const float* qi = q + tok[i] * ldq + h * head_dim;
+#if QP_PLANT == PLANT_ATTN_MAX_FLOOR
+        double mx = -1e30;
+#else
         double mx = -INFINITY;
+#endif
         for (int64_t r = 0; r <= last; ++r) {
           const float* kr = kf + (r * n_kv + g) * head_dim;
           double dot = 0.0;

@@ -41,6 +41,7 @@ SIGNATURES = {
     "qp_grouped_expert_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "qp_grouped_expert_gemm": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP, _VP,
                                       _SZ, _VP]),
+    "qp_grouped_expert_dropped_pairs": (_INT, [_VP, _VP, _VP]),
     "qp_prompt_attention": (_INT, [_INT, _VP, _I64, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _F32C, _VP, _I64, _VP]),
     "qp_status_string": (C.c_char_p, [_INT]),
     "qp_last_error_detail": (C.c_char_p, []),
@@ -109,10 +110,51 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
+def _gpu(*named):
+    """Raise unless every (tensor, name) is on the GPU (there is no CPU path)."""
+    for t, name in named:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_bytes(t, nbytes: int, name: str) -> None:
+    """Raise before any launch if tensor t holds fewer than nbytes bytes."""
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, the call reads or writes {nbytes}")
+
+
+def _need_dtype(t, dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _need_rows(t, rows: int, cols: int, name: str) -> None:
+    """A 2-D tensor with unit column stride covering rows x cols elements."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} is {tuple(t.shape)}, the call needs at least ({rows}, {cols})")
+
+
+def _weights_bytes(qtype: int, rows: int, cols: int) -> int:
+    rb = row_bytes(qtype, cols)
+    if rb < 0:
+        raise ValueError(f"type {qtype} has no block layout here")
+    return rows * rb
+
+
 def dequant_f32(qtype: int, w, rows: int, cols: int, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=w.device)
+    if qtype in _BLOCK_TYPES and rows > 0 and cols > 0:
+        _need_bytes(w, _weights_bytes(qtype, rows, cols), "w")
+        _need_dtype(out, torch.float32, "out")
+        _need_bytes(out, 4 * rows * cols, "out")
     check(lib().qp_dequant_f32(qtype, _dev(w, "w"), rows, cols, _dev(out, "out"), _stream()))
     return out
 
@@ -121,26 +163,57 @@ def dequant_f16(qtype: int, w, rows: int, cols: int, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float16, device=w.device)
+    if qtype in _BLOCK_TYPES and rows > 0 and cols > 0:
+        _need_bytes(w, _weights_bytes(qtype, rows, cols), "w")
+        if out.element_size() != 2:
+            raise TypeError("out must hold 2-byte elements (binary16 bit patterns)")
+        _need_bytes(out, 2 * rows * cols, "out")
     check(lib().qp_dequant_f16(qtype, _dev(w, "w"), rows, cols, _dev(out, "out"), _stream()))
     return out
 
 
+_BLOCK_TYPES = (F16W, Q8_0, Q2_K, Q4_K, Q5_K, Q6_K)
+
+# Cached workspaces, one per (device, stream): calls on one stream run in
+# order, so they may share a buffer; calls on two streams may overlap and
+# get one each.  A buffer replaced by a larger one is released by the
+# caching allocator only after the work already queued on its stream.
 _GEMM_WORKSPACE = {}
+_QKV_WORKSPACE = {}
 
 
-def gemm_workspace(n: int, k: int, t: int, device):
-    """Workspace for prefill_gemm's K split (None when it would not split),
-    kept per device and grown as needed."""
+def _workspace_key(device, stream: int):
+    return (_torch().device(device).index, int(stream or 0))
+
+
+def _cached_workspace(cache: dict, nbytes: int, device, stream=None):
     torch = _torch()
+    key = _workspace_key(device, _stream() if stream is None else stream)
+    ws = cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        cache[key] = ws
+    return ws
+
+
+def gemm_workspace(n: int, k: int, t: int, device, stream=None):
+    """Workspace for prefill_gemm's K split (None when it would not split),
+    kept per device and stream (the current one by default) and grown as
+    needed."""
     nbytes = lib().qp_prefill_gemm_workspace_bytes(n, k, t)
     if nbytes == 0:
         return None
-    key = torch.device(device).index
-    ws = _GEMM_WORKSPACE.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _GEMM_WORKSPACE[key] = ws
-    return ws
+    return _cached_workspace(_GEMM_WORKSPACE, nbytes, device, stream)
+
+
+def _check_gemm_args(qtype: int, w, n: int, k: int, x, t: int, out, out_name="out"):
+    torch = _torch()
+    if qtype in _BLOCK_TYPES and n > 0 and k > 0:
+        _need_bytes(w, _weights_bytes(qtype, n, k), "w")
+    if t > 0:
+        _need_rows(x, t, k, "x")
+        _need_dtype(out, torch.float32, out_name)
+        _need_rows(out, t, n, out_name)
 
 
 def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None, workspace=None):
@@ -155,11 +228,13 @@ def prefill_gemm(qtype: int, w, n: int, k: int, x, out=None, workspace=None):
         xd = F32
     else:
         raise TypeError("x must be float16 or float32")
-    if not x.is_cuda or x.stride(1) != 1:
-        raise ValueError("x must be a GPU tensor with unit column stride")
     if out is None:
         out = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    _check_gemm_args(qtype, w, n, k, x, t, out)
     ws = gemm_workspace(n, k, t, x.device) if workspace is None else (None if workspace is False else workspace)
+    if ws is not None:
+        _need_bytes(ws, lib().qp_prefill_gemm_workspace_bytes(n, k, t), "workspace")
+    _gpu((x, "x"), (out, "out"))
     check(lib().qp_prefill_gemm_ws(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0), out.data_ptr(),
                                    out.stride(0), _dev(ws, "workspace") if ws is not None else None,
                                    ws.numel() if ws is not None else 0, _stream()))
@@ -182,9 +257,9 @@ def prefill_gemm_noalloc(qtype: int, w, n: int, k: int, x, out):
         xd = F32
     else:
         raise TypeError("x must be float16 or float32")
-    if not x.is_cuda or x.stride(1) != 1 or not out.is_cuda or out.stride(1) != 1:
-        raise ValueError("x and out must be GPU tensors with unit column stride")
     t = x.shape[0]
+    _check_gemm_args(qtype, w, n, k, x, t, out)
+    _gpu((x, "x"), (out, "out"))
     check(lib().qp_prefill_gemm_noalloc(qtype, _dev(w, "w"), n, k, x.data_ptr(), xd, t, x.stride(0),
                                         out.data_ptr(), out.stride(0), _stream()))
     return out
@@ -195,13 +270,14 @@ def prefill_gemm_gate_up(qtype: int, w_gate, w_up, n: int, k: int, x, out_gate=N
     torch = _torch()
     if x.dtype != torch.float16:
         raise TypeError("x must be float16")
-    if not x.is_cuda or x.stride(1) != 1:
-        raise ValueError("x must be a GPU tensor with unit column stride")
     t = x.shape[0]
     if out_gate is None:
         out_gate = torch.empty((t, n), dtype=torch.float32, device=x.device)
     if out_up is None:
         out_up = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    _check_gemm_args(qtype, w_gate, n, k, x, t, out_gate, "out_gate")
+    _check_gemm_args(qtype, w_up, n, k, x, t, out_up, "out_up")
+    _gpu((x, "x"), (out_gate, "out_gate"), (out_up, "out_up"))
     check(lib().qp_prefill_gemm_gate_up(qtype, _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), n, k, x.data_ptr(), t,
                                         x.stride(0), out_gate.data_ptr(), out_gate.stride(0), out_up.data_ptr(),
                                         out_up.stride(0), _stream()))
@@ -213,30 +289,31 @@ def prefill_gemm_qknorm(qtype: int, w, n: int, k: int, x, head_dim: int, gain, g
     torch = _torch()
     if x.dtype != torch.float16:
         raise TypeError("x must be float16")
-    if not x.is_cuda or x.stride(1) != 1:
-        raise ValueError("x must be a GPU tensor with unit column stride")
     t = x.shape[0]
     if out is None:
         out = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    _check_gemm_args(qtype, w, n, k, x, t, out)
+    _check_gain(gain, n, head_dim, gain_head_stride, "gain")
+    _gpu((x, "x"), (out, "out"))
     check(lib().qp_prefill_gemm_qknorm(qtype, _dev(w, "w"), n, k, x.data_ptr(), t, x.stride(0), head_dim,
                                        _dev(gain, "gain"), gain_head_stride, float(eps), out.data_ptr(),
                                        out.stride(0), _stream()))
     return out
 
 
-_QKV_WORKSPACE = {}
-
-
-def qkv_workspace(n_q: int, n_k: int, n_v: int, t: int, device):
-    """Workspace for prefill_gemm_qkv, kept per device and grown as needed."""
+def _check_gain(gain, n: int, head_dim: int, stride: int, name: str) -> None:
+    """The f32 gains the norm reads: head h at h * stride, head_dim values."""
     torch = _torch()
+    if head_dim > 0 and n >= head_dim and stride >= 0:
+        _need_dtype(gain, torch.float32, name)
+        _need_bytes(gain, 4 * ((n // head_dim - 1) * stride + head_dim), name)
+
+
+def qkv_workspace(n_q: int, n_k: int, n_v: int, t: int, device, stream=None):
+    """Workspace for prefill_gemm_qkv, kept per device and stream (the current
+    one by default) and grown as needed."""
     nbytes = lib().qp_prefill_gemm_qkv_workspace_bytes(n_q, n_k, n_v, t)
-    key = torch.device(device).index
-    ws = _QKV_WORKSPACE.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _QKV_WORKSPACE[key] = ws
-    return ws
+    return _cached_workspace(_QKV_WORKSPACE, max(nbytes, 256), device, stream)
 
 
 def prefill_gemm_qkv(qtype: int, w_q, n_q: int, w_k, n_k: int, w_v, n_v: int, k: int, x, head_dim: int,
@@ -248,8 +325,6 @@ def prefill_gemm_qkv(qtype: int, w_q, n_q: int, w_k, n_k: int, w_v, n_v: int, k:
     torch = _torch()
     if x.dtype != torch.float16:
         raise TypeError("x must be float16")
-    if not x.is_cuda or x.stride(1) != 1:
-        raise ValueError("x must be a GPU tensor with unit column stride")
     t = x.shape[0]
     if workspace is None:
         ws = qkv_workspace(n_q, n_k, n_v, t, x.device)
@@ -258,6 +333,15 @@ def prefill_gemm_qkv(qtype: int, w_q, n_q: int, w_k, n_k: int, w_v, n_v: int, k:
     outs = []
     for o, n in ((out_q, n_q), (out_k, n_k), (out_v, n_v)):
         outs.append(o if o is not None else torch.empty((t, max(n, 1)), dtype=torch.float32, device=x.device))
+    _check_gemm_args(qtype, w_q, n_q, k, x, t, outs[0], "out_q")
+    _check_gemm_args(qtype, w_k, n_k, k, x, t, outs[1], "out_k")
+    if n_v:
+        _check_gemm_args(qtype, w_v, n_v, k, x, t, outs[2], "out_v")
+    _check_gain(gain_q, n_q, head_dim, gain_q_stride, "gain_q")
+    _check_gain(gain_k, n_k, head_dim, gain_k_stride, "gain_k")
+    if ws is not None:
+        _need_bytes(ws, lib().qp_prefill_gemm_qkv_workspace_bytes(n_q, n_k, n_v, t), "workspace")
+    _gpu((x, "x"), *((o, "out") for o in outs))
     check(lib().qp_prefill_gemm_qkv(qtype, _dev(w_q, "w_q"), n_q, _dev(w_k, "w_k"), n_k,
                                     _dev(w_v, "w_v") if n_v else None, n_v, k, x.data_ptr(), t, x.stride(0),
                                     head_dim, _dev(gain_q, "gain_q"), gain_q_stride, _dev(gain_k, "gain_k"),
@@ -275,6 +359,11 @@ def moe_route_topk(logits, top_k: int, renorm: bool = False, ids=None, weights=N
         ids = torch.empty((t, top_k), dtype=torch.int32, device=logits.device)
     if weights is None:
         weights = torch.empty((t, top_k), dtype=torch.float32, device=logits.device)
+    _need_dtype(logits, torch.float32, "logits")
+    _need_dtype(ids, torch.int32, "ids")
+    _need_dtype(weights, torch.float32, "weights")
+    _need_bytes(ids, 4 * t * top_k, "ids")
+    _need_bytes(weights, 4 * t * top_k, "weights")
     check(lib().qp_moe_route_topk(_dev(logits, "logits"), t, e, top_k, int(bool(renorm)), _dev(ids, "ids"),
                                   _dev(weights, "weights"), _stream()))
     return ids, weights
@@ -293,6 +382,18 @@ def grouped_expert_gemm(qtype: int, w_gate, w_up, w_down, n_experts: int, hidden
     nbytes = grouped_expert_workspace_bytes(t, top_k, n_experts, hidden, inter)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    if t > 0 and qtype in _BLOCK_TYPES:
+        _need_bytes(w_gate, n_experts * _weights_bytes(qtype, inter, hidden), "w_gate")
+        _need_bytes(w_up, n_experts * _weights_bytes(qtype, inter, hidden), "w_up")
+        _need_bytes(w_down, n_experts * _weights_bytes(qtype, hidden, inter), "w_down")
+        _need_dtype(x, torch.float16, "x")
+        _need_bytes(x, 2 * t * hidden, "x")
+        _need_dtype(ids, torch.int32, "ids")
+        _need_dtype(weights, torch.float32, "weights")
+        _need_bytes(weights, 4 * t * top_k, "weights")
+        _need_dtype(out, torch.float32, "out")
+        _need_bytes(out, 4 * t * hidden, "out")
+        _need_bytes(workspace, nbytes, "workspace")
     check(lib().qp_grouped_expert_gemm(qtype, _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"),
                                        n_experts, hidden, inter, _dev(x, "x"), t, top_k, _dev(ids, "ids"),
                                        _dev(weights, "weights"), _dev(out, "out"), _dev(workspace, "workspace"),
@@ -300,16 +401,34 @@ def grouped_expert_gemm(qtype: int, w_gate, w_up, w_down, n_experts: int, hidden
     return out
 
 
+def grouped_expert_dropped_pairs(workspace) -> int:
+    """Pairs the last grouped_expert_gemm call with this workspace dropped for
+    an expert id outside [0, n_experts) (synchronizes with the current stream)."""
+    torch = _torch()
+    cnt = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    check(lib().qp_grouped_expert_dropped_pairs(_dev(workspace, "workspace"), cnt.data_ptr(), _stream()))
+    return int(cnt.item())
+
+
 def prompt_attention(kv_type: int, q, k_cache, v_cache, n_past: int, n_head: int, n_kv_head: int,
                      head_dim: int = 128, scale: float | None = None, out=None):
     """Causal prompt attention of a chunk of q.shape[0] queries over a KV cache of
-    n_past + q.shape[0] tokens (flat byte tensors of binary16, Q8_0 or Q4_0 rows)."""
+    n_past + q.shape[0] tokens (flat byte tensors of binary16, Q8_0 or Q4_0 rows).
+    scale None takes the library's default, 1 / sqrt(head_dim)."""
     torch = _torch()
     t = q.shape[0]
     if scale is None:
-        scale = head_dim ** -0.5
+        scale = 0.0  # the library's default
     if out is None:
         out = torch.empty((t, n_head * head_dim), dtype=torch.float32, device=q.device)
+    if t > 0:
+        _need_dtype(q, torch.float32, "q")
+        _need_rows(q, t, n_head * head_dim, "q")
+        _need_dtype(out, torch.float32, "out")
+        _need_rows(out, t, n_head * head_dim, "out")
+        kv_bytes = (n_past + t) * n_kv_head * row_bytes(kv_type, head_dim) if row_bytes(kv_type, head_dim) > 0 else 0
+        _need_bytes(k_cache, kv_bytes, "k_cache")
+        _need_bytes(v_cache, kv_bytes, "v_cache")
     check(lib().qp_prompt_attention(kv_type, _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
                                     _dev(v_cache, "v_cache"), n_past, t, n_head, n_kv_head, head_dim, float(scale),
                                     _dev(out, "out"), out.stride(0), _stream()))

@@ -50,7 +50,7 @@ extern "C" {
 int64_t qp_block_size(int qtype) {
   switch (qtype) {
     case QP_F16W: return 1;
-    case QP_Q8_0: return 32;
+    case QP_Q8_0: case QP_Q4_0: return 32;
     case QP_Q4_K: case QP_Q5_K: case QP_Q6_K: case QP_Q2_K: return 256;
     default: return -1;
   }
@@ -60,6 +60,7 @@ int64_t qp_type_size(int qtype) {
   switch (qtype) {
     case QP_F16W: return 2;
     case QP_Q8_0: return 34;
+    case QP_Q4_0: return 18;
     case QP_Q4_K: return 144;
     case QP_Q5_K: return 176;
     case QP_Q6_K: return 210;
@@ -170,8 +171,8 @@ qp_status qp_prefill_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k,
                                  float eps, float* y, int64_t ldy, hipStream_t stream) {
   qp_status st = gemm_checks(qtype, w, n, k, x, t, ldx, 2, y, ldy);
   if (st != QP_OK) return st;
-  if (head_dim != 64 && head_dim != 128)
-    return fail(QP_ERR_INVALID_PARAMETER, "head_dim=%lld must be 64 or 128", (long long)head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(QP_ERR_INVALID_PARAMETER, "head_dim=%lld must be 64, 128 or 256", (long long)head_dim);
   if (n % head_dim != 0) return fail(QP_ERR_INVALID_PARAMETER, "n must be a multiple of head_dim");
   if (!(eps > 0.f) || !isfinite(eps)) return fail(QP_ERR_INVALID_PARAMETER, "eps must be finite and > 0");
   if (gain_head_stride < 0) return fail(QP_ERR_INVALID_PARAMETER, "gain_head_stride must be >= 0");
@@ -197,8 +198,8 @@ qp_status qp_prefill_gemm_qkv(int qtype, const void* w_q, int64_t n_q, const voi
     st = gemm_checks(qtype, w_v, n_v, k, x, t, ldx, 2, y_v, ldy_v);
     if (st != QP_OK) return st;
   }
-  if (head_dim != 64 && head_dim != 128)
-    return fail(QP_ERR_INVALID_PARAMETER, "head_dim=%lld must be 64 or 128", (long long)head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(QP_ERR_INVALID_PARAMETER, "head_dim=%lld must be 64, 128 or 256", (long long)head_dim);
   if (n_q % head_dim != 0 || n_k % head_dim != 0)
     return fail(QP_ERR_INVALID_PARAMETER, "n_q and n_k must be multiples of head_dim");
   if (!(eps > 0.f) || !isfinite(eps)) return fail(QP_ERR_INVALID_PARAMETER, "eps must be finite and > 0");
@@ -272,6 +273,14 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
                   "grouped expert launch");
 }
 
+qp_status qp_grouped_expert_dropped_pairs(const void* workspace, uint32_t* count, hipStream_t stream) {
+  if (!workspace || !count) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(workspace, 256) || !aligned(count, 4)) return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  return from_hip(hipMemcpyAsync(count, (const char*)workspace + QP_MOE_DROPPED_PAIRS_OFFSET, sizeof(uint32_t),
+                                 hipMemcpyDefault, stream),
+                  "dropped-pairs copy");
+}
+
 qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
                               int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
                               float scale, float* out, int64_t ldo, hipStream_t stream) {
@@ -289,6 +298,7 @@ qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const vo
     return fail(QP_ERR_INVALID_PARAMETER, "ldq=%lld ldo=%lld for %lld columns", (long long)ldq, (long long)ldo,
                 (long long)width);
   if (!std::isfinite(scale)) return fail(QP_ERR_INVALID_PARAMETER, "scale is not finite");
+  if (scale == 0.0f) scale = (float)(1.0 / std::sqrt((double)head_dim));
   if (t == 0) return ok();
   if (!q || !k_cache || !v_cache || !out) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
   const size_t cache_align = kv_type == QP_F16W ? 16 : 2;

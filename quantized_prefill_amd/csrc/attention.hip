@@ -208,7 +208,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int a = 0; a < 16; ++a) o[dt][a] = 0.0f;
-  float m_run = -1e30f;  // finite: a fully masked block leaves alpha = 1, p = 0
+  // -inf until the first block: every live query sees key 0 there, so the
+  // running maximum is finite from then on, whatever the (finite) scores
+  float m_run = -INFINITY;
   float l_part = 0.0f;   // this lane's share of the row sum (its 16 key rows per tile)
   const int qpos_lo = p.n_past + q0w;
   const int qpos = qpos_lo + r;
@@ -247,7 +249,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // a row with no visible key yet (m_new = -inf) subtracts 0 instead, so
+      // that exp2 sees -inf, never -inf - -inf
+      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
       l_part *= alpha;
       if (__any(m_new != m_run)) {  // the maximum moved for some query of the wave
 #pragma unroll
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + e] - m_new);
+          pv[e] = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + e] - m_sub);
           l_part += pv[e];
         }
         const u32x4 h = {pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),

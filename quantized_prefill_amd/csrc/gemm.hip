@@ -379,9 +379,47 @@ hipError_t launch_gemm_noalloc(int qtype, const void* w, int64_t n, int64_t k, c
                            (int64_t)(kNoAllocScratchBytes / sizeof(float)), s);
 }
 
+// Per-head RMSNorm of y in place, for heads wider than the 128-column tile
+// that the fused epilogue normalises within (head_dim 256): one wave per
+// (token, head), lane l holding columns l, l + 64, ...; the same products as
+// the epilogue (sum of squares, times 1 / head_dim, plus eps, v_rsq_f32, then
+// value * scale * gain).
+__global__ __launch_bounds__(256) void head_rmsnorm_kernel(float* __restrict__ y, int64_t ldy, int t, int n, int hd,
+                                                           const float* __restrict__ gain, int64_t gstride, float eps) {
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int heads = n / hd;
+  if (wid >= (int64_t)t * heads) return;
+  const int tok = (int)(wid / heads), h = (int)(wid - (int64_t)tok * heads);
+  const int lane = threadIdx.x & 63;
+  float* row = y + (int64_t)tok * ldy + (int64_t)h * hd;
+  const float* g = gain + (int64_t)h * gstride;
+  float v[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = lane + 64 * e < hd ? row[lane + 64 * e] : 0.f;
+    ss += v[e] * v[e];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  const float scale = __builtin_amdgcn_rsqf(ss * (1.f / (float)hd) + eps);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (lane + 64 * e < hd) row[lane + 64 * e] = v[e] * scale * g[lane + 64 * e];
+}
+
 hipError_t launch_gemm_qknorm(int qtype, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t t,
                               int64_t ldx, int64_t head_dim, const float* gain, int64_t gain_head_stride,
                               float eps, float* y, int64_t ldy, hipStream_t s) {
+  if (head_dim > 128) {
+    // the projection, then the norm over each head of the stored rows
+    hipError_t e = launch_gemm(qtype, w, n, k, x, false, t, ldx, y, ldy, s);
+    if (e != hipSuccess || t == 0) return e;
+    const int64_t waves = t * (n / head_dim);
+    hipLaunchKernelGGL(head_rmsnorm_kernel, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0, s, y, ldy, (int)t, (int)n,
+                       (int)head_dim, gain, gain_head_stride, eps);
+    return hipGetLastError();
+  }
   GemmParams p = {};
   p.w = (const uint8_t*)w;
   p.rb = row_bytes_of(qtype, k);
@@ -536,7 +574,7 @@ hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3]
   int64_t ntiles = 0;
   for (int i = 0; i < 3; ++i) ntiles += (n[i] + BN - 1) / BN;
   const int64_t mt = (t + 255) / 256;
-  const bool fused = t >= 512 && ntiles * mt >= 256 && tall_weights_ok(qtype, k) &&
+  const bool fused = head_dim <= 128 && t >= 512 && ntiles * mt >= 256 && tall_weights_ok(qtype, k) &&
                      tall_strides_ok(ldx, ldy[0]) &&
                      tall_strides_ok(ldx, ldy[1]) && (n[2] == 0 || tall_strides_ok(ldx, ldy[2]));
   if (!fused) {
@@ -705,24 +743,32 @@ hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t 
 // scan over its chunk counts; over experts, an exclusive scan of the totals;
 // then a stable scatter (rank among the earlier pairs of the chunk with the
 // same expert).  Each expert's list
-// is therefore in pair order.  Ids outside [0, n_experts) are dropped.
+// is therefore in pair order.  Ids outside [0, n_experts) are dropped and
+// counted: per chunk here, summed into the workspace header by the offsets
+// pass.
 constexpr int kMoeChunk = 256;
 
 __global__ __launch_bounds__(kMoeChunk) void moe_hist_kernel(const int32_t* __restrict__ ids, int npairs, int ne,
                                                              int nchunks, int* __restrict__ ccount,
-                                                             uint32_t* __restrict__ rowmax) {
+                                                             int* __restrict__ cbad, uint32_t* __restrict__ rowmax) {
   __shared__ int hist[1024];
+  __shared__ int bad;
   const int ch = blockIdx.x;
   for (int e = threadIdx.x; e < ne; e += kMoeChunk) hist[e] = 0;
+  if (threadIdx.x == 0) bad = 0;
   __syncthreads();
   const int i = ch * kMoeChunk + threadIdx.x;
   if (i < npairs) {
     const int e = ids[i];
-    if (e >= 0 && e < ne) atomicAdd(&hist[e], 1);
+    if (e >= 0 && e < ne)
+      atomicAdd(&hist[e], 1);
+    else
+      atomicAdd(&bad, 1);
     rowmax[i] = 0u;  // max |h| of compact row i, accumulated by the gate/up pass
   }
   __syncthreads();
   for (int e = threadIdx.x; e < ne; e += kMoeChunk) ccount[(int64_t)e * nchunks + ch] = hist[e];
+  if (threadIdx.x == 0) cbad[ch] = bad;
 }
 
 // Inclusive scan of v over the 1024 threads of a workgroup (wave shuffles,
@@ -766,11 +812,21 @@ __global__ __launch_bounds__(1024) void moe_escan_kernel(const int* __restrict__
 }
 
 // One workgroup: first compact row of each expert (exclusive scan of the
-// counts), the table of 128-row tiles per expert and the number of tiles.
+// counts), the table of 128-row tiles per expert and the number of tiles;
+// and the header's count of dropped pairs (the chunks' counts added in chunk
+// order).
 __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__ counts, int ne,
                                                          int* __restrict__ offsets, int* __restrict__ tiles,
-                                                         int* __restrict__ ntiles) {
+                                                         int* __restrict__ ntiles, const int* __restrict__ cbad,
+                                                         int nchunks, uint32_t* __restrict__ header) {
   __shared__ int wsum[16];
+  {
+    int nb = 0;
+    for (int j = threadIdx.x; j < nchunks; j += 1024) nb += cbad[j];
+    int tot;
+    block_scan_1024(nb, wsum, &tot);
+    if (threadIdx.x == 0) header[0] = (uint32_t)tot;
+  }
   const int e = threadIdx.x;
   const int c = e < ne ? counts[e] : 0;
   const int nt = (c + BM - 1) / BM;
@@ -836,7 +892,9 @@ bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t h
   ws.max_tiles = n_experts + (pairs + BM - 1) / BM;
   size_t o = 0;
   ws.nchunks = (pairs + kMoeChunk - 1) / kMoeChunk;
+  ws.header = o;  o += 256;  // uint32 [0]: pairs dropped for an id outside [0, n_experts)
   ws.ccount = o;  o += align256(sizeof(int) * n_experts * ws.nchunks);
+  ws.cbad = o;    o += align256(sizeof(int) * ws.nchunks);
   ws.cpref = o;   o += align256(sizeof(int) * n_experts * ws.nchunks);
   ws.counts = o;  o += align256(sizeof(int) * n_experts);
   ws.offsets = o; o += align256(sizeof(int) * n_experts);
@@ -867,16 +925,19 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
   hipError_t err;
 
   int* ccount = (int*)(wsb + ws.ccount);
+  int* cbad = (int*)(wsb + ws.cbad);
   int* cpref = (int*)(wsb + ws.cpref);
+  uint32_t* header = (uint32_t*)(wsb + ws.header);
   const int nch = (int)ws.nchunks;
   if (nch > 0) {
     hipLaunchKernelGGL(moe_hist_kernel, dim3((uint32_t)nch), dim3(kMoeChunk), 0, s, ids, npairs, (int)n_experts, nch,
-                       ccount, rowmax);
+                       ccount, cbad, rowmax);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(moe_escan_kernel, dim3((uint32_t)n_experts), dim3(1024), 0, s, ccount, nch, cpref, counts);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_oscan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles);
+  hipLaunchKernelGGL(moe_oscan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles, cbad,
+                     nch, header);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (nch > 0) {
     hipLaunchKernelGGL(moe_scatter_kernel, dim3((uint32_t)nch), dim3(kMoeChunk), 0, s, ids, npairs, (int)n_experts,

@@ -633,4 +633,22 @@ def pin_attention_two_keys_logistic(o):
     assert np.array_equal(one[0], v16[0, 0]), "single key"
 
 
+def pin_attention_huge_negative_scores(o):
+    """Every key equal and every scaled score about -1e31: the softmax is still
+    uniform, so query i returns the mean of value rows 0 .. n_past + i (a
+    running maximum started at a finite floor above the scores would lose
+    every weight)."""
+    n_past, t, hd = 2, 4, 32
+    kv = n_past + t
+    rng = np.random.default_rng(604)
+    v16 = rng.integers(-64, 64, size=(kv, 1, hd)) / 8.0
+    k16 = np.full((kv, 1, hd), -1.0)
+    q = np.full((t, hd), 100.0, np.float32)
+    scale = 1e31 / (100.0 * hd)
+    out = o.attention(F16W, q, _f16_cache(k16), _f16_cache(v16), n_past, 1, 1, hd, scale=scale)
+    for i in range(t):
+        want = v16[:n_past + i + 1, 0].mean(axis=0)
+        assert np.allclose(out[i], want, rtol=0, atol=1e-12), f"huge negative scores q{i}"
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

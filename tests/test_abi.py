@@ -38,7 +38,8 @@ def test_geometry():
                                                                                                84]
     assert qp.row_bytes(qp.Q6_K, 4173) == 17 * 210
     assert qp.row_bytes(qp.Q8_0, 33) == 2 * 34
-    assert qp.block_size(2) == -1 and qp.row_bytes(qp.Q4_K, 0) == -1
+    assert qp.block_size(3) == -1 and qp.row_bytes(qp.Q4_K, 0) == -1
+    assert qp.block_size(qp.Q4_0) == 32 and qp.type_size(qp.Q4_0) == 18 and qp.row_bytes(qp.Q4_0, 128) == 4 * 18
 
 
 def status_name(s):
@@ -77,6 +78,11 @@ def test_gemm_rejections():
     assert q(qp.Q4_K, FAKE, 192, 256, FAKE, 8, 256, 128, FAKE, 0, 1e-6, FAKE, 192, None) == 1  # n % hd
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, FAKE, 0, 0.0, FAKE, 256, None) == 1   # eps
     assert q(qp.Q4_K, FAKE, 256, 256, FAKE, 8, 256, 128, None, 0, 1e-6, FAKE, 256, None) == 1  # gain
+    # head_dim 256 is accepted (t == 0: validated, nothing to launch); 192 and 512 are not
+    assert q(qp.Q4_K, FAKE, 512, 256, FAKE, 0, 256, 256, FAKE, 256, 1e-6, FAKE, 512, None) == 0
+    assert q(qp.Q4_K, FAKE, 768, 256, FAKE, 8, 256, 192, FAKE, 0, 1e-6, FAKE, 768, None) == 1
+    assert q(qp.Q4_K, FAKE, 512, 256, FAKE, 8, 256, 512, FAKE, 0, 1e-6, FAKE, 512, None) == 1
+    assert q(qp.Q4_K, FAKE, 384, 256, FAKE, 8, 256, 256, FAKE, 0, 1e-6, FAKE, 384, None) == 1  # n % 256
     # the K-split variant: same checks, plus its workspace
     gw = L.qp_prefill_gemm_ws
     assert gw(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 8, 128, FAKE, 64, None, 0, None) == 1   # ldx < k
@@ -90,6 +96,12 @@ def test_gemm_rejections():
     good = [qp.Q4_K, FAKE, 256, FAKE, 128, FAKE, 128, 256, FAKE, 8, 256, 128, FAKE, 0, FAKE, 0, 1e-6,
             FAKE, 256, FAKE, 128, FAKE, 128, None, 0, None]
     assert f(*(good[:9] + [0] + good[10:])) == 0                  # t == 0: nothing to do
+    hd256 = list(good)
+    hd256[2], hd256[4], hd256[6], hd256[9], hd256[11] = 512, 256, 256, 0, 256
+    hd256[18], hd256[20], hd256[22] = 512, 256, 256
+    assert f(*hd256) == 0                                         # head_dim 256 accepted
+    hd256[4] = 128
+    assert f(*hd256) == 1                                         # n_k not a multiple of 256
     need = L.qp_prefill_gemm_qkv_workspace_bytes(256, 128, 128, 8)
     assert need == 2 * 8 * 256 * 4                                # partial sums of k and v, two halves
     assert L.qp_prefill_gemm_qkv_workspace_bytes(256, -1, 128, 8) == 0
@@ -121,6 +133,12 @@ def test_moe_rejections():
     bad = list(args)
     bad[0] = 3
     assert f(*bad, ws, None) == 2
+    # the dropped-pair reader: pointers checked before any copy is enqueued
+    d = L.qp_grouped_expert_dropped_pairs
+    assert d(None, FAKE, None) == 1
+    assert d(FAKE, None, None) == 1
+    assert d(FAKE + 16, FAKE, None) == 1      # workspace not 256-byte aligned
+    assert d(FAKE, FAKE + 2, None) == 1       # count not 4-byte aligned
 
 
 def test_attention_rejections():
@@ -149,6 +167,8 @@ def test_attention_rejections():
     assert call(ldq=4095) == 1          # below n_head * head_dim
     assert call(ldo=4098) == 1          # not a multiple of 4
     assert call(scale=float("inf")) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(scale=0.0, t=0, q=None, k=None, v=None, out=None) == 0   # 0: the default 1/sqrt(head_dim)
     assert call(t=0, q=None, k=None, v=None, out=None) == 0   # empty chunk: nothing to do
     assert call(q=None) == 1
     assert call(q=FAKE + 4) == 1        # q not 16-byte aligned

@@ -104,3 +104,26 @@ def test_attention_qwen3_8b_t2048(orc, kvtype):
     tok = sample_tokens(t, 24, 12803)
     ref = orc.attention(kvtype, q, kc, vc, 0, n_head, n_kv, HD, tokens=tok)
     assert_close(y[tok], ref, f"attention 8B {synth.NAMES[kvtype]}")
+
+
+def test_attention_default_scale_and_huge_negative_scores(orc):
+    """scale None takes the library's 1 / sqrt(head_dim), bit for bit the same
+    as passing that f32 value; with every key equal and scaled scores near
+    -1e31 the output is still the prefix mean of V (the running maximum
+    starts at -inf)."""
+    t, n_head, n_kv = 96, 4, 2
+    q = queries(t, n_head, 9900)
+    kc = synth.kv_cache(F16W, t, n_kv, HD, 9901)
+    vc = synth.kv_cache(F16W, t, n_kv, HD, 9902)
+    say("attention default scale")
+    a = run_attention(F16W, q, kc, vc, 0, n_head, n_kv)
+    b = run_attention(F16W, q, kc, vc, 0, n_head, n_kv, scale=float(np.float32(1.0 / np.sqrt(HD))))
+    assert np.array_equal(a, b), "default scale differs from 1/sqrt(head_dim)"
+    say("attention huge negative scores")
+    qn = np.full((t, n_head * HD), 100.0, np.float32)
+    kneg = np.full((t, n_kv, HD), -1.0, np.float16).view(np.uint8).reshape(-1)
+    scale = 1e31 / (100.0 * HD)
+    y = run_attention(F16W, qn, kneg, vc, 0, n_head, n_kv, scale=scale)
+    assert np.isfinite(y).all(), "non-finite outputs"
+    ref = orc.attention(F16W, qn, kneg, vc, 0, n_head, n_kv, HD, scale=scale)
+    assert_close(y, ref, "huge negative scores")

@@ -151,10 +151,10 @@ def run_qknorm(qtype, raw, n, k, x, hd, gain, gstride, eps):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("qtype", QTYPES, ids=[synth.NAMES[q] for q in QTYPES])
 def test_qknorm_small(orc, qtype, hd):
-    t, n, k = 77, 384, 512
+    t, n, k = 77, (512 if hd == 256 else 384), 512
     raw = weights(qtype, n, k, 8400 + hd)
     x = act_f16(t, k, 8401)
     for gstride, gn in ((0, hd), (hd, n)):
@@ -300,6 +300,30 @@ def test_qkv_ragged(orc, qtype):
     c = check_qkv(orc, qtype, ws, ns, k, x, 128, gains, [0, 128], None, f"qkv whole {synth.NAMES[qtype]}",
                   workspace=False)
     assert np.array_equal(a[0], c[0]), "q differs between the split and the whole launch"
+
+
+@pytest.mark.parametrize("qtype", [Q4_K, Q6_K], ids=["Q4_K", "Q6_K"])
+def test_qknorm_head_dim_256(orc, qtype):
+    """Heads of 256 columns (the projection, then the norm over each stored
+    head): a ragged T on the 256-token tiles with per-head gains, every row
+    against the oracle and every head unit-RMS up to its gains; then q/k/v in
+    one call with head_dim 256 (three separate launches)."""
+    t, n, k, hd = 777, 8192, 512, 256
+    raw = weights(qtype, n, k, 8900)
+    x = act_f16(t, k, 8901)
+    gain = synth.gains(n, 8902)
+    say(f"qknorm hd=256 {synth.NAMES[qtype]} t={t} n={n}")
+    y = run_qknorm(qtype, raw, n, k, x, hd, gain, hd, 1e-6)
+    ref = orc.prefill_gemm_qknorm(qtype, raw, n, k, x, hd, gain, hd, 1e-6)
+    assert_close(y, ref, f"qknorm hd=256 {synth.NAMES[qtype]}")
+    hn = (y / gain[None, :]).reshape(t, n // hd, hd)
+    ms = (hn.astype(np.float64) ** 2).mean(axis=2)
+    assert np.allclose(ms, 1.0, atol=2e-3), f"head mean squares off: {ms.min()} {ms.max()}"
+    ns = [2048, 512, 512]
+    ws = [weights(qtype, nn, k, 8910 + i) for i, nn in enumerate(ns)]
+    gains = [synth.gains(hd, 8920), synth.gains(ns[1], 8921)]
+    say(f"qkv hd=256 {synth.NAMES[qtype]}")
+    check_qkv(orc, qtype, ws, ns, k, x, hd, gains, [0, hd], None, f"qkv hd=256 {synth.NAMES[qtype]}")
 
 
 def test_qkv_small_falls_back(orc):

@@ -31,12 +31,19 @@ def test_router(orc, t, e, k):
     assert np.allclose(w, rw, rtol=2e-6, atol=1e-9)
 
 
-def run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts):
+def run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts, dropped=None):
+    """The routed FFN's output; with dropped=<expected count>, also checks the
+    workspace header's count of pairs dropped for an out-of-range id."""
     import torch
+    t, top_k = ids.shape
+    ws = torch.empty(qp.grouped_expert_workspace_bytes(t, top_k, ne, hidden, inter), dtype=torch.uint8, device="cuda")
     out = qp.grouped_expert_gemm(qtype, to_dev(wg), to_dev(wu), to_dev(wd), ne, hidden, inter,
                                  to_dev(x).view(torch.float16), to_dev(ids.astype(np.int32)),
-                                 to_dev(wts.astype(np.float32)))
+                                 to_dev(wts.astype(np.float32)), workspace=ws)
     torch.cuda.synchronize()
+    if dropped is not None:
+        got = qp.grouped_expert_dropped_pairs(ws)
+        assert got == dropped, f"dropped-pair count {got}, want {dropped}"
     return out.cpu().numpy()
 
 
@@ -52,7 +59,7 @@ def test_moe_small(orc, qtype):
     lg = synth.router_logits(t, ne, 9604)
     lg[:, 5] -= 100.0  # expert 5 never chosen
     ids, wts = orc.route_topk(lg, k)
-    y = run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts)
+    y = run_moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts, dropped=0)
     ref = orc.moe(qtype, wg, wu, wd, ne, hidden, inter, x, ids, wts)
     assert_close(y, ref, f"moe small {synth.NAMES[qtype]}")
 
@@ -91,8 +98,8 @@ def test_moe_invalid_ids_and_determinism(orc):
     bad = ids.copy()
     bad[::3, 1] = ne + 5
     bad[1::7, 0] = -1
-    y = run_moe(Q4_K, wg, wu, wd, ne, hidden, inter, x, bad, wts)
     keep = (bad >= 0) & (bad < ne)
+    y = run_moe(Q4_K, wg, wu, wd, ne, hidden, inter, x, bad, wts, dropped=int((~keep).sum()))
     ref = orc.moe(Q4_K, wg, wu, wd, ne, hidden, inter, x, np.where(keep, bad, 0), np.where(keep, wts, 0.0))
     rows = np.flatnonzero(np.abs(ref).sum(axis=1) > 0)
     assert_close(y[rows], ref[rows], "moe with dropped pairs")
