@@ -76,6 +76,10 @@ class Oracle:
         L.or_moe.restype = i32
         L.or_attention.argtypes = [i32, vp, i64, vp, vp, i64, i64, i64, i64, i64, dbl, vp, i64, vp]
         L.or_attention.restype = i32
+        L.or_rope.argtypes = [vp, i64, i64, i64, i64, i64, dbl]
+        L.or_rope.restype = i32
+        L.or_kv_quantize.argtypes = [i32, vp, i64, i64, i64, i64, vp]
+        L.or_kv_quantize.restype = i32
         L.or_plant.restype = i32
         L.or_plant_count.restype = i32
         L.or_plant_name.argtypes = [i32]
@@ -222,6 +226,33 @@ class Oracle:
                                   float(scale), _p(tok), tok.size, _p(out))
         if rc != 0:
             raise ValueError("oracle attention rejected its arguments")
+        return out
+
+    # -- rotary step and KV cache rows --------------------------------------
+    def rope(self, x: np.ndarray, n_head: int, head_dim: int, pos0: int, base: float) -> np.ndarray:
+        """float32 copy of x [T, >= n_head*head_dim] with each head of row i
+        rotated to position pos0 + i (half-split pairs, binary64 angles)."""
+        y = np.array(x, dtype=np.float32, order="C", copy=True)
+        if y.ndim != 2:
+            raise ValueError("x must be 2-D")
+        rc = self._L.or_rope(_p(y), y.shape[1], y.shape[0], n_head, head_dim, pos0, float(base))
+        if rc != 0:
+            raise ValueError("oracle rope rejected its arguments")
+        return y
+
+    def kv_quantize(self, kvtype: int, src: np.ndarray, n_kv: int, head_dim: int) -> np.ndarray:
+        """Cache rows (flat uint8, token-major then kv head) of src [T, >= n_kv*head_dim] f32."""
+        x = np.ascontiguousarray(src, dtype=np.float32)
+        if x.ndim != 2:
+            raise ValueError("src must be 2-D")
+        t = x.shape[0]
+        rb = self.row_bytes(kvtype, head_dim)
+        if rb <= 0:
+            raise ValueError("unsupported cache type")
+        out = np.zeros(t * n_kv * rb, dtype=np.uint8)
+        rc = self._L.or_kv_quantize(kvtype, _p(x), x.shape[1], t, n_kv, head_dim, _p(out))
+        if rc != 0:
+            raise ValueError("oracle kv_quantize rejected its arguments")
         return out
 
 

@@ -17,11 +17,13 @@
  *     "What changes": the batched prefill is a chunk of prompt tokens against
  *     each projection, FP16, for models with a per-head QK norm.
  *   - "CUDA prefill VRAM loans and SM75 Q4/native-IQ opt-ins" (Strata PR),
- *     sections "Summary" and "Correctness and safety": routed experts run as a
- *     fused prefill path whose routing ids, expert selection, route weights
- *     and scatter order are those of the unfused path.  Section "Summary"
- *     and the table after it: prompt attention runs over a KV cache held
- *     quantized (Q4_0 or INT8 per row), as a tensor-core path of its own.
+ *     sections "Summary" and "Correctness and safety": the routed experts get
+ *     a fused prefill path that chooses and weighs the same experts, and adds
+ *     their outputs in the same order, as the unfused path.  Section
+ *     "Summary" and the table after it: prompt attention runs over a KV cache
+ *     held quantized (Q4_0 or INT8 per row), as a tensor-core path of its own;
+ *     the K and V rows of the chunk are written into that cache first, K
+ *     after its QK norm and a rotary position step.
  * The pages name the block types but do not print their bit layouts; the
  * layouts below are the GGUF/ggml on-disk convention, restated as formulas.
  *
@@ -87,7 +89,13 @@
 #define PLANT_Q4_0_HALVES      30  /* Q4_0: values 0..15 from high nibbles, 16..31 from low */
 #define PLANT_Q4_0_OFFSET      31  /* Q4_0 quant without the -8 */
 #define PLANT_ATTN_MAX_FLOOR   32  /* softmax maximum taken from a finite floor of -1e30 */
-#define PLANT_COUNT            33
+#define PLANT_ROPE_ADJACENT    33  /* RoPE pairs values 2j and 2j+1 instead of j and j + head_dim/2 */
+#define PLANT_ROPE_FREQ        34  /* RoPE frequency base^(-j/head_dim) instead of base^(-2j/head_dim) */
+#define PLANT_ROPE_SIGN        35  /* RoPE rotates the other way */
+#define PLANT_KV_Q8_TRUNC      36  /* Q8_0 cache codes truncated instead of rounded */
+#define PLANT_KV_Q4_ABSMAX     37  /* Q4_0 cache scale from |max| / 8 instead of max / -8 */
+#define PLANT_KV_Q8_F16_D      38  /* Q8_0 cache codes from the binary16-rounded scale */
+#define PLANT_COUNT            39
 
 static const char* const plant_names[PLANT_COUNT] = {
     "none", "q8_unsigned", "q6_no_offset", "q6_no_high", "q4_scale_high",
@@ -95,7 +103,8 @@ static const char* const plant_names[PLANT_COUNT] = {
     "q2_nibbles", "q4_nibble", "q6_shift", "gemm_transpose", "gemm_drop_k",
     "qkn_sum", "qkn_eps", "qkn_gain", "silu_sign", "moe_weight", "router_tie",
     "router_renorm", "moe_up", "q5_no_high", "q5_high_bit", "f16w_bytes",
-    "attn_no_mask", "attn_gqa", "attn_no_scale", "q4_0_halves", "q4_0_offset", "attn_max_floor"};
+    "attn_no_mask", "attn_gqa", "attn_no_scale", "q4_0_halves", "q4_0_offset", "attn_max_floor",
+    "rope_adjacent", "rope_freq", "rope_sign", "kv_q8_trunc", "kv_q4_absmax", "kv_q8_f16_d"};
 
 int or_plant(void) { return QP_PLANT; }
 int or_plant_count(void) { return PLANT_COUNT; }
@@ -784,5 +793,142 @@ int or_attention(int kvtype, const float* q, int64_t ldq, const uint8_t* kc, con
   }
   free(kf);
   free(vf);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rotary position step and KV cache rows                                     */
+
+/* Rotary position embedding, in place, of t rows of n_head heads of head_dim
+ * f32 values (row stride ldx), row i at position pos0 + i.  Reading: the
+ * pages name a rotary step after the QK norm but print no formula; this is
+ * the rotation of the published rotary embedding in its half-split pairing
+ * (the one Qwen3 models use): for j < head_dim / 2, values j and
+ * j + head_dim / 2 of a head form a pair turned by the angle
+ * (pos0 + i) * base^(-2j / head_dim).  Angle, cosine, sine and the two
+ * products are binary64; each result is rounded to f32 once. */
+int or_rope(float* x, int64_t ldx, int64_t t, int64_t n_head, int64_t head_dim, int64_t pos0, double base) {
+  if (t < 0 || n_head <= 0 || head_dim <= 0 || head_dim % 2 != 0 || ldx < n_head * head_dim || pos0 < 0 ||
+      !(base > 0.0))
+    return -1;
+  const int64_t half = head_dim / 2;
+  for (int64_t i = 0; i < t; ++i) {
+    const double pos = (double)(pos0 + i);
+    for (int64_t h = 0; h < n_head; ++h) {
+      float* v = x + i * ldx + h * head_dim;
+      for (int64_t j = 0; j < half; ++j) {
+#if QP_PLANT == PLANT_ROPE_FREQ
+        const double theta = pos * pow(base, -(double)j / (double)head_dim);
+#else
+        const double theta = pos * pow(base, -2.0 * (double)j / (double)head_dim);
+#endif
+        const double c = cos(theta), sn = sin(theta);
+#if QP_PLANT == PLANT_ROPE_ADJACENT
+        const int64_t ia = 2 * j, ib = 2 * j + 1;
+#else
+        const int64_t ia = j, ib = j + half;
+#endif
+        const double a = (double)v[ia], b = (double)v[ib];
+#if QP_PLANT == PLANT_ROPE_SIGN
+        v[ia] = (float)(a * c + b * sn);
+        v[ib] = (float)(b * c - a * sn);
+#else
+        v[ia] = (float)(a * c - b * sn);
+        v[ib] = (float)(a * sn + b * c);
+#endif
+      }
+    }
+  }
+  return 0;
+}
+
+static void put_half(uint8_t* p, uint16_t h) {
+  p[0] = (uint8_t)(h & 0xFF);
+  p[1] = (uint8_t)(h >> 8);
+}
+
+/* Q8_0 block of 32 f32 values.  Reading (the pages name an INT8 cache but
+ * print no quantizer): the GGUF reference rounding, in binary32: the scale
+ * d = amax / 127 for amax the largest |x|, each code the nearest integer of
+ * x * (1/d), halves away from zero (0 when d = 0); the block stores the
+ * nearest-even binary16 of d, while the codes come from the f32 d. */
+static void q8_0_block(const float* x, uint8_t* b) {
+  float amax = 0.0f;
+  for (int j = 0; j < 32; ++j) {
+    const float a = fabsf(x[j]);
+    if (a > amax) amax = a;
+  }
+  const float d = amax / 127.0f;
+#if QP_PLANT == PLANT_KV_Q8_F16_D
+  const float dq = or_half_to_float(or_float_to_half(d));
+  const float id = dq != 0.0f ? 1.0f / dq : 0.0f;
+#else
+  const float id = d != 0.0f ? 1.0f / d : 0.0f;
+#endif
+  put_half(b, or_float_to_half(d));
+  for (int j = 0; j < 32; ++j) {
+    const float v = x[j] * id;
+#if QP_PLANT == PLANT_KV_Q8_TRUNC
+    b[2 + j] = (uint8_t)(int8_t)(int)v;
+#else
+    b[2 + j] = (uint8_t)(int8_t)(int)roundf(v);
+#endif
+  }
+}
+
+/* Q4_0 block of 32 f32 values.  Reading, as for Q8_0, the GGUF reference
+ * rounding in binary32: m is the first value of largest magnitude, d = m / -8,
+ * each code the integer part of x * (1/d) + 8.5 (the product rounded before
+ * the sum), at most 15 (0 when d = 0 gives code 8); codes of values 0..15 go
+ * to the low nibbles of bytes 2..17, values 16..31 to the high nibbles. */
+static void q4_0_block(const float* x, uint8_t* b) {
+  float amax = 0.0f, m = 0.0f;
+  for (int j = 0; j < 32; ++j) {
+    if (fabsf(x[j]) > amax) {
+      amax = fabsf(x[j]);
+      m = x[j];
+    }
+  }
+#if QP_PLANT == PLANT_KV_Q4_ABSMAX
+  const float d = amax / 8.0f;
+#else
+  const float d = m / -8.0f;
+#endif
+  const float id = d != 0.0f ? 1.0f / d : 0.0f;
+  put_half(b, or_float_to_half(d));
+  int q[32];
+  for (int j = 0; j < 32; ++j) {
+    const float p = x[j] * id;
+    const float v = p + 8.5f;
+    int c = (int)v;
+    q[j] = c > 15 ? 15 : c;
+  }
+  for (int j = 0; j < 16; ++j) b[2 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+}
+
+/* The cache rows of t tokens: token i, kv head g of src (row stride lds,
+ * head g at column g * head_dim) becomes cache row i * n_kv + g, in kvtype
+ * (F16: the nearest-even binary16 of each value; Q8_0 and Q4_0 as above),
+ * rows back to back in dst. */
+int or_kv_quantize(int kvtype, const float* src, int64_t lds, int64_t t, int64_t n_kv, int64_t head_dim,
+                   uint8_t* dst) {
+  if ((kvtype != OR_F16 && kvtype != OR_Q8_0 && kvtype != OR_Q4_0) || t < 0 || n_kv <= 0 || head_dim <= 0 ||
+      head_dim % 32 != 0 || lds < n_kv * head_dim)
+    return -1;
+  const int64_t rb = or_row_bytes(kvtype, head_dim);
+  for (int64_t i = 0; i < t; ++i)
+    for (int64_t g = 0; g < n_kv; ++g) {
+      const float* x = src + i * lds + g * head_dim;
+      uint8_t* row = dst + (i * n_kv + g) * rb;
+      for (int64_t c = 0; c < head_dim; c += 32) {
+        if (kvtype == OR_F16) {
+          for (int j = 0; j < 32; ++j) put_half(row + 2 * (c + j), or_float_to_half(x[c + j]));
+        } else if (kvtype == OR_Q8_0) {
+          q8_0_block(x + c, row + (c / 32) * 34);
+        } else {
+          q4_0_block(x + c, row + (c / 32) * 18);
+        }
+      }
+    }
   return 0;
 }

@@ -651,4 +651,110 @@ def pin_attention_huge_negative_scores(o):
         assert np.allclose(out[i], want, rtol=0, atol=1e-12), f"huge negative scores q{i}"
 
 
+# Rotary step.  Values of cos and sin below are constants of the functions
+# (to 16 digits), not calls of a library.
+def pin_rope_identity_norms_compose(o):
+    """Position 0 is the identity (bit for bit); every half-split pair keeps
+    its length; turning by a then by b equals turning by a + b."""
+    rng = np.random.default_rng(701)
+    n_head, hd = 3, 64
+    x = rng.standard_normal((5, n_head * hd + 4)).astype(np.float32)  # 4 spare columns: stride > heads
+    y = o.rope(x, n_head, hd, 0, 1e6)
+    assert np.array_equal(y[0], x[0]), "position 0 moved"
+    assert np.array_equal(y[:, -4:], x[:, -4:]), "columns past the heads changed"
+    y = o.rope(x, n_head, hd, 1000, 1e6)
+    xa, ya = x[:, :n_head * hd].reshape(5, n_head, 2, hd // 2), y[:, :n_head * hd].reshape(5, n_head, 2, hd // 2)
+    nx = np.hypot(xa[:, :, 0].astype(np.float64), xa[:, :, 1])
+    ny = np.hypot(ya[:, :, 0].astype(np.float64), ya[:, :, 1])
+    assert np.allclose(ny, nx, rtol=1e-6, atol=1e-7), "pair lengths changed"
+    a = o.rope(o.rope(x[:1], n_head, hd, 37, 1e6), n_head, hd, 1200, 1e6)
+    b = o.rope(x[:1], n_head, hd, 1237, 1e6)
+    assert np.allclose(a, b, rtol=1e-5, atol=1e-5), "rotations do not compose"
+
+
+def pin_rope_closed_form(o):
+    """head_dim 4, base 10^4: pair 0 (values 0 and 2) turns by 1 rad per
+    position, pair 1 (values 1 and 3) by 10^4^(-1/2) = 0.01 rad.  At position
+    50 the unit vectors go to (cos 50, sin 50) and (cos 0.5, sin 0.5)."""
+    cos50, sin50 = 0.9649660284921133, -0.26237485370392877
+    cos05, sin05 = 0.8775825618903728, 0.479425538604203
+    x = np.zeros((1, 4), np.float32)
+    x[0, 0] = 1.0
+    y = o.rope(x, 1, 4, 50, 1e4)[0]
+    assert np.allclose(y, [cos50, 0.0, sin50, 0.0], rtol=0, atol=1e-7), f"pair 0 {y}"
+    x = np.zeros((1, 4), np.float32)
+    x[0, 1] = 1.0
+    y = o.rope(x, 1, 4, 50, 1e4)[0]
+    assert np.allclose(y, [0.0, cos05, 0.0, sin05], rtol=0, atol=1e-7), f"pair 1 {y}"
+    # the second token of a chunk sits one position further
+    x = np.zeros((2, 4), np.float32)
+    x[:, 1] = 1.0
+    y = o.rope(x, 1, 4, 49, 1e4)
+    assert np.allclose(y[1], [0.0, cos05, 0.0, sin05], rtol=0, atol=1e-7), "row 1 not at pos0 + 1"
+
+
+# KV cache rows: hand-worked blocks and exact round trips.
+def pin_kv_q8_0_hand_rows(o):
+    """amax 63.5 gives d = 0.5 and codes x * 2 rounded half away from zero;
+    amax 1 gives d = 1/127 (binary16 0x2008 stored) and 0.79131 * 127 =
+    100.496 -> 100 from the f32 d (the binary16 d would give 100.50 -> 101)."""
+    x = np.zeros(32, np.float32)
+    x[:8] = [63.5, -63.5, 1.25, -1.25, 0.75, -0.75, 0.24, 0.26]
+    b = o.kv_quantize(Q8_0, x[None, :], 1, 32)
+    want = np.zeros(34, np.uint8)
+    want[0], want[1] = 0x00, 0x38
+    want[2:10] = np.array([127, -127, 3, -3, 2, -2, 0, 1], np.int8).view(np.uint8)
+    assert np.array_equal(b, want), f"Q8_0 row {b[:10]}"
+    x = np.zeros(32, np.float32)
+    x[:2] = [1.0, 0.79131]
+    b = o.kv_quantize(Q8_0, x[None, :], 1, 32)
+    assert (b[0], b[1]) == (0x08, 0x20), "d of amax 1"
+    assert list(b[2:4].view(np.int8)) == [127, 100], f"codes {b[2:4].view(np.int8)}"
+
+
+def pin_kv_q4_0_hand_rows(o):
+    """First value of largest magnitude -8: d = 1, code = int(x + 8.5), at most
+    15; first such value +8: d = -1, code = int(8.5 - x).  Values 0..15 in
+    the low nibbles, 16..31 in the high nibbles."""
+    x = np.zeros(32, np.float32)
+    x[:9] = [-8.0, 8.0, 7.0, 7.9, 0.5, -0.5, 0.49, 3.2, -2.6]
+    x[16:18] = [-3.0, 6.5]
+    b = o.kv_quantize(Q4_0, x[None, :], 1, 32)
+    assert (b[0], b[1]) == (0x00, 0x3C), "d = 1"
+    low = [0, 15, 15, 15, 9, 8, 8, 11, 5] + [8] * 7
+    high = [5, 15] + [8] * 14
+    assert list(b[2:18] & 0x0F) == low, f"low nibbles {list(b[2:18] & 0x0F)}"
+    assert list(b[2:18] >> 4) == high, f"high nibbles {list(b[2:18] >> 4)}"
+    x = np.zeros(32, np.float32)
+    x[:4] = [8.0, -8.0, 7.0, 0.25]
+    b = o.kv_quantize(Q4_0, x[None, :], 1, 32)
+    assert (b[0], b[1]) == (0x00, 0xBC), "d = -1"
+    assert list(b[2:6] & 0x0F) == [0, 15, 1, 8], f"low nibbles {list(b[2:6] & 0x0F)}"
+
+
+def pin_kv_round_trips(o):
+    """Values the formats hold exactly come back exactly through the cache:
+    Q8_0 multiples of 1/8 with a largest |code| of 127; Q4_0 values d (c - 8)
+    whose first largest magnitude is -8 d; binary16 values through F16."""
+    rng = np.random.default_rng(702)
+    t, n_kv, hd = 3, 2, 64
+    k = rng.integers(-127, 128, size=(t, n_kv * hd))
+    k[:, ::32] = 127
+    x = (k / 8.0).astype(np.float32)
+    back = o.dequant_f32(Q8_0, o.kv_quantize(Q8_0, x, n_kv, hd), t * n_kv, hd).reshape(t, n_kv * hd)
+    assert np.array_equal(back, x), "Q8_0 round trip"
+    c = rng.integers(0, 16, size=(t, n_kv * hd))
+    c[:, ::32] = 0
+    x = ((c - 8) * 0.375).astype(np.float32)
+    back = o.dequant_f32(Q4_0, o.kv_quantize(Q4_0, x, n_kv, hd), t * n_kv, hd).reshape(t, n_kv * hd)
+    assert np.array_equal(back, x), "Q4_0 round trip"
+    x = rng.standard_normal((t, n_kv * hd)).astype(np.float16).astype(np.float32)
+    back = o.dequant_f32(F16W, o.kv_quantize(F16W, x, n_kv, hd), t * n_kv, hd).reshape(t, n_kv * hd)
+    assert np.array_equal(back, x), "F16 round trip"
+    # rows are token-major, then kv head: head 1 of token 2 is cache row 5
+    rows = o.kv_quantize(Q8_0, (k / 8.0).astype(np.float32), n_kv, hd).reshape(t * n_kv, -1)
+    one = o.kv_quantize(Q8_0, (k[2:3, hd:] / 8.0).astype(np.float32), 1, hd)
+    assert np.array_equal(rows[5], one), "row order"
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
