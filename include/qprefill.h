@@ -330,6 +330,52 @@ qp_status qp_grouped_expert_gemm(int qtype, const void* w_gate, const void* w_up
 qp_status qp_grouped_expert_dropped_pairs(const void* workspace, uint32_t* count, hipStream_t stream);
 
 /*
+ * Rotary position step on the QK-normed Q or K rows of a chunk, in place
+ * (the Strata PR's "Summary": prompt attention over the chunk's Q and K; the
+ * pages print no rotary formula, so this is the published rotary embedding in
+ * its half-split pairing, the form Qwen3 models use):  for row i (position
+ * pos0 + i), head h and j < head_dim / 2, the values a = x[i, h*hd + j] and
+ * b = x[i, h*hd + j + hd/2] become
+ *   a cos(th) - b sin(th),  a sin(th) + b cos(th),   th = (pos0 + i) * base^(-2j / head_dim)
+ * with the angle, cosine, sine and products in binary64 and each result
+ * rounded to f32 once.
+ *   x (device): t rows of f32, row stride ldx (>= n_head * head_dim), 4-byte
+ *               aligned; columns past n_head * head_dim are not touched.
+ *   base: the rotary base (1e6 for Qwen3), finite and > 1.
+ * Requires head_dim even and <= 1024, n_head <= 4096, 0 <= pos0 <= 2^40.
+ * t == 0 is a no-op.  Errors: QP_ERR_INVALID_PARAMETER.
+ */
+qp_status qp_rope(float* x, int64_t ldx, int64_t t, int64_t n_head, int64_t head_dim, int64_t pos0, double base,
+                  hipStream_t stream);
+
+/*
+ * Writes the K or V rows of a chunk into a KV cache held as binary16, Q8_0
+ * ("INT8") or Q4_0 rows (the Strata PR's "Summary" and the KV table after
+ * it): token i, kv head g of src becomes cache row (row0 + i) * n_kv_head + g
+ * (row0 = n_past: the cache layout qp_prompt_attention reads).  The pages
+ * print no quantizer; each 32 values are stored with the GGUF reference
+ * rounding, in binary32:
+ *   QP_Q8_0: d = amax / 127, code = x * (1 / d) rounded half away from zero;
+ *   QP_Q4_0: d = m / -8 for m the first value of largest magnitude,
+ *            code = min(15, trunc(x * (1 / d) + 8.5)) (the product rounded
+ *            first), values 16..31 in the high nibbles;
+ *   QP_F16W: the nearest-even binary16 of each value;
+ * the codes come from the f32 d (0 when d = 0), the block stores the
+ * nearest-even binary16 of d.
+ *   src (device): t rows of f32 (the k or v projection's output, k after its
+ *                 norm and qp_rope), row stride lds (>= n_kv_head * head_dim,
+ *                 a multiple of 4), 16-byte aligned.
+ *   cache (device): at least (row0 + t) * n_kv_head * qp_row_bytes(kv_type,
+ *                 head_dim) bytes, 2-byte aligned (4 for binary16); only the
+ *                 chunk's rows are written.
+ * Requires head_dim a multiple of 32 and <= 1024, n_kv_head <= 4096, row0 >= 0.
+ * t == 0 is a no-op.  Errors: QP_ERR_UNSUPPORTED_TYPE for another kv_type,
+ * QP_ERR_INVALID_PARAMETER otherwise.
+ */
+qp_status qp_kv_cache_write(int kv_type, const float* src, int64_t lds, int64_t t, int64_t n_kv_head,
+                            int64_t head_dim, void* cache, int64_t row0, hipStream_t stream);
+
+/*
  * Causal prompt attention of one prefill chunk over a KV cache held as
  * binary16, Q8_0 or Q4_0 rows ("CUDA prefill VRAM loans and SM75 Q4/native-IQ
  * opt-ins", section "Summary" and the KV table after it: prompt attention as

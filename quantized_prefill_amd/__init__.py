@@ -42,6 +42,8 @@ SIGNATURES = {
     "qp_grouped_expert_gemm": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP, _VP,
                                       _SZ, _VP]),
     "qp_grouped_expert_dropped_pairs": (_INT, [_VP, _VP, _VP]),
+    "qp_rope": (_INT, [_VP, _I64, _I64, _I64, _I64, _I64, C.c_double, _VP]),
+    "qp_kv_cache_write": (_INT, [_INT, _VP, _I64, _I64, _I64, _I64, _VP, _I64, _VP]),
     "qp_prompt_attention": (_INT, [_INT, _VP, _I64, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _F32C, _VP, _I64, _VP]),
     "qp_status_string": (C.c_char_p, [_INT]),
     "qp_last_error_detail": (C.c_char_p, []),
@@ -408,6 +410,34 @@ def grouped_expert_dropped_pairs(workspace) -> int:
     cnt = torch.zeros(1, dtype=torch.int32, device=workspace.device)
     check(lib().qp_grouped_expert_dropped_pairs(_dev(workspace, "workspace"), cnt.data_ptr(), _stream()))
     return int(cnt.item())
+
+
+def rope(x, n_head: int, head_dim: int, pos0: int, base: float = 1e6):
+    """Rotary step, in place, on x [T, >= n_head*head_dim] float32 (row i at
+    position pos0 + i); returns x."""
+    torch = _torch()
+    t = x.shape[0]
+    _need_dtype(x, torch.float32, "x")
+    _need_rows(x, t, n_head * head_dim, "x")
+    _gpu((x, "x"))
+    check(lib().qp_rope(x.data_ptr(), x.stride(0), t, n_head, head_dim, pos0, float(base), _stream()))
+    return x
+
+
+def kv_cache_write(kv_type: int, src, n_kv_head: int, head_dim: int, cache, row0: int):
+    """Write src [T, >= n_kv_head*head_dim] float32 (K or V rows of a chunk)
+    into cache (flat uint8) at token rows row0 .. row0 + T - 1."""
+    torch = _torch()
+    t = src.shape[0]
+    _need_dtype(src, torch.float32, "src")
+    _need_rows(src, t, n_kv_head * head_dim, "src")
+    rb = row_bytes(kv_type, head_dim)
+    if t > 0 and rb > 0:
+        _need_bytes(cache, (row0 + t) * n_kv_head * rb, "cache")
+    _gpu((src, "src"), (cache, "cache"))
+    check(lib().qp_kv_cache_write(kv_type, src.data_ptr(), src.stride(0), t, n_kv_head, head_dim, cache.data_ptr(),
+                                  row0, _stream()))
+    return cache
 
 
 def prompt_attention(kv_type: int, q, k_cache, v_cache, n_past: int, n_head: int, n_kv_head: int,

@@ -281,6 +281,40 @@ qp_status qp_grouped_expert_dropped_pairs(const void* workspace, uint32_t* count
                   "dropped-pairs copy");
 }
 
+qp_status qp_rope(float* x, int64_t ldx, int64_t t, int64_t n_head, int64_t head_dim, int64_t pos0, double base,
+                  hipStream_t stream) {
+  if (t < 0 || t > kMaxDim || n_head < 1 || n_head > 4096 || head_dim < 2 || head_dim > 1024 || head_dim % 2 != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "t=%lld n_head=%lld head_dim=%lld out of range", (long long)t,
+                (long long)n_head, (long long)head_dim);
+  if (ldx < n_head * head_dim) return fail(QP_ERR_INVALID_PARAMETER, "ldx=%lld below n_head * head_dim", (long long)ldx);
+  if (pos0 < 0 || pos0 > ((int64_t)1 << 40)) return fail(QP_ERR_INVALID_PARAMETER, "pos0=%lld", (long long)pos0);
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(QP_ERR_INVALID_PARAMETER, "base must be finite and > 1");
+  if (t == 0) return ok();
+  if (!x) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(x, 4)) return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  return from_hip(qp::launch_rope(x, ldx, t, n_head, head_dim, pos0, base, stream), "rope launch");
+}
+
+qp_status qp_kv_cache_write(int kv_type, const float* src, int64_t lds, int64_t t, int64_t n_kv_head,
+                            int64_t head_dim, void* cache, int64_t row0, hipStream_t stream) {
+  if (kv_type != QP_F16W && kv_type != QP_Q8_0 && kv_type != QP_Q4_0)
+    return fail(QP_ERR_UNSUPPORTED_TYPE, "no KV cache rows of ggml type %d", kv_type);
+  if (t < 0 || t > kMaxDim || n_kv_head < 1 || n_kv_head > 4096 || head_dim < 32 || head_dim > 1024 ||
+      head_dim % 32 != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "t=%lld n_kv_head=%lld head_dim=%lld out of range", (long long)t,
+                (long long)n_kv_head, (long long)head_dim);
+  if (lds < n_kv_head * head_dim || lds % 4 != 0)
+    return fail(QP_ERR_INVALID_PARAMETER, "lds=%lld: at least n_kv_head * head_dim and a multiple of 4",
+                (long long)lds);
+  if (row0 < 0 || row0 + t > kMaxDim) return fail(QP_ERR_INVALID_PARAMETER, "row0=%lld out of range", (long long)row0);
+  if (t == 0) return ok();
+  if (!src || !cache) return fail(QP_ERR_INVALID_PARAMETER, "null pointer");
+  if (!aligned(src, 16) || !aligned(cache, kv_type == QP_F16W ? 4 : 2))
+    return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  return from_hip(qp::launch_kv_write(kv_type, src, lds, t, n_kv_head, head_dim, cache, row0, stream),
+                  "kv write launch");
+}
+
 qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
                               int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
                               float scale, float* out, int64_t ldo, hipStream_t stream) {

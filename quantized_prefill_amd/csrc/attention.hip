@@ -27,7 +27,6 @@
 namespace qp {
 namespace {
 
-constexpr int kQ4_0 = 2;             // ggml type id; a KV cache format here, not a weight type
 constexpr int kD = 128;              // head dim
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;     // queries per workgroup

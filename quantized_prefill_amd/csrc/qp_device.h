@@ -27,7 +27,8 @@
 
 namespace qp {
 
-constexpr int kF16 = 1, kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14;
+// ggml type ids (Q4_0 is a KV cache format here, not a weight type)
+constexpr int kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ2_K = 10, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14;
 
 template <int QT> struct Fmt;
 // F16 weights (one binary16 per weight) are handled by the GEMM kernels as

@@ -60,6 +60,13 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
                                  int64_t top_k, const int32_t* ids, const float* weights, float* out,
                                  void* workspace, const MoeWorkspace& ws, hipStream_t s);
 
+// Rotary step in place (half-split pairs) and the write of K / V rows into a
+// binary16, Q8_0 or Q4_0 KV cache at cache rows (row0 + i) * n_kv + g.
+hipError_t launch_rope(float* x, int64_t ldx, int64_t t, int64_t n_head, int64_t head_dim, int64_t pos0, double base,
+                       hipStream_t s);
+hipError_t launch_kv_write(int kv_type, const float* src, int64_t lds, int64_t t, int64_t n_kv, int64_t head_dim,
+                           void* cache, int64_t row0, hipStream_t s);
+
 // Causal prompt attention over a binary16 or Q8_0 KV cache, head_dim 128.
 int64_t attention_row_bytes(int kv_type);
 hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,

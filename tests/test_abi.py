@@ -186,3 +186,29 @@ def test_noalloc_rejections():
     assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 256, FAKE, 7, 8, 256, FAKE, 64, None) == 1
     assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 256, FAKE + 8, qp.F16, 8, 256, FAKE, 64, None) == 1
     assert L.qp_prefill_gemm_noalloc(qp.Q4_K, FAKE, 64, 256, FAKE, qp.F16, 0, 256, FAKE, 64, None) == 0
+
+
+def test_rope_and_kv_write_rejections():
+    L = qp.lib()
+    r = L.qp_rope
+    # x, ldx, t, n_head, head_dim, pos0, base, stream
+    assert r(FAKE, 4096, 8, 32, 127, 0, 1e6, None) == 1           # odd head_dim
+    assert r(FAKE, 4095, 8, 32, 128, 0, 1e6, None) == 1           # ldx below the heads
+    assert r(FAKE, 4096, 8, 32, 128, -1, 1e6, None) == 1          # negative position
+    assert r(FAKE, 4096, 8, 32, 128, 0, 1.0, None) == 1           # base not > 1
+    assert r(FAKE, 4096, 8, 32, 128, 0, float("inf"), None) == 1
+    assert r(None, 4096, 8, 32, 128, 0, 1e6, None) == 1
+    assert r(FAKE + 2, 4096, 8, 32, 128, 0, 1e6, None) == 1       # not 4-byte aligned
+    assert r(None, 4096, 0, 32, 128, 0, 1e6, None) == 0           # t == 0: nothing to do
+    w = L.qp_kv_cache_write
+    # kv_type, src, lds, t, n_kv, head_dim, cache, row0, stream
+    assert w(qp.Q4_K, FAKE, 1024, 8, 8, 128, FAKE, 0, None) == 2  # not a cache format
+    assert w(qp.Q8_0, FAKE, 1024, 8, 8, 96 + 8, FAKE, 0, None) == 1   # head_dim % 32
+    assert w(qp.Q8_0, FAKE, 1020, 8, 8, 128, FAKE, 0, None) == 1  # lds below the heads
+    assert w(qp.Q8_0, FAKE, 1026, 8, 8, 128, FAKE, 0, None) == 1  # lds not a multiple of 4
+    assert w(qp.Q8_0, FAKE, 1024, 8, 8, 128, FAKE, -1, None) == 1
+    assert w(qp.Q8_0, FAKE + 4, 1024, 8, 8, 128, FAKE, 0, None) == 1  # src not 16-byte aligned
+    assert w(qp.Q8_0, FAKE, 1024, 8, 8, 128, FAKE + 1, 0, None) == 1  # cache on an odd byte
+    assert w(qp.F16W, FAKE, 1024, 8, 8, 128, FAKE + 2, 0, None) == 1  # binary16 cache needs 4 bytes
+    assert w(qp.Q4_0, None, 1024, 0, 8, 128, None, 0, None) == 0  # t == 0
+
