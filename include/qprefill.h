@@ -145,7 +145,10 @@ qp_status qp_prefill_gemm(int qtype, const void* w, int64_t n, int64_t k, const 
  * Where the 128-token tile's launch has fewer tiles than the GPU has compute
  * units, K is split into 2, 4 or 8 parts of whole 256-weight blocks; each
  * part writes its partial sums into the workspace and one more pass adds
- * them in part order into y.  The result is the same on every call with the
+ * them in part order into y.  Likewise, for Q2_K weights, K >= 8192 and
+ * exactly half a round of 256 x 256 tiles, the two K halves run in one
+ * launch of that tile, the second half's sums go to the workspace and one
+ * pass adds them into y.  The result is the same on every call with the
  * same inputs and matches qp_prefill_gemm within the GEMM tolerance (the
  * summation order differs).  Calls that share a workspace must not run
  * concurrently.  Errors: those of qp_prefill_gemm, and
@@ -155,9 +158,10 @@ qp_status qp_prefill_gemm_ws(int qtype, const void* w, int64_t n, int64_t k, con
                              int64_t t, int64_t ldx, float* y, int64_t ldy, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of the workspace qp_prefill_gemm_ws uses for these sizes on the
- * current device (parts * t * n floats, rounded up to 256); 0 when it would
- * not split, or for sizes out of range (the shape-dependent split of the
+/* Bytes of the workspace qp_prefill_gemm_ws may use for these sizes on the
+ * current device, whatever the weight type (parts * t * n floats for the
+ * 128-token split, t * n for the K halves, rounded up to 256); 0 when no
+ * split applies, or for sizes out of range (the shape-dependent split of the
  * Strata PR's "Summary", as for qp_prefill_gemm_ws). */
 size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t);
 

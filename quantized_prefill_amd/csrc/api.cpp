@@ -151,8 +151,9 @@ qp_status qp_prefill_gemm_noalloc(int qtype, const void* w, int64_t n, int64_t k
 size_t qp_prefill_gemm_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   if (n <= 0 || k <= 0 || t < 0 || n > kMaxDim || k > kMaxDim || t > kMaxDim) return 0;
   const int parts = qp::gemm_ksplit_parts(n, k, t);
-  if (parts <= 1) return 0;
-  return (size_t)((parts * t * n * 4 + 255) / 256 * 256);
+  int64_t floats = parts > 1 ? parts * t * n : 0;
+  if (qp::wide_halves_shape(n, k, t) && t * n > floats) floats = t * n;  // the 256 x 256 tile's second K half
+  return (size_t)((floats * 4 + 255) / 256 * 256);
 }
 
 qp_status qp_prefill_gemm_gate_up(int qtype, const void* w_gate, const void* w_up, int64_t n, int64_t k,

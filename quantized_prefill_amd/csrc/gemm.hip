@@ -260,6 +260,24 @@ static bool use_wide_tiles(int qtype, int mode, int64_t n, int64_t t, int64_t ld
   return wide_fills(cols * ((t + 255) / 256));
 }
 
+// y[r, c] = y[r, c] + part[r, c] (part dense, row stride n): the second K
+// half added to the first.  One thread per 4 columns of a row.
+__global__ __launch_bounds__(256) void add_partial_kernel(const float* __restrict__ part, float* __restrict__ y,
+                                                          int64_t ldy, int t, int n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = (n + 3) / 4;
+  if (i >= (int64_t)t * q) return;
+  const int r = (int)(i / q), c = 4 * (int)(i - (int64_t)r * q);
+  float* yr = y + (int64_t)r * ldy;
+  const float* pr = part + (int64_t)r * n;
+  if (c + 4 <= n && ldy % 4 == 0 && n % 4 == 0) {
+    const float4v a = *(const float4v*)(yr + c), b = *(const float4v*)(pr + c);
+    *(float4v*)(yr + c) = a + b;
+  } else {
+    for (int e = c; e < n && e < c + 4; ++e) yr[e] = yr[e] + pr[e];
+  }
+}
+
 // Sum of a plain projection's K parts, in part order:
 // y[r, c] = (..((p_0 + p_1) + p_2) ..) + p_{S-1}, partials dense (row stride n)
 // and part_stride floats apart.  One thread per 4 columns of a row.
@@ -283,6 +301,17 @@ __global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict
 // K parts for a plain 128-tile launch that leaves the GPU under-filled: the
 // smallest power of two (at most 8) that gives one workgroup per CU, with
 // parts of whole 256-weight blocks.  1: no split.
+// The 256 x 256-tile kernel in two K halves: for a launch of exactly half a
+// round of those tiles (the 8B layer's down at T = 2048: 128 tiles), each
+// half runs as one segment of one launch, a full round together; half 0
+// writes y, half 1 dense partial sums, and one pass adds them in that order.
+// The partial sums fill t * n floats, at most 128 tiles of 256 x 256 on a
+// 256-CU GPU: 32 MiB.  (Taken for Q2_K weights and K >= 8192; see below.)
+bool wide_halves_shape(int64_t n, int64_t k, int64_t t) {
+  const int64_t tiles = ((n + 255) / 256) * ((t + 255) / 256);
+  return k % 512 == 0 && k >= 8192 && 2 * tiles == cu_count();
+}
+
 int gemm_ksplit_parts(int64_t n, int64_t k, int64_t t) {
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
   const int cus = cu_count();
@@ -311,6 +340,36 @@ hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, con
   p.ldy = ldy;
   p.vec_store = ldy % 4 == 0;
   if (!x_f32 && use_wide_tiles(qtype, kPlainF16, n, t, ldx, ldy)) return launch_gemm_wide(qtype, kPlainF16, 8, p, s);
+  // Launches of half a round of 256 x 256 tiles (the 8B o and down at
+  // T = 2048): measured per type, the producer-wave tall kernel below is the
+  // fastest for Q6_K, Q4_K and Q5_K, whose decode it keeps off the MFMA
+  // waves; Q2_K's cheap decode favours the wide kernel, in two K halves for
+  // long K (down: 197 against 208 us) and with 128-token tiles otherwise (o:
+  // 77 against 82 us).
+  const bool q2_half_round = !x_f32 && qtype == kQ2_K && tall_strides_ok(ldx, ldy) &&
+                             !wide_fills(((n + 255) / 256) * ((t + 255) / 256));
+  if (q2_half_round && wide_halves_shape(n, k, t) && k >= 8192 && partial != nullptr && t * n <= partial_floats) {
+    const int64_t cols = (n + wide_cols() - 1) / wide_cols();
+    const int64_t kh = k / 2;
+    p.seg.nseg = 2;
+    for (int i = 0; i < 2; ++i) {
+      p.seg.tile0[i] = (int)(i * cols);
+      p.seg.w[i] = (const uint8_t*)w + i * row_bytes_of(qtype, kh);  // whole blocks: kh % 256 == 0
+      p.seg.n[i] = (int)n;
+      p.seg.k[i] = (int)kh;
+      p.seg.xoff[i] = i * kh;
+      p.seg.y[i] = i == 0 ? y : partial;
+      p.seg.ldy[i] = i == 0 ? ldy : n;
+    }
+    for (int i = 2; i <= kMaxSeg; ++i) p.seg.tile0[i] = (int)(2 * cols);
+    hipError_t e = launch_gemm_wide(qtype, kMulti, 8, p, s);
+    if (e != hipSuccess) return e;
+    const int64_t threads = t * ((n + 3) / 4);
+    hipLaunchKernelGGL(add_partial_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, s, partial, y, ldy,
+                       (int)t, (int)n);
+    return hipGetLastError();
+  }
+  if (q2_half_round && wide_fills(((n + 255) / 256) * ((t + 127) / 128))) return launch_gemm_wide(qtype, kPlainF16, 4, p, s);
   if (!x_f32 && use_tall_tiles(qtype, n, k, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);

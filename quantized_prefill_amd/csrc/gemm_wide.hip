@@ -600,6 +600,8 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     tile_x -= pk.seg.tile0[sg];
     p.w = pk.seg.w[sg];
     p.n = pk.seg.n[sg];
+    p.k = pk.seg.k[sg];  // a K part: its weights start at seg.w, its activations xoff into each row
+    p.x = (const _Float16*)pk.x + pk.seg.xoff[sg];
     p.y = pk.seg.y[sg];
     p.ldy = pk.seg.ldy[sg];
   }

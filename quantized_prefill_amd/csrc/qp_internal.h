@@ -19,6 +19,7 @@ hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, con
                              int64_t ldx, float* y, int64_t ldy, float* partial, int64_t partial_floats,
                              hipStream_t s);
 int gemm_ksplit_parts(int64_t n, int64_t k, int64_t t);
+bool wide_halves_shape(int64_t n, int64_t k, int64_t t);
 // launch_gemm_split with the library's static device scratch as the room for
 // partial sums (kNoAllocScratchBytes; no allocation, no caller workspace).
 constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;

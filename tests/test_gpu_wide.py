@@ -104,3 +104,33 @@ def test_plain_wide_dispatch(orc, qtype):
     tok = tile_rows(t, 256, 16, 9952)
     assert_close(y[tok], orc.prefill_gemm(qtype, raw, n, k, x, tokens=tok), f"plain wide {synth.NAMES[qtype]}")
     weights.cache_clear()
+
+
+@pytest.mark.parametrize("t,n,k", [(2048, 4096, 12288), (2000, 4000, 8192), (2048, 4096, 4096), (2000, 4000, 4096)],
+                         ids=["down-halves", "ragged-halves", "o-128-token-tiles", "ragged-128-token-tiles"])
+def test_wide_half_round_q2_k(orc, t, n, k):
+    """Q2_K launches of half a round of 256 x 256 tiles: with K >= 8192 and a
+    workspace, two K halves in one launch plus an in-order add; otherwise the
+    wide kernel with 128-token tiles.  Against the oracle on every 256-token
+    tile's first and last row, against the call without workspace within the
+    tolerance, the same bits on two calls, and the allocation-free call bit
+    for bit equal to the workspace call."""
+    import torch
+    qtype = Q2_K
+    say(f"Q2_K half round t={t} n={n} k={k}")
+    raw = weights(qtype, n, k, 9700 + k // 256)
+    x = act_f16(t, k, 9701)
+    w, xt = to_dev(raw), to_dev(x).view(torch.float16)
+    if k >= 8192:
+        assert qp.lib().qp_prefill_gemm_workspace_bytes(n, k, t) >= 4 * t * n
+    a = qp.prefill_gemm(qtype, w, n, k, xt).cpu().numpy()
+    b = qp.prefill_gemm(qtype, w, n, k, xt).cpu().numpy()
+    assert np.array_equal(a, b), "two calls differ"
+    tok = tile_rows(t, 256, 8, 9702)
+    assert_close(a[tok], orc.prefill_gemm(qtype, raw, n, k, x, tokens=tok), f"Q2_K half round k={k}")
+    whole = qp.prefill_gemm(qtype, w, n, k, xt, workspace=False).cpu().numpy()
+    assert_close(a, whole.astype(np.float64), "against the call without workspace")
+    out = torch.empty((t, n), dtype=torch.float32, device="cuda")
+    qp.prefill_gemm_noalloc(qtype, w, n, k, xt, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), a), "allocation-free call differs from the workspace call"
