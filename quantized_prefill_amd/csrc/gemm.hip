@@ -876,7 +876,8 @@ __global__ __launch_bounds__(1024) void moe_escan_kernel(const int* __restrict__
 // order).
 __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__ counts, int ne,
                                                          int* __restrict__ offsets, int* __restrict__ tiles,
-                                                         int* __restrict__ ntiles, const int* __restrict__ cbad,
+                                                         int* __restrict__ ntiles, int* __restrict__ tiles2,
+                                                         int* __restrict__ ntiles2, const int* __restrict__ cbad,
                                                          int nchunks, uint32_t* __restrict__ header) {
   __shared__ int wsum[16];
   {
@@ -889,8 +890,10 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
   const int e = threadIdx.x;
   const int c = e < ne ? counts[e] : 0;
   const int nt = (c + BM - 1) / BM;
-  int tot;
-  const int cin = block_scan_1024(c, wsum, &tot);
+  const int nt2 = (c + 255) / 256;  // tiles of the 256-row kernel
+  int tot, tot2, rows_tot;
+  const int cin = block_scan_1024(c, wsum, &rows_tot);
+  const int tin2 = block_scan_1024(nt2, wsum, &tot2);
   const int tin = block_scan_1024(nt, wsum, &tot);
   if (e < ne) {
     offsets[e] = cin - c;
@@ -899,8 +902,17 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
       tiles[2 * (t0 + k)] = e;
       tiles[2 * (t0 + k) + 1] = k * BM;
     }
+    const int u0 = tin2 - nt2;
+    for (int k = 0; k < nt2; ++k) {
+      tiles2[2 * (u0 + k)] = e;
+      tiles2[2 * (u0 + k) + 1] = k * 256;
+    }
   }
-  if (e == 0) *ntiles = tot;
+  if (e == 0) {
+    ntiles[0] = tot;
+    ntiles[1] = rows_tot;  // compact rows in all lists
+    *ntiles2 = tot2;
+  }
 }
 
 // Stable scatter: pair i of chunk j with expert e goes to compact row
@@ -942,6 +954,83 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   *(float4v*)(out + (int64_t)tok * hidden + 4 * c4) = acc;
 }
 
+// Between the two passes of the 256-row kernel: per compact row, h =
+// SiLU(g) * u = g / (1 + exp(-g)) * u (the same f32 products as the 128-row
+// kernel's epilogue), the row's largest |h| (bits into pairmax at the row's
+// pair), and h times
+// the power of two that brings that maximum into [2^14, 2^15), rounded to
+// binary16 (the down pass's A rows).  One wave per row; lane l holds columns
+// 4 (l + 64 j) .. + 3, read and written 16 / 8 bytes at a time (inter is a
+// multiple of 256, so of 4).
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+template <int NJ>
+__global__ __launch_bounds__(256) void moe_silu_kernel(const float* __restrict__ g, const float* __restrict__ u,
+                                                       const int* __restrict__ nrows, const int* __restrict__ list,
+                                                       int inter, uint32_t* __restrict__ pairmax,
+                                                       _Float16* __restrict__ h16) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= *nrows) return;
+  const float* gr = g + (int64_t)row * inter;
+  const float* ur = u + (int64_t)row * inter;
+  float4v h[NJ];
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = 4 * (lane + 64 * j);
+    if (c < inter) {
+      const float4v gv = *(const float4v*)(gr + c), uv = *(const float4v*)(ur + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[j][e] = gv[e] / (1.f + __expf(-gv[e])) * uv[e];
+        mx = __builtin_fmaxf(mx, __builtin_fabsf(h[j][e]));
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, 64));
+  const uint32_t bits = __builtin_bit_cast(uint32_t, mx);
+  const float sc = row_scale_from_max(bits, false);
+  if (lane == 0) pairmax[list[row]] = bits;  // by pair: the combine reads a token's slots in order
+  _Float16* hr = h16 + (int64_t)row * inter;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = 4 * (lane + 64 * j);
+    if (c < inter) {
+      const uint32_t lo = pack_f16x2(h[j][0] * sc, h[j][1] * sc), hi = pack_f16x2(h[j][2] * sc, h[j][3] * sc);
+      *(uint2v*)(hr + c) = (uint2v){lo, hi};
+    }
+  }
+}
+
+// out[t, :] = sum over slots s (in order) of weights[t, s] * inverse scale *
+// the down pass's row of pair t * top_k + s; pairs with an id outside
+// [0, n_experts) add nothing.  The factor is the product the 128-row
+// kernel's down epilogue applies, in the same order.  One thread per float4
+// of out: a token's slot rows are consecutive rows of dbuf.
+__global__ __launch_bounds__(256) void moe_combine_rows_kernel(const float* __restrict__ dbuf,
+                                                               const int32_t* __restrict__ ids,
+                                                               const uint32_t* __restrict__ pairmax,
+                                                               const float* __restrict__ weights, int t, int top_k,
+                                                               int ne, int hidden, float* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nq = (int64_t)t * hidden / 4;
+  if (q >= nq) return;
+  const int tok = (int)(q / (hidden / 4));
+  const int c4 = (int)(q - (int64_t)tok * (hidden / 4));
+  float4v acc = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < top_k; ++s) {
+    const int64_t pair = (int64_t)tok * top_k + s;
+    const int id = ids[pair];
+    if (id < 0 || id >= ne) continue;
+    const float f = row_scale_from_max(pairmax[pair], true) * weights[pair];
+    const float4v v = *(const float4v*)(dbuf + pair * hidden + 4 * c4);
+    acc += v * f;
+  }
+  *(float4v*)(out + (int64_t)tok * hidden + 4 * c4) = acc;
+}
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden, int64_t inter,
@@ -957,11 +1046,16 @@ bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t h
   ws.cpref = o;   o += align256(sizeof(int) * n_experts * ws.nchunks);
   ws.counts = o;  o += align256(sizeof(int) * n_experts);
   ws.offsets = o; o += align256(sizeof(int) * n_experts);
+  ws.max_tiles2 = n_experts + (pairs + 255) / 256;
   ws.ntiles = o;  o += align256(sizeof(int) * 4);
   ws.tiles = o;   o += align256(sizeof(int) * 2 * ws.max_tiles);
+  ws.ntiles2 = o; o += align256(sizeof(int) * 4);
+  ws.tiles2 = o;  o += align256(sizeof(int) * 2 * ws.max_tiles2);
   ws.list = o;    o += align256(sizeof(int) * pairs);
   ws.rowmax = o;  o += align256(sizeof(uint32_t) * pairs);
-  ws.hbuf = o;    o += align256(sizeof(float) * pairs * inter);
+  ws.hbuf = o;    o += align256(sizeof(float) * pairs * inter);    // h (128-row kernel) or g (256-row kernel)
+  ws.ubuf = o;    o += align256(sizeof(float) * pairs * inter);    // u (256-row kernel)
+  ws.h16 = o;     o += align256(sizeof(uint16_t) * pairs * inter); // scaled binary16 h (256-row kernel)
   ws.dbuf = o;    o += align256(sizeof(float) * pairs * hidden);
   ws.total = o;
   return true;
@@ -995,13 +1089,90 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
   }
   hipLaunchKernelGGL(moe_escan_kernel, dim3((uint32_t)n_experts), dim3(1024), 0, s, ccount, nch, cpref, counts);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_oscan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles, cbad,
-                     nch, header);
+  int* ntiles2 = (int*)(wsb + ws.ntiles2);
+  int* tiles2 = (int*)(wsb + ws.tiles2);
+  // the 256-row kernel (the K-quant weight types) or the 128-row kernel
+  const bool wide = wide_supported(qtype, kGrouped) && tall_strides_ok(hidden, inter) && tall_strides_ok(inter, hidden) &&
+                    t * hidden * 2 < ((int64_t)1 << 31) &&  // gathered X rows: 32-bit byte offsets from x
+                    inter <= 4096;                          // the SiLU pass holds a row in registers
+  hipLaunchKernelGGL(moe_oscan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles,
+                     tiles2, ntiles2, cbad, nch, header);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (nch > 0) {
     hipLaunchKernelGGL(moe_scatter_kernel, dim3((uint32_t)nch), dim3(kMoeChunk), 0, s, ids, npairs, (int)n_experts,
                        nch, offsets, cpref, list);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (wide) {
+    // gate and up: the tokens of each 256-row tile gathered through the list,
+    // g and u into two f32 arrays of compact rows
+    float* gbuf = (float*)(wsb + ws.hbuf);
+    float* ubuf = (float*)(wsb + ws.ubuf);
+    _Float16* h16 = (_Float16*)(wsb + ws.h16);
+    const int64_t icols = (inter + 255) / 256, hcols = (hidden + 255) / 256;
+    GemmParams p = {};
+    p.tiles = tiles2;
+    p.ntiles = ntiles2;
+    p.offsets = offsets;
+    p.counts = counts;
+    p.list = list;
+    p.top_k = (int)top_k;
+    p.gather = 1;
+    p.x = x;
+    p.ldx = hidden;
+    p.k = (int)hidden;
+    p.rb = row_bytes_of(qtype, hidden);
+    p.estride = p.rb * inter;
+    p.t = (int)ws.max_tiles2;
+    p.seg.nseg = 2;
+    const uint8_t* wgu[2] = {(const uint8_t*)w_gate, (const uint8_t*)w_up};
+    float* ygu[2] = {gbuf, ubuf};
+    for (int i = 0; i < 2; ++i) {
+      p.seg.tile0[i] = (int)(i * icols);
+      p.seg.w[i] = wgu[i];
+      p.seg.n[i] = (int)inter;
+      p.seg.k[i] = (int)hidden;
+      p.seg.y[i] = ygu[i];
+      p.seg.ldy[i] = inter;
+    }
+    for (int i = 2; i <= kMaxSeg; ++i) p.seg.tile0[i] = (int)(2 * icols);
+    if ((err = launch_gemm_wide(qtype, kGrouped, 8, p, s)) != hipSuccess) return err;
+    {
+      const dim3 g((uint32_t)((npairs + 3) / 4));
+      if (inter <= 1024)
+        hipLaunchKernelGGL(moe_silu_kernel<4>, g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, rowmax,
+                           h16);
+      else if (inter <= 2048)
+        hipLaunchKernelGGL(moe_silu_kernel<8>, g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, rowmax,
+                           h16);
+      else
+        hipLaunchKernelGGL(moe_silu_kernel<16>, g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, rowmax,
+                           h16);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    // down: A = the binary16 h rows of each tile (compact rows, contiguous),
+    // the raw products into dbuf's rows in pair order (row r of a tile goes
+    // to pair list[r]), which the combine reads per token
+    GemmParams d = p;
+    d.gather = 0;  // d.list stays: the epilogue stores row r of a tile at pair list[base + r]
+    d.x = h16;
+    d.ldx = inter;
+    d.k = (int)inter;
+    d.rb = row_bytes_of(qtype, inter);
+    d.estride = d.rb * hidden;
+    d.seg.nseg = 1;
+    d.seg.tile0[0] = 0;
+    d.seg.w[0] = (const uint8_t*)w_down;
+    d.seg.n[0] = (int)hidden;
+    d.seg.k[0] = (int)inter;
+    d.seg.y[0] = dbuf;
+    d.seg.ldy[0] = hidden;
+    for (int i = 1; i <= kMaxSeg; ++i) d.seg.tile0[i] = (int)hcols;
+    if ((err = launch_gemm_wide(qtype, kGrouped, 8, d, s)) != hipSuccess) return err;
+    const int64_t nq = t * hidden / 4;
+    hipLaunchKernelGGL(moe_combine_rows_kernel, dim3((uint32_t)((nq + 255) / 256)), dim3(256), 0, s, dbuf, ids, rowmax,
+                       weights, (int)t, (int)top_k, (int)n_experts, (int)hidden, out);
+    return hipGetLastError();
   }
 
   GemmParams p = {};

@@ -14,7 +14,7 @@ namespace qp {
 
 constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
 
-enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4, kMulti = 5 };
+enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4, kMulti = 5, kGrouped = 6 };
 
 // Projections sharing one X fused into one launch of the tall kernel (mode
 // kMulti): segment s owns the output-column tiles [tile0[s], tile0[s + 1]),
@@ -67,6 +67,10 @@ struct GemmParams {
   GemmSegments seg;      // fused projections (kMulti)
   int64_t part_stride;   // 128-tile plain modes split over gridDim.z K parts: floats between partial outputs
   int vec_store;         // 128-tile kernel: output rows are 16-byte multiples (16-byte stores)
+  // routed experts on the 256 x 256-tile kernel (kGrouped): a tile table of
+  // 256-row tiles of the per-expert lists; gather: X rows are the tokens
+  // list[row] / top_k (gate/up), else the compact rows themselves (down)
+  int gather;
 };
 
 // Power of two bringing a row's largest |h| into [2^14, 2^15): binary16 then

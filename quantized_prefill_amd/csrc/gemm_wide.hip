@@ -368,7 +368,11 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   for (int q = 0; q < XL; ++q) {
     const int row = w * (BMW / NW) + 8 * q + (lane >> 3);
     const int piece = (lane & 7) ^ ((row >> 1) & 7);
-    xoff[q] = (uint32_t)(2 * (min(row, m_rows - 1) * p.ldx + 8 * piece));
+    int xr = min(row, m_rows - 1);
+    if constexpr (MODE == kGrouped) {
+      if (p.gather) xr = p.list[xr] / p.top_k;  // the token of compact row xr
+    }
+    xoff[q] = (uint32_t)(2 * (xr * p.ldx + 8 * piece));
   }
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)xtile, (short)0, -1, 0x00020000);
   auto load_x = [&](int c) __attribute__((always_inline)) {
@@ -582,6 +586,15 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   float16v accs[MI][1];
 #pragma unroll
   for (int i = 0; i < MI; ++i) accs[i][0] = acc[i];
+  if constexpr (MODE == kGrouped) {
+    if (!p.gather) {  // routed down pass: row r of the tile is pair list[r]'s row of y
+      store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
+                             [&](int r) __attribute__((always_inline)) {
+                               return p.y + (int64_t)p.list[min(r, m_rows - 1)] * p.ldy;  // rows past the tile: not stored
+                             });
+      return;
+    }
+  }
   store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
                          [&](int r) __attribute__((always_inline)) { return p.y + (int64_t)(m0 + r) * p.ldy; });
 }
@@ -605,8 +618,33 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     p.y = pk.seg.y[sg];
     p.ldy = pk.seg.ldy[sg];
   }
+  int m0 = blockIdx.y * Cfg<QT, MI>::BMW;
+  if constexpr (MODE == kGrouped) {
+    // routed experts: blockIdx.y is a tile of the table (the grid covers the
+    // largest possible table; workgroups past its end leave at once), the
+    // column tile picks the segment (gate / up, or the down projection)
+    const int ti = blockIdx.y;
+    if (ti >= *pk.ntiles) return;
+    const int e = pk.tiles[2 * ti], r0 = pk.tiles[2 * ti + 1];
+    const int base = pk.offsets[e] + r0;  // first compact row of the tile
+    int sg = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
+    tile_x -= pk.seg.tile0[sg];
+    p.w = pk.seg.w[sg] + (int64_t)e * pk.estride;
+    p.n = pk.seg.n[sg];
+    p.ldy = pk.seg.ldy[sg];
+    p.t = min(Cfg<QT, MI>::BMW, pk.counts[e] - r0);
+    p.list = pk.list + base;  // the tile's pairs
+    if (pk.gather) {          // gate / up: X rows are the pairs' tokens, y the compact rows
+      p.y = pk.seg.y[sg] + (int64_t)base * pk.seg.ldy[sg];
+    } else {                  // down: A the compact rows, y the pairs' rows
+      p.x = (const _Float16*)pk.x + (int64_t)base * pk.ldx;
+      p.y = pk.seg.y[sg];
+    }
+    m0 = 0;
+  }
   const int n0 = tile_x * Cfg<QT, MI>::BNW;
-  const int m0 = blockIdx.y * Cfg<QT, MI>::BMW;
   if (n0 + Cfg<QT, MI>::BNW <= p.n)
     wide_tile<QT, MODE, MI, true>(p, sm, n0, m0);
   else
@@ -614,7 +652,8 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
 }
 
 bool wide_supported(int qtype, int mode) {
-  return (qtype == kQ6_K || qtype == kQ2_K || qtype == kQ4_K || qtype == kQ5_K) && (mode == kPlainF16 || mode == kMulti);
+  return (qtype == kQ6_K || qtype == kQ2_K || qtype == kQ4_K || qtype == kQ5_K) &&
+         (mode == kPlainF16 || mode == kMulti || mode == kGrouped);
 }
 
 int wide_cols() { return 32 * NW; }
@@ -622,17 +661,21 @@ int wide_cols() { return 32 * NW; }
 template <int QT, int MODE, int MI>
 static void launch_wide_t(const GemmParams& p, uint32_t col_tiles, hipStream_t s) {
   constexpr int BMW = 32 * MI;
-  const dim3 grid(col_tiles, (uint32_t)((p.t + BMW - 1) / BMW));
+  // kGrouped: p.t carries the size of the tile table (its largest possible length)
+  const dim3 grid(col_tiles, MODE == kGrouped ? (uint32_t)p.t : (uint32_t)((p.t + BMW - 1) / BMW));
   hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), grid, dim3(NTW), 0, s, p);
 }
 
 // Tiles of 32 * mi tokens x 256 features (mi = 8 or 4); kMulti: p.seg
 // holds the segments and col_tiles their total.
 hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s) {
-  if (mode != kPlainF16 && mode != kMulti) return hipErrorInvalidValue;
-  const uint32_t cols = mode == kMulti ? (uint32_t)p.seg.tile0[p.seg.nseg] : (uint32_t)((p.n + 255) / 256);
+  if (mode != kPlainF16 && mode != kMulti && mode != kGrouped) return hipErrorInvalidValue;
+  if (mode == kGrouped && mi != 8) return hipErrorInvalidValue;
+  const uint32_t cols = mode != kPlainF16 ? (uint32_t)p.seg.tile0[p.seg.nseg] : (uint32_t)((p.n + 255) / 256);
 #define QP_WIDE_T(QT)                                                                              \
-  if (mode == kMulti) {                                                                            \
+  if (mode == kGrouped) {                                                                          \
+    launch_wide_t<QT, kGrouped, 8>(p, cols, s);                                                    \
+  } else if (mode == kMulti) {                                                                     \
     if (mi == 8) launch_wide_t<QT, kMulti, 8>(p, cols, s); else launch_wide_t<QT, kMulti, 4>(p, cols, s); \
   } else {                                                                                         \
     if (mi == 8) launch_wide_t<QT, kPlainF16, 8>(p, cols, s); else launch_wide_t<QT, kPlainF16, 4>(p, cols, s); \

@@ -50,8 +50,9 @@ hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t 
 // Workspace carve-up of the grouped expert GEMM (offsets in bytes, each
 // 256-byte aligned).
 struct MoeWorkspace {
-  size_t header, ccount, cbad, cpref, counts, offsets, ntiles, tiles, list, rowmax, hbuf, dbuf, total;
-  int64_t max_tiles, nchunks;
+  size_t header, ccount, cbad, cpref, counts, offsets, ntiles, tiles, ntiles2, tiles2, list, rowmax, hbuf, ubuf, h16,
+      dbuf, total;
+  int64_t max_tiles, max_tiles2, nchunks;
 };
 bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t hidden, int64_t inter,
                           MoeWorkspace& ws);
