@@ -890,10 +890,15 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
   const int e = threadIdx.x;
   const int c = e < ne ? counts[e] : 0;
   const int nt = (c + BM - 1) / BM;
-  const int nt2 = (c + 255) / 256;  // tiles of the 256-row kernel
-  int tot, tot2, rows_tot;
+  // tiles of the 256-row kernel: those of more than 128 rows first, then the
+  // last tiles of at most 128 rows (which take about half the time) at the
+  // end of the table, so that they fill the launch's last round
+  const int rem = c % 256;
+  const int nbig = c / 256 + (rem > 128), nsmall = rem > 0 && rem <= 128;
+  int tot, tot2, tot2s, rows_tot;
   const int cin = block_scan_1024(c, wsum, &rows_tot);
-  const int tin2 = block_scan_1024(nt2, wsum, &tot2);
+  const int tin2 = block_scan_1024(nbig, wsum, &tot2);
+  const int tin2s = block_scan_1024(nsmall, wsum, &tot2s);
   const int tin = block_scan_1024(nt, wsum, &tot);
   if (e < ne) {
     offsets[e] = cin - c;
@@ -902,16 +907,21 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
       tiles[2 * (t0 + k)] = e;
       tiles[2 * (t0 + k) + 1] = k * BM;
     }
-    const int u0 = tin2 - nt2;
-    for (int k = 0; k < nt2; ++k) {
+    const int u0 = tin2 - nbig;
+    for (int k = 0; k < nbig; ++k) {
       tiles2[2 * (u0 + k)] = e;
       tiles2[2 * (u0 + k) + 1] = k * 256;
+    }
+    if (nsmall) {
+      const int u = tot2 + tin2s - 1;
+      tiles2[2 * u] = e;
+      tiles2[2 * u + 1] = nbig * 256;
     }
   }
   if (e == 0) {
     ntiles[0] = tot;
     ntiles[1] = rows_tot;  // compact rows in all lists
-    *ntiles2 = tot2;
+    *ntiles2 = tot2 + tot2s;
   }
 }
 

@@ -471,112 +471,125 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   float16v acc[MI];
 #pragma unroll
   for (int i = 0; i < MI; ++i) acc[i] = (float16v){};
-  // activation fragment of k-step s: row 32 i + l % 32, piece 4 (s % 2) + 2 g + s / 2;
-  // rows 32 apart share the slot order
-  int aoff[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) aoff[s] = 2 * xswz(lane & 31, 4 * (s & 1) + 2 * g + (s >> 1));
-  auto a_ptr = [&](int c, int s) __attribute__((always_inline)) -> const char* {
-    return (const char*)sm.x[min(c, nch - 1) % XB] + aoff[s];
-  };
+  // The loop over K for the first MA M blocks (a tile of at most 32 MA rows
+  // skips the MFMAs and fragment reads of the blocks past its rows).
+  auto main_loop = [&](auto mac) __attribute__((always_inline)) {
+    constexpr int MA = decltype(mac)::value;
+    // activation fragment of k-step s: row 32 i + l % 32, piece 4 (s % 2) + 2 g + s / 2;
+    // rows 32 apart share the slot order
+    int aoff[4];
+  #pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[s] = 2 * xswz(lane & 31, 4 * (s & 1) + 2 * g + (s >> 1));
+    auto a_ptr = [&](int c, int s) __attribute__((always_inline)) -> const char* {
+      return (const char*)sm.x[min(c, nch - 1) % XB] + aoff[s];
+    };
 
-  uint32_t b[4][4];
-  half8 a[MI];
-  uint32_t u0[D::NU], u1[D::NU];
-  UnitScale s0, s1;
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
+    uint32_t b[4][4];
+    half8 a[MA];
+    uint32_t u0[D::NU], u1[D::NU];
+    UnitScale s0, s1;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
-  // ---- prologue: steps 0 and 1 staged, activation chunks 0 .. 2; chunk 0's
-  // slots 0..2 decoded (slot 3 in the loop's first k-step)
-  stage_part(0, 0, P0{}, P4{});
-  stage_part(1, 1, P0{}, P4{});
-  load_x(0);
-  load_x(1);
-  load_x(2);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_barrier();
-  {
-    const char* ap = a_ptr(0, 0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) a[i] = *(const half8*)(ap + 32 * 64 * 2 * i);
-  }
-  read_unit(0, I0{}, I0{}, u0);
-  read_unit(0, I0{}, I1{}, u1);
-  s0 = D::template scale<0, 0>(u0, dec_arg(0), g);
-  s1 = D::template scale<0, 1>(u1, dec_arg(0), g);
-  D::template half<0, 0, 0>(u0, dec_arg(0), s0, b);
-  D::template half<0, 1, 0>(u1, dec_arg(0), s1, b);
-  D::template half<0, 0, 1>(u0, dec_arg(0), s0, b);
-
-  // k-step s of chunk c: MFMA i, then the read of M block i of the next
-  // fragment (k-step s + 1, or k-step 0 of chunk c + 1)
-  auto mfmas = [&](int c, int s) __attribute__((always_inline)) {
-    const char* ap = s < 3 ? a_ptr(c, s + 1) : a_ptr(c + 1, 0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], __builtin_bit_cast(half8, b[s]), acc[i], 0, 0, 0);
-      a[i] = *(const half8*)(ap + 32 * 64 * 2 * i);
-    }
-  };
-  // per MFMA: the fragment read after it, a share of the VALU and of the global loads
-  auto interleave = [&](auto nvc, auto nmc) __attribute__((always_inline)) {
-    constexpr int NV = decltype(nvc)::value, NM = decltype(nmc)::value;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, (NM + MI - 1) / MI, 0);  // global load
-      __builtin_amdgcn_sched_group_barrier(0x002, (NV + MI - 1) / MI, 0);  // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  using V0 = std::integral_constant<int, 40>;
-
-  // chunk c = 2 st + O
-  auto chunk = [&](int st, auto oc) __attribute__((always_inline)) {
-    constexpr int O = decltype(oc)::value;
-    constexpr int ON = 1 - O;  // chunk c + 1 within its step
-    const int c = 2 * st + O;
-    const int sn = O ? st + 1 : st;  // step of chunk c + 1
-    using ONc = std::integral_constant<int, ON>;
-    const uint32_t da = dec_arg(st), dn = dec_arg(sn);
-    // k-step 0
-    if constexpr (O == 1) stage_part(st + 2, st & 1, P1{}, P2{});
-    mfmas(c, 0);
-    D::template half<O, 1, 1>(u1, da, s1, b);  // slot 3, this chunk
-    read_unit(sn, ONc{}, I0{}, u0);
-    interleave(V0{}, std::integral_constant<int, O == 1 ? P2::value - P1::value : 0>{});
-    // k-step 1
-    if constexpr (O == 1) stage_part(st + 2, st & 1, P2{}, P3{});
-    mfmas(c, 1);
-    s0 = D::template scale<ON, 0>(u0, dn, g);
-    D::template half<ON, 0, 0>(u0, dn, s0, b);  // slot 0, next chunk
-    read_unit(sn, ONc{}, I1{}, u1);
-    interleave(V0{}, std::integral_constant<int, O == 1 ? P3::value - P2::value : 0>{});
-    // k-step 2
-    if constexpr (O == 1) stage_part(st + 2, st & 1, P3{}, P4{});
-    mfmas(c, 2);
-    s1 = D::template scale<ON, 1>(u1, dn, g);
-    D::template half<ON, 1, 0>(u1, dn, s1, b);  // slot 1, next chunk
-    interleave(V0{}, std::integral_constant<int, O == 1 ? P4::value - P3::value : 0>{});
-    // activations of chunk c + 1 (and for odd c the staging of step st + 2) have landed
-    if constexpr (O == 1)
-      wait_vm<XL + NI>();
-    else
-      wait_vm<XL>();
+    // ---- prologue: steps 0 and 1 staged, activation chunks 0 .. 2; chunk 0's
+    // slots 0..2 decoded (slot 3 in the loop's first k-step)
+    stage_part(0, 0, P0{}, P4{});
+    stage_part(1, 1, P0{}, P4{});
+    load_x(0);
+    load_x(1);
+    load_x(2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    // k-step 3
-    load_x(c + 3);  // its buffer held chunk c
-    if constexpr (O == 0) stage_part(st + 2, st & 1, P0{}, P1{});  // its buffer held step st
-    mfmas(c, 3);
-    D::template half<ON, 0, 1>(u0, dn, s0, b);  // slot 2, next chunk
-    interleave(V0{}, std::integral_constant<int, XL + (O == 0 ? P1::value : 0)>{});
-  };
+    {
+      const char* ap = a_ptr(0, 0);
+  #pragma unroll
+      for (int i = 0; i < MA; ++i) a[i] = *(const half8*)(ap + 32 * 64 * 2 * i);
+    }
+    read_unit(0, I0{}, I0{}, u0);
+    read_unit(0, I0{}, I1{}, u1);
+    s0 = D::template scale<0, 0>(u0, dec_arg(0), g);
+    s1 = D::template scale<0, 1>(u1, dec_arg(0), g);
+    D::template half<0, 0, 0>(u0, dec_arg(0), s0, b);
+    D::template half<0, 1, 0>(u1, dec_arg(0), s1, b);
+    D::template half<0, 0, 1>(u0, dec_arg(0), s0, b);
 
-  for (int st = 0; st < nsteps; ++st) {
-    chunk(st, I0{});
-    chunk(st, I1{});
+    // k-step s of chunk c: MFMA i, then the read of M block i of the next
+    // fragment (k-step s + 1, or k-step 0 of chunk c + 1)
+    auto mfmas = [&](int c, int s) __attribute__((always_inline)) {
+      const char* ap = s < 3 ? a_ptr(c, s + 1) : a_ptr(c + 1, 0);
+  #pragma unroll
+      for (int i = 0; i < MA; ++i) {
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], __builtin_bit_cast(half8, b[s]), acc[i], 0, 0, 0);
+        a[i] = *(const half8*)(ap + 32 * 64 * 2 * i);
+      }
+    };
+    // per MFMA: the fragment read after it, a share of the VALU and of the global loads
+    auto interleave = [&](auto nvc, auto nmc) __attribute__((always_inline)) {
+      constexpr int NV = decltype(nvc)::value, NM = decltype(nmc)::value;
+  #pragma unroll
+      for (int i = 0; i < MA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x020, (NM + MA - 1) / MA, 0);  // global load
+        __builtin_amdgcn_sched_group_barrier(0x002, (NV + MA - 1) / MA, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using V0 = std::integral_constant<int, 40>;
+
+    // chunk c = 2 st + O
+    auto chunk = [&](int st, auto oc) __attribute__((always_inline)) {
+      constexpr int O = decltype(oc)::value;
+      constexpr int ON = 1 - O;  // chunk c + 1 within its step
+      const int c = 2 * st + O;
+      const int sn = O ? st + 1 : st;  // step of chunk c + 1
+      using ONc = std::integral_constant<int, ON>;
+      const uint32_t da = dec_arg(st), dn = dec_arg(sn);
+      // k-step 0
+      if constexpr (O == 1) stage_part(st + 2, st & 1, P1{}, P2{});
+      mfmas(c, 0);
+      D::template half<O, 1, 1>(u1, da, s1, b);  // slot 3, this chunk
+      read_unit(sn, ONc{}, I0{}, u0);
+      interleave(V0{}, std::integral_constant<int, O == 1 ? P2::value - P1::value : 0>{});
+      // k-step 1
+      if constexpr (O == 1) stage_part(st + 2, st & 1, P2{}, P3{});
+      mfmas(c, 1);
+      s0 = D::template scale<ON, 0>(u0, dn, g);
+      D::template half<ON, 0, 0>(u0, dn, s0, b);  // slot 0, next chunk
+      read_unit(sn, ONc{}, I1{}, u1);
+      interleave(V0{}, std::integral_constant<int, O == 1 ? P3::value - P2::value : 0>{});
+      // k-step 2
+      if constexpr (O == 1) stage_part(st + 2, st & 1, P3{}, P4{});
+      mfmas(c, 2);
+      s1 = D::template scale<ON, 1>(u1, dn, g);
+      D::template half<ON, 1, 0>(u1, dn, s1, b);  // slot 1, next chunk
+      interleave(V0{}, std::integral_constant<int, O == 1 ? P4::value - P3::value : 0>{});
+      // activations of chunk c + 1 (and for odd c the staging of step st + 2) have landed
+      if constexpr (O == 1)
+        wait_vm<XL + NI>();
+      else
+        wait_vm<XL>();
+      lds_barrier();
+      // k-step 3
+      load_x(c + 3);  // its buffer held chunk c
+      if constexpr (O == 0) stage_part(st + 2, st & 1, P0{}, P1{});  // its buffer held step st
+      mfmas(c, 3);
+      D::template half<ON, 0, 1>(u0, dn, s0, b);  // slot 2, next chunk
+      interleave(V0{}, std::integral_constant<int, XL + (O == 0 ? P1::value : 0)>{});
+    };
+
+    for (int st = 0; st < nsteps; ++st) {
+      chunk(st, I0{});
+      chunk(st, I1{});
+    }
+  };
+  if constexpr (MI == 8) {
+    if (m_rows <= 128)
+      main_loop(std::integral_constant<int, 4>{});
+    else
+      main_loop(std::integral_constant<int, 8>{});
+  } else {
+    main_loop(std::integral_constant<int, MI>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
   lds_barrier();
