@@ -45,6 +45,7 @@ struct AttnArgs {
   int n_head, n_kv, group;
   int nqt;     // query tiles of 128
   int xcd;     // 1: the workgroups of one kv group go to one XCD
+  int fold;    // 1: the launch is one round of workgroups (two per CU)
   float c;     // scale * log2(e)
 };
 
@@ -133,7 +134,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     unit = b / p.group;
     member = b % p.group;
   }
-  const int qt = p.nqt - 1 - unit / p.n_kv;
+  // Longest first; in a launch of one round (fold), the second half of the
+  // order runs from the shortest up: workgroups b and b + half the grid then
+  // have query tiles whose key counts add up to about the same for every b,
+  // so that CUs given one of each finish together.
+  const int rank = unit / p.n_kv;
+  const int nh = p.nqt / 2;
+  const int qt = (p.fold && rank >= p.nqt - nh) ? rank - (p.nqt - nh) : p.nqt - 1 - rank;
   const int g = unit % p.n_kv;
   const int head = g * p.group + member;
   const int q0 = qt * kBM;
@@ -333,6 +340,7 @@ hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void
   p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
   const int64_t blocks = (int64_t)p.nqt * n_head;
   p.xcd = blocks % (8 * p.group) == 0 ? 1 : 0;
+  p.fold = (blocks <= 2 * (int64_t)cu_count() && p.nqt % 2 == 0) ? 1 : 0;
   if (kv_type == kF16)
     hipLaunchKernelGGL(attention_kernel<kF16>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
   else if (kv_type == kQ8_0)
