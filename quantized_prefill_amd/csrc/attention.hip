@@ -3,10 +3,19 @@
 // Q4/native-IQ opt-ins", section "Summary" and the KV table after it: prompt
 // attention as a tensor-core path over a quantized KV cache).
 //
-// One workgroup = 128 queries of one query head: 4 waves of 32 queries.  The
-// keys of the head's kv head stream through LDS in blocks of 64, double
-// buffered: K as rows (64 x 128), V transposed (128 x 64), both binary16,
-// decoded from the cache as they are staged.  Per wave and key block:
+// One workgroup = 128 queries of one query head: 4 waves of 32 queries
+// (NH = 1), or two halves of 4 such waves with the same queries (NH = 2).
+// The keys of the head's kv head stream through LDS in blocks of 64: half h
+// takes blocks h, h + NH, h + 2 NH, .. into its own double buffer, K as rows
+// (64 x 128), V transposed (128 x 64), both binary16, decoded from the cache
+// as they are staged.  With two halves, the second hands its running
+// maximum, row-sum share and O through LDS to the first at the end, which
+// merges the two (the usual rescale of both by 2^(m_h - max)) and stores.
+// Two halves keep a CU at two waves per SIMD for the whole of every tile,
+// whatever the tiles' lengths: the choice for a launch of one round, where
+// the causal tiles' lengths differ up to the grid size and nothing else
+// evens them out; with several rounds, single halves (two workgroups per
+// CU, no shared barrier) are faster.  Per wave and key block:
 //   S^T (64 keys x 32 queries) = K . Q^T    16 v_mfma_f32_32x32x16_f16
 //   online softmax over the keys            one lane owns one query column
 //   O^T (128 x 32) += V^T . P^T             16 v_mfma_f32_32x32x16_f16
@@ -28,7 +37,7 @@ namespace qp {
 namespace {
 
 constexpr int kD = 128;              // head dim
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;            // per half
 constexpr int kBM = 32 * kWaves;     // queries per workgroup
 constexpr int kBK = 64;              // keys per staged block
 constexpr int kKP = kD + 8;          // K row pitch in halves: 16-lane reads hit distinct banks
@@ -45,7 +54,6 @@ struct AttnArgs {
   int n_head, n_kv, group;
   int nqt;     // query tiles of 128
   int xcd;     // 1: the workgroups of one kv group go to one XCD
-  int fold;    // 1: the launch is one round of workgroups (two per CU)
   float c;     // scale * log2(e)
 };
 
@@ -114,12 +122,15 @@ template <> struct Chunk<kQ4_0> {
   }
 };
 
-template <int KV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnArgs p) {
+template <int KV, int NH>
+__global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnArgs p) {
   using C = Chunk<KV>;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * kStage];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) _Float16 smem[NH * 2 * kStage];
+  const int half = NH == 1 ? 0 : (int)(threadIdx.x >> 8);  // wave-uniform
+  const int tid = threadIdx.x & 255;          // thread within the half
+  const int lane = tid & 63, wave = tid >> 6;  // wave within the half
   const int r = lane & 31, hh = lane >> 5;
+  _Float16* const lds = smem + half * 2 * kStage;  // the half's double buffer
 
   // workgroup -> (query tile, head); the longest tiles first.  With the XCD
   // map, the group's query heads of one (tile, kv head) unit are dispatched
@@ -134,13 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     unit = b / p.group;
     member = b % p.group;
   }
-  // Longest first; in a launch of one round (fold), the second half of the
-  // order runs from the shortest up: workgroups b and b + half the grid then
-  // have query tiles whose key counts add up to about the same for every b,
-  // so that CUs given one of each finish together.
-  const int rank = unit / p.n_kv;
-  const int nh = p.nqt / 2;
-  const int qt = (p.fold && rank >= p.nqt - nh) ? rank - (p.nqt - nh) : p.nqt - 1 - rank;
+  const int qt = p.nqt - 1 - unit / p.n_kv;
   const int g = unit % p.n_kv;
   const int head = g * p.group + member;
   const int q0 = qt * kBM;
@@ -221,14 +226,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int qpos_lo = p.n_past + q0w;
   const int qpos = qpos_lo + r;
 
-  load_block(0);
-  store_block(0);
+  // half h: blocks h + NH i, i < niter (the second half may have one fewer)
+  const int niter = (nkb + NH - 1) / NH;
+  if (half < nkb) {
+    load_block(half);
+    store_block(0);
+  }
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) load_block(kb + 1);
+  for (int i = 0; i < niter; ++i) {
+    const int kb = NH * i + half;
+    if (kb + NH < nkb) load_block(kb + NH);
     const int key0 = kb * kBK;
-    if (wave_live && key0 <= qpos_lo + 31) {
-      const _Float16* ks = lds + (kb & 1) * kStage;
+    if (kb < nkb && wave_live && key0 <= qpos_lo + 31) {
+      const _Float16* ks = lds + (i & 1) * kStage;
       const _Float16* vt = ks + kBK * kKP;
       float16v s[2];
 #pragma unroll
@@ -292,8 +302,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[st], o[dt], 0, 0, 0);
         }
     }
-    if (kb + 1 < nkb) store_block((kb + 1) & 1);
+    if (kb + NH < nkb) store_block((i + 1) & 1);
     __syncthreads();
+  }
+
+  // merge: the second half's m, row-sum share and O go through LDS (66 floats
+  // per lane, lane-minor, so that every access is one dword per lane)
+  float* xch = (float*)smem + wave * 66 * 64 + lane;
+  if (NH == 2 && half == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) xch[(16 * dt + a) * 64] = o[dt][a];
+    xch[64 * 64] = m_run;
+    xch[65 * 64] = l_part;
+  }
+  if (NH == 2) __syncthreads();
+  if (half == 1) return;
+  if (NH == 2) {
+    const float m_b = xch[64 * 64], l_b = xch[65 * 64];
+    const float m = fmaxf(m_run, m_b);  // finite for a live query: key 0 is in the first half's block 0
+    const float m_s = m == -INFINITY ? 0.f : m;
+    const float fa = __builtin_amdgcn_exp2f(m_run - m_s), fb = __builtin_amdgcn_exp2f(m_b - m_s);
+    l_part = l_part * fa + l_b * fb;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) o[dt][a] = o[dt][a] * fa + xch[(16 * dt + a) * 64] * fb;
   }
 
   const float l = l_part + __shfl_xor(l_part, 32, 64);
@@ -340,15 +375,23 @@ hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void
   p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
   const int64_t blocks = (int64_t)p.nqt * n_head;
   p.xcd = blocks % (8 * p.group) == 0 ? 1 : 0;
-  p.fold = (blocks <= 2 * (int64_t)cu_count() && p.nqt % 2 == 0) ? 1 : 0;
-  if (kv_type == kF16)
-    hipLaunchKernelGGL(attention_kernel<kF16>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
-  else if (kv_type == kQ8_0)
-    hipLaunchKernelGGL(attention_kernel<kQ8_0>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
-  else if (kv_type == kQ4_0)
-    hipLaunchKernelGGL(attention_kernel<kQ4_0>, dim3((uint32_t)blocks), dim3(256), 0, s, p);
-  else
-    return hipErrorInvalidValue;
+  // one round of workgroups (two per CU): halves; more: single halves
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const bool two = blocks <= 2 * (int64_t)cus;
+  const dim3 grid((uint32_t)blocks), blk(two ? 512 : 256);
+  if (kv_type != kF16 && kv_type != kQ8_0 && kv_type != kQ4_0) return hipErrorInvalidValue;
+  if (two) {
+    if (kv_type == kF16) hipLaunchKernelGGL((attention_kernel<kF16, 2>), grid, blk, 0, s, p);
+    if (kv_type == kQ8_0) hipLaunchKernelGGL((attention_kernel<kQ8_0, 2>), grid, blk, 0, s, p);
+    if (kv_type == kQ4_0) hipLaunchKernelGGL((attention_kernel<kQ4_0, 2>), grid, blk, 0, s, p);
+  } else {
+    if (kv_type == kF16) hipLaunchKernelGGL((attention_kernel<kF16, 1>), grid, blk, 0, s, p);
+    if (kv_type == kQ8_0) hipLaunchKernelGGL((attention_kernel<kQ8_0, 1>), grid, blk, 0, s, p);
+    if (kv_type == kQ4_0) hipLaunchKernelGGL((attention_kernel<kQ4_0, 1>), grid, blk, 0, s, p);
+  }
   return hipGetLastError();
 }
 

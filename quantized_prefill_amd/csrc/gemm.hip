@@ -221,7 +221,7 @@ static hipError_t launch_mode(int qtype, dim3 grid, const GemmParams& p, hipStre
   return hipGetLastError();
 }
 
-int cu_count() {
+static int cu_count() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)

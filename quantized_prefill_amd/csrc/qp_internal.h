@@ -20,8 +20,6 @@ hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, con
                              hipStream_t s);
 int gemm_ksplit_parts(int64_t n, int64_t k, int64_t t);
 bool wide_halves_shape(int64_t n, int64_t k, int64_t t);
-// compute units of the current device (256 if the query fails)
-int cu_count();
 // launch_gemm_split with the library's static device scratch as the room for
 // partial sums (kNoAllocScratchBytes; no allocation, no caller workspace).
 constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;

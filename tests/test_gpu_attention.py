@@ -106,6 +106,24 @@ def test_attention_qwen3_8b_t2048(orc, kvtype):
     assert_close(y[tok], ref, f"attention 8B {synth.NAMES[kvtype]}")
 
 
+@pytest.mark.parametrize("kvtype,t", [(Q8_0, 8192), (Q4_0, 8192), (F16W, 2200)], ids=["Q8_0-8192", "Q4_0-8192",
+                                                                                   "F16-2200"])
+def test_attention_several_rounds(orc, kvtype, t):
+    """Launches of more than one round of workgroups (32 heads: T = 2200, 18
+    query tiles with a ragged last one, and the T = 8192 launch the bench
+    times) take the single-half workgroups; sampled queries, the last
+    included, against the oracle."""
+    n_head, n_kv = 32, 8
+    q = queries(t, n_head, 12900 + t)
+    kc = synth.kv_cache(kvtype, t, n_kv, HD, 12901 + t)
+    vc = synth.kv_cache(kvtype, t, n_kv, HD, 12902 + t)
+    say(f"attention 8B t={t} {synth.NAMES[kvtype]}")
+    y = run_attention(kvtype, q, kc, vc, 0, n_head, n_kv)
+    tok = np.unique(np.concatenate([sample_tokens(t, 12, 12903 + t), [0, 127, 128, t - 1]]))
+    ref = orc.attention(kvtype, q, kc, vc, 0, n_head, n_kv, HD, tokens=tok)
+    assert_close(y[tok], ref, f"attention 8B t={t} {synth.NAMES[kvtype]}")
+
+
 def test_attention_default_scale_and_huge_negative_scores(orc):
     """scale None takes the library's 1 / sqrt(head_dim), bit for bit the same
     as passing that f32 value; with every key equal and scaled scores near
