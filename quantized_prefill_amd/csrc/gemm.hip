@@ -298,9 +298,6 @@ __global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict
   }
 }
 
-// K parts for a plain 128-tile launch that leaves the GPU under-filled: the
-// smallest power of two (at most 8) that gives one workgroup per CU, with
-// parts of whole 256-weight blocks.  1: no split.
 // The 256 x 256-tile kernel in two K halves: for a launch of exactly half a
 // round of those tiles (the 8B layer's down at T = 2048: 128 tiles), each
 // half runs as one segment of one launch, a full round together; half 0
@@ -312,11 +309,34 @@ bool wide_halves_shape(int64_t n, int64_t k, int64_t t) {
   return k % 512 == 0 && k >= 8192 && 2 * tiles == cu_count();
 }
 
+// The projection kernel in K slices, for launches that the 256 x 256 tiles
+// and the tall tiles leave short of the CUs: of the tilings 64 x 64 (four
+// slices), 64 x 128 and 128 x 128 (two slices), the one with the most
+// workgroups that still fit one round; none if none fits.
+static bool wide_ks_choice(int64_t n, int64_t k, int64_t t, int& mi, int& ks) {
+  const int64_t cus = cu_count();
+  const int cand[3][2] = {{2, 4}, {2, 2}, {4, 2}};
+  int64_t best = 0;
+  for (const auto& c : cand) {
+    const int64_t wgs = ((n + 256 / c[1] - 1) / (256 / c[1])) * ((t + 32 * c[0] - 1) / (32 * c[0]));
+    if (k % (256 * c[1]) == 0 && wgs <= cus && wgs > best) {
+      best = wgs;
+      mi = c[0];
+      ks = c[1];
+    }
+  }
+  return best > 0;
+}
+
+// K parts for a plain 128-tile launch that leaves the GPU under-filled: the
+// largest power of two (at most 8) whose parts still fit one round of
+// workgroups (a second, partly filled round costs more than the split
+// saves), with parts of whole 256-weight blocks.  1: no split.
 int gemm_ksplit_parts(int64_t n, int64_t k, int64_t t) {
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
   const int cus = cu_count();
   int parts = 1;
-  while (parts < 8 && tiles * parts < cus && k % (256 * 2 * parts) == 0) parts *= 2;
+  while (parts < 8 && tiles * parts * 2 <= cus && k % (256 * 2 * parts) == 0) parts *= 2;
   return parts;
 }
 
@@ -373,6 +393,10 @@ hipError_t launch_gemm_split(int qtype, const void* w, int64_t n, int64_t k, con
   if (!x_f32 && use_tall_tiles(qtype, n, k, t, ldx, ldy)) {
     dim3 grid((uint32_t)((n + BN - 1) / BN), (uint32_t)((t + 255) / 256));
     return launch_gemm_tall(qtype, kPlainF16, grid, p, s);
+  }
+  if (!x_f32 && wide_supported(qtype, kPlainF16) && tall_strides_ok(ldx, ldy)) {
+    int mi = 0, ks = 0;
+    if (wide_ks_choice(n, k, t, mi, ks)) return launch_gemm_wide_ks(qtype, mi, ks, p, s);
   }
   const int parts = partial != nullptr ? gemm_ksplit_parts(n, k, t) : 1;
   if (parts > 1 && (int64_t)parts * t * n <= partial_floats) {

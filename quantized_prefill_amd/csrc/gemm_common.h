@@ -376,5 +376,9 @@ hipError_t launch_gemm_tall(int qtype, int mode, dim3 grid, const GemmParams& p,
 bool wide_supported(int qtype, int mode);
 int wide_cols();
 hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s);
+// The projection kernel in ks K slices: tiles of 32 mi tokens x 256 / ks
+// features, (mi, ks) = (2, 2), (2, 4) or (4, 2), k % (256 ks) == 0, K-quant
+// weights, binary16 activations, plain mode.
+hipError_t launch_gemm_wide_ks(int qtype, int mi, int ks, const GemmParams& p, hipStream_t s);
 
 }  // namespace qp

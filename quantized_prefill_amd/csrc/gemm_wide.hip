@@ -290,27 +290,35 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int QT, int MI>
+// KS: K slices.  KS = 2 or 4 splits the 8 waves into KS groups that take
+// the KS parts of K with buffers of their own (a tile of 32 * MI tokens x
+// 256 / KS features); the other groups' sums join the first's through LDS
+// at the end, in slice order.  For short prefill chunks, where
+// 256-feature tiles would leave CUs idle and a K split across workgroups
+// writes partial sums to memory.
+template <int QT, int MI, int KS = 1>
 struct Cfg {
-  static constexpr int BMW = 32 * MI, BNW = 32 * NW;
+  static constexpr int NWS = NW / KS;                      // waves per K slice
+  static constexpr int BMW = 32 * MI, BNW = 32 * NWS;
   static constexpr int RSD = Stage<QT>::RSD;
   static constexpr int R = 64 / RSD;                       // rows per staging instruction
   static constexpr int NG = (BNW + R - 1) / R;             // groups of R rows per tile
-  static constexpr int NI = (NG + NW - 1) / NW;            // staging instructions per wave and step
+  static constexpr int NI = (NG + NWS - 1) / NWS;          // staging instructions per wave and step
   static constexpr int XTILE = BMW * 64;                   // halfs per activation chunk
   static constexpr int RAWB = BNW * RSD + 64;              // dwords per staging buffer (64 of padding)
   static constexpr int XB = 3;
-  static constexpr int XL = BMW * 8 / 64 / NW;             // activation loads per wave and chunk (16 B per lane)
+  static constexpr int XL = BMW * 8 / 64 / NWS;            // activation loads per wave and chunk (16 B per lane)
   static_assert((NG - 1) * R * RSD + 64 <= RAWB, "the padding takes the last group's spare lanes");
-  static_assert(XB * XTILE * 2 + 2 * RAWB * 4 <= kLds, "LDS budget");
-  static_assert(XL * NW * 64 == BMW * 8, "whole activation loads per wave");
+  static_assert(KS * (XB * XTILE * 2 + 2 * RAWB * 4) <= kLds, "LDS budget");
+  static_assert(XL * NWS * 64 == BMW * 8, "whole activation loads per wave");
+  static_assert((KS - 1) * NWS * MI * 16 * 64 <= XB * XTILE / 2 * KS, "the slice sums fit the activation buffers");
 };
 
-template <int QT, int MI>
+template <int QT, int MI, int KS = 1>
 struct Smem {
-  using C = Cfg<QT, MI>;
-  _Float16 x[C::XB][C::XTILE];
-  uint32_t raw[2][C::RAWB];
+  using C = Cfg<QT, MI, KS>;
+  _Float16 x[KS][C::XB][C::XTILE];
+  uint32_t raw[KS][2][C::RAWB];
 };
 
 }  // namespace wide
@@ -344,29 +352,34 @@ using namespace wide;
 // first read after the barrier of chunk 2t + 2.  Indices past the end are
 // clamped to the last chunk or step (the loads and decodes then repeat valid
 // data that nothing uses), so the loop body has no branches.
-template <int QT, int MODE, int MI, bool FULL>
-__device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm, int n0, int m0) {
-  using C = Cfg<QT, MI>;
+template <int QT, int MODE, int MI, bool FULL, int KS = 1>
+__device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>& sm, int n0, int m0) {
+  using C = Cfg<QT, MI, KS>;
+  constexpr int NWS = C::NWS;
   using S = Stage<QT>;
   using D = Dec<QT>;
   constexpr int BMW = C::BMW, BNW = C::BNW, XB = C::XB, RSD = C::RSD, R = C::R, NI = C::NI, XL = C::XL;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = wv / NWS;      // K slice of the wave
+  const int w = wv % NWS;       // wave within the slice
   const int g = lane >> 5;
   const int m_rows = min(BMW, p.t - m0);
-  const int nch = p.k / BK;     // chunks of 64 (a multiple of 4)
+  const int kslice = p.k / KS;  // the slice: weights kslice * ks .. of every row
+  const int ub0 = ks * (kslice / 256);  // its first block
+  const int nch = kslice / BK;  // chunks of 64 (a multiple of 4)
   const int nsteps = nch / 2;   // staging steps of 128
   const int64_t rb = p.rb;
   const uint32_t rb3 = (uint32_t)(rb & 3);
 
   // ---- activation copy: load q of wave w puts lane l at tile row
-  // w * BMW / NW + 8 q + l / 8, slot l % 8
-  const _Float16* xtile = (const _Float16*)p.x + (int64_t)m0 * p.ldx;
+  // w * BMW / NWS + 8 q + l / 8, slot l % 8
+  const _Float16* xtile = (const _Float16*)p.x + (int64_t)m0 * p.ldx + (int64_t)ks * kslice;
   uint32_t xoff[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
-    const int row = w * (BMW / NW) + 8 * q + (lane >> 3);
+    const int row = w * (BMW / NWS) + 8 * q + (lane >> 3);
     const int piece = (lane & 7) ^ ((row >> 1) & 7);
     int xr = min(row, m_rows - 1);
     if constexpr (MODE == kGrouped) {
@@ -377,7 +390,7 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)xtile, (short)0, -1, 0x00020000);
   auto load_x = [&](int c) __attribute__((always_inline)) {
     c = min(c, nch - 1);  // past the end: the last chunk again (keeps the load count uniform)
-    _Float16* dst = sm.x[c % XB] + w * (BMW / NW) * 64;
+    _Float16* dst = sm.x[ks][c % XB] + w * (BMW / NWS) * 64;
 #pragma unroll
     for (int q = 0; q < XL; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (__attribute__((address_space(3))) void*)(dst + 8 * q * 64), 16,
@@ -416,17 +429,17 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   auto stage_part = [&](int st, int buf, auto q0c, auto q1c) __attribute__((always_inline)) {
     constexpr int Q0 = decltype(q0c)::value, Q1 = decltype(q1c)::value;
     st = min(st, nsteps - 1);
-    const int u = st >> 1, h = st & 1;
+    const int u = (st >> 1) + ub0, h = st & 1;
     const uint32_t boff = (uint32_t)u * S::TS;
-    uint32_t* dst = sm.raw[buf];
+    uint32_t* dst = sm.raw[ks][buf];
     if constexpr (FULL) {
       const uint32_t ab = (boff >> 1) & 1u;
       const uint32_t v0 = vo00 + ab * vo_a + (uint32_t)h * vo_h;
       const uint32_t vl = vl00 + ab * vl_a + (uint32_t)h * vl_h;
 #pragma unroll
       for (int q = Q0; q < Q1; ++q) {
-        const int grp = min(NW * q + w, C::NG - 1);
-        const bool last = NW * q + NW - 1 >= C::NG - 1 && grp == C::NG - 1;
+        const int grp = min(NWS * q + w, C::NG - 1);
+        const bool last = NWS * q + NWS - 1 >= C::NG - 1 && grp == C::NG - 1;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (__attribute__((address_space(3))) void*)(dst + grp * R * RSD), 4,
                                                  (int)(last ? vl : v0), (int)((int64_t)grp * R * rb + (boff & ~3u)), 0, 0);
       }
@@ -438,7 +451,7 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
       const uint32_t v0 = ((((uint32_t)(sgr * rb) + boff) & ~3u) + S::off(sd, h));
 #pragma unroll
       for (int q = Q0; q < Q1; ++q) {
-        const int grp = min(NW * q + w, C::NG - 1);
+        const int grp = min(NWS * q + w, C::NG - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc_part,
                                                  (__attribute__((address_space(3))) void*)(dst + grp * R * RSD), 4,
                                                  (int)(v0 + (uint32_t)(grp * R * rb)), 0, 0, 0);
@@ -457,13 +470,13 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   // staged bytes of unit (O, r) of step st (clamped)
   auto read_unit = [&](int st, auto oc, auto rc, uint32_t (&u)[D::NU]) __attribute__((always_inline)) {
     st = min(st, nsteps - 1);
-    D::template read<decltype(oc)::value, decltype(rc)::value>(sm.raw[st & 1] + nrow * RSD, g, u);
+    D::template read<decltype(oc)::value, decltype(rc)::value>(sm.raw[ks][st & 1] + nrow * RSD, g, u);
   };
   // Q6_K: misalignment of the block start; Q4_K / Q5_K: the step's half
   auto dec_arg = [&](int st) __attribute__((always_inline)) -> uint32_t {
     st = min(st, nsteps - 1);
     if constexpr (QT == kQ6_K)
-      return (rdelta + (uint32_t)(st >> 1) * S::TS) & 3;
+      return (rdelta + (uint32_t)((st >> 1) + ub0) * S::TS) & 3;
     else
       return (uint32_t)(st & 1);
   };
@@ -481,7 +494,7 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   #pragma unroll
     for (int s = 0; s < 4; ++s) aoff[s] = 2 * xswz(lane & 31, 4 * (s & 1) + 2 * g + (s >> 1));
     auto a_ptr = [&](int c, int s) __attribute__((always_inline)) -> const char* {
-      return (const char*)sm.x[min(c, nch - 1) % XB] + aoff[s];
+      return (const char*)sm.x[ks][min(c, nch - 1) % XB] + aoff[s];
     };
 
     uint32_t b[4][4];
@@ -593,6 +606,33 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
   lds_barrier();
+  if constexpr (KS > 1) {
+    // the other slices' sums into the first's, in slice order (one dword
+    // per lane and value), then all past a barrier before the stores reuse
+    // the buffer
+    float* red = (float*)&sm.x[0][0][0] + lane;
+    constexpr int SW = MI * 16 * 64;  // floats per wave
+    if (ks > 0) {
+      float* dst = red + ((ks - 1) * NWS + w) * SW;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) dst[(16 * i + a) * 64] = acc[i][a];
+    }
+    lds_barrier();
+    if (ks == 0) {
+#pragma unroll
+      for (int k = 1; k < KS; ++k) {
+        const float* src = red + ((k - 1) * NWS + w) * SW;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) acc[i][a] = acc[i][a] + src[(16 * i + a) * 64];
+      }
+    }
+    lds_barrier();
+    if (ks > 0) return;
+  }
 
   // ---- epilogue: 16-byte stores through a per-wave LDS transpose
   float* scr = (float*)sm.x + 32 * 40 * w;
@@ -614,9 +654,9 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI>& sm,
 
 // Grid: (column tiles, token tiles).  kMulti: projections over one X, each
 // a segment of whole column tiles (its own weights, rows and output).
-template <int QT, int MODE, int MI>
+template <int QT, int MODE, int MI, int KS = 1>
 __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
-  __shared__ __attribute__((aligned(16))) Smem<QT, MI> sm;
+  __shared__ __attribute__((aligned(16))) Smem<QT, MI, KS> sm;
   GemmParams p = pk;
   int tile_x = blockIdx.x;
   if constexpr (MODE == kMulti) {
@@ -657,11 +697,11 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     }
     m0 = 0;
   }
-  const int n0 = tile_x * Cfg<QT, MI>::BNW;
-  if (n0 + Cfg<QT, MI>::BNW <= p.n)
-    wide_tile<QT, MODE, MI, true>(p, sm, n0, m0);
+  const int n0 = tile_x * Cfg<QT, MI, KS>::BNW;
+  if (n0 + Cfg<QT, MI, KS>::BNW <= p.n)
+    wide_tile<QT, MODE, MI, true, KS>(p, sm, n0, m0);
   else
-    wide_tile<QT, MODE, MI, false>(p, sm, n0, m0);
+    wide_tile<QT, MODE, MI, false, KS>(p, sm, n0, m0);
 }
 
 bool wide_supported(int qtype, int mode) {
@@ -701,6 +741,30 @@ hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hi
     default: return hipErrorInvalidValue;
   }
 #undef QP_WIDE_T
+  return hipGetLastError();
+}
+
+// K slices: tiles of 32 mi tokens x 256 / ks features, (mi, ks) = (2, 2),
+// (2, 4) or (4, 2); k % (256 ks) == 0; plain mode.
+hipError_t launch_gemm_wide_ks(int qtype, int mi, int ks, const GemmParams& p, hipStream_t s) {
+  if (!((mi == 2 && (ks == 2 || ks == 4)) || (mi == 4 && ks == 2))) return hipErrorInvalidValue;
+  const int bn = 256 / ks, bm = 32 * mi;
+  const dim3 grid((uint32_t)((p.n + bn - 1) / bn), (uint32_t)((p.t + bm - 1) / bm));
+#define QP_WIDE_KS(QT)                                                                                     \
+  if (mi == 4)                                                                                             \
+    hipLaunchKernelGGL((gemm_wide_kernel<QT, kPlainF16, 4, 2>), grid, dim3(NTW), 0, s, p);                 \
+  else if (ks == 2)                                                                                        \
+    hipLaunchKernelGGL((gemm_wide_kernel<QT, kPlainF16, 2, 2>), grid, dim3(NTW), 0, s, p);                 \
+  else                                                                                                     \
+    hipLaunchKernelGGL((gemm_wide_kernel<QT, kPlainF16, 2, 4>), grid, dim3(NTW), 0, s, p);
+  switch (qtype) {
+    case kQ6_K: QP_WIDE_KS(kQ6_K) break;
+    case kQ2_K: QP_WIDE_KS(kQ2_K) break;
+    case kQ4_K: QP_WIDE_KS(kQ4_K) break;
+    case kQ5_K: QP_WIDE_KS(kQ5_K) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QP_WIDE_KS
   return hipGetLastError();
 }
 

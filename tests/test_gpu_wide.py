@@ -134,3 +134,31 @@ def test_wide_half_round_q2_k(orc, t, n, k):
     qp.prefill_gemm_noalloc(qtype, w, n, k, xt, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), a), "allocation-free call differs from the workspace call"
+
+
+KSLICE = [(200, 1000, 2048), (500, 4000, 1024), (500, 6000, 1024)]
+
+
+@pytest.mark.parametrize("qtype", [Q4_K, Q5_K, Q6_K, Q2_K], ids=["Q4_K", "Q5_K", "Q6_K", "Q2_K"])
+@pytest.mark.parametrize("t,n,k", KSLICE, ids=["64x64-4-slices", "64x128-2-slices", "128x128-2-slices"])
+def test_wide_k_slices(orc, qtype, t, n, k):
+    """Short chunks on the wide kernel in K slices (on a 256-CU GPU the three
+    shapes take the 64 x 64 tiling with four slices, 64 x 128 and 128 x 128
+    with two): ragged token and feature tails, against the oracle on the
+    first and last row of every 64-token tile; two calls give the same bits,
+    and the allocation-free call matches them."""
+    import torch
+    say(f"K slices {synth.NAMES[qtype]} t={t} n={n} k={k}")
+    raw = weights(qtype, n, k, 9800 + n)
+    x = act_f16(t, k, 9801 + t)
+    w, xt = to_dev(raw), to_dev(x).view(torch.float16)
+    a = qp.prefill_gemm(qtype, w, n, k, xt).cpu().numpy()
+    b = qp.prefill_gemm(qtype, w, n, k, xt).cpu().numpy()
+    assert np.array_equal(a, b), "two calls differ"
+    tok = tile_rows(t, 64, 6, 9802)
+    assert_close(a[tok], orc.prefill_gemm(qtype, raw, n, k, x, tokens=tok), f"K slices {synth.NAMES[qtype]} {t}x{n}x{k}")
+    out = torch.empty((t, n), dtype=torch.float32, device="cuda")
+    qp.prefill_gemm_noalloc(qtype, w, n, k, xt, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), a), "allocation-free call differs"
+    weights.cache_clear()
