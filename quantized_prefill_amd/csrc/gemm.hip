@@ -749,14 +749,14 @@ hipError_t launch_gemm_qkv(int qtype, const void* const w[3], const int64_t n[3]
 // One wave per token: softmax over the experts, top_k by logit (largest
 // first, ties to the lower index), weight = softmax probability.  Lane s
 // keeps the s-th choice (top_k <= 64), so no register array is indexed at
-// run time.
+// run time.  PER: slots of 64 experts (ne <= 64 PER).
+template <int PER>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int t, int ne, int top_k,
                                                          int renorm, int32_t* __restrict__ ids,
                                                          float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tok >= t) return;
-  constexpr int PER = 16;  // up to 1024 experts, expert lane + 64 i in slot i
   float v[PER];
   const float* lg = logits + (int64_t)tok * ne;
   float mx = -__builtin_inff();
@@ -814,8 +814,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 hipError_t launch_route_topk(const float* logits, int64_t t, int64_t e, int64_t top_k, int renorm, int32_t* ids,
                              float* weights, hipStream_t s) {
-  hipLaunchKernelGGL(route_topk_kernel, dim3((uint32_t)((t + 3) / 4)), dim3(256), 0, s, logits, (int)t, (int)e,
-                     (int)top_k, renorm, ids, weights);
+  const dim3 grid((uint32_t)((t + 3) / 4));
+  if (e <= 64)
+    hipLaunchKernelGGL(route_topk_kernel<1>, grid, dim3(256), 0, s, logits, (int)t, (int)e, (int)top_k, renorm, ids,
+                       weights);
+  else if (e <= 128)
+    hipLaunchKernelGGL(route_topk_kernel<2>, grid, dim3(256), 0, s, logits, (int)t, (int)e, (int)top_k, renorm, ids,
+                       weights);
+  else if (e <= 256)
+    hipLaunchKernelGGL(route_topk_kernel<4>, grid, dim3(256), 0, s, logits, (int)t, (int)e, (int)top_k, renorm, ids,
+                       weights);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<16>, grid, dim3(256), 0, s, logits, (int)t, (int)e, (int)top_k, renorm, ids,
+                       weights);
   return hipGetLastError();
 }
 
