@@ -925,15 +925,23 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
   const int e = threadIdx.x;
   const int c = e < ne ? counts[e] : 0;
   const int nt = (c + BM - 1) / BM;
-  // tiles of the 256-row kernel: those of more than 128 rows first, then the
-  // last tiles of at most 128 rows (which take about half the time) at the
-  // end of the table, so that they fill the launch's last round
-  const int rem = c % 256;
-  const int nbig = c / 256 + (rem > 128), nsmall = rem > 0 && rem <= 128;
-  int tot, tot2, tot2s, rows_tot;
+  // Tiles of the 256-row kernel as (expert, first row, rows).  The kernel
+  // runs a tile of at most 128 rows over 4 M blocks and one of at most 192
+  // over 6, so a list of 256 f + r rows with 0 < r <= 64 ends in tiles of
+  // 192 and 64 + r rows rather than 256 and r (the weights are decoded once
+  // per tile, whatever its rows).  Table order: tiles of more than 192
+  // rows, then of 129-192, then of at most 128, so that the cheaper ones
+  // fill the launch's last round.
+  const int full = c / 256, rem = c % 256;
+  const bool split = full >= 1 && rem > 0 && rem <= 64;
+  const int n8 = split ? full - 1 : full + (rem > 192);
+  const int n6 = split ? 1 : (rem > 128 && rem <= 192);
+  const int n4 = split ? 1 : (rem > 0 && rem <= 128);
+  int tot, tot8, tot6, tot4, rows_tot;
   const int cin = block_scan_1024(c, wsum, &rows_tot);
-  const int tin2 = block_scan_1024(nbig, wsum, &tot2);
-  const int tin2s = block_scan_1024(nsmall, wsum, &tot2s);
+  const int tin8 = block_scan_1024(n8, wsum, &tot8);
+  const int tin6 = block_scan_1024(n6, wsum, &tot6);
+  const int tin4 = block_scan_1024(n4, wsum, &tot4);
   const int tin = block_scan_1024(nt, wsum, &tot);
   if (e < ne) {
     offsets[e] = cin - c;
@@ -942,21 +950,20 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
       tiles[2 * (t0 + k)] = e;
       tiles[2 * (t0 + k) + 1] = k * BM;
     }
-    const int u0 = tin2 - nbig;
-    for (int k = 0; k < nbig; ++k) {
-      tiles2[2 * (u0 + k)] = e;
-      tiles2[2 * (u0 + k) + 1] = k * 256;
-    }
-    if (nsmall) {
-      const int u = tot2 + tin2s - 1;
-      tiles2[2 * u] = e;
-      tiles2[2 * u + 1] = nbig * 256;
-    }
+    auto put = [&](int u, int r0, int rows) {
+      tiles2[3 * u] = e;
+      tiles2[3 * u + 1] = r0;
+      tiles2[3 * u + 2] = rows;
+    };
+    const int u8 = tin8 - n8;
+    for (int k = 0; k < n8; ++k) put(u8 + k, 256 * k, min(256, c - 256 * k));
+    if (n6) put(tot8 + tin6 - 1, 256 * n8, split ? 192 : rem);
+    if (n4) put(tot8 + tot6 + tin4 - 1, split ? 256 * n8 + 192 : 256 * n8, split ? 64 + rem : rem);
   }
   if (e == 0) {
     ntiles[0] = tot;
     ntiles[1] = rows_tot;  // compact rows in all lists
-    *ntiles2 = tot2 + tot2s;
+    *ntiles2 = tot8 + tot6 + tot4;
   }
 }
 
@@ -1095,7 +1102,7 @@ bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t h
   ws.ntiles = o;  o += align256(sizeof(int) * 4);
   ws.tiles = o;   o += align256(sizeof(int) * 2 * ws.max_tiles);
   ws.ntiles2 = o; o += align256(sizeof(int) * 4);
-  ws.tiles2 = o;  o += align256(sizeof(int) * 2 * ws.max_tiles2);
+  ws.tiles2 = o;  o += align256(sizeof(int) * 3 * ws.max_tiles2);
   ws.list = o;    o += align256(sizeof(int) * pairs);
   ws.rowmax = o;  o += align256(sizeof(uint32_t) * pairs);
   ws.hbuf = o;    o += align256(sizeof(float) * pairs * inter);    // h (128-row kernel) or g (256-row kernel)

@@ -485,7 +485,8 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
 #pragma unroll
   for (int i = 0; i < MI; ++i) acc[i] = (float16v){};
   // The loop over K for the first MA M blocks (a tile of at most 32 MA rows
-  // skips the MFMAs and fragment reads of the blocks past its rows).
+  // skips the MFMAs and fragment reads of the blocks past its rows; MA = 4,
+  // 6 or 8 for 256-row tiles).
   auto main_loop = [&](auto mac) __attribute__((always_inline)) {
     constexpr int MA = decltype(mac)::value;
     // activation fragment of k-step s: row 32 i + l % 32, piece 4 (s % 2) + 2 g + s / 2;
@@ -599,6 +600,8 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   if constexpr (MI == 8) {
     if (m_rows <= 128)
       main_loop(std::integral_constant<int, 4>{});
+    else if (m_rows <= 192)
+      main_loop(std::integral_constant<int, 6>{});
     else
       main_loop(std::integral_constant<int, 8>{});
   } else {
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     // column tile picks the segment (gate / up, or the down projection)
     const int ti = blockIdx.y;
     if (ti >= *pk.ntiles) return;
-    const int e = pk.tiles[2 * ti], r0 = pk.tiles[2 * ti + 1];
+    const int e = pk.tiles[3 * ti], r0 = pk.tiles[3 * ti + 1];
     const int base = pk.offsets[e] + r0;  // first compact row of the tile
     int sg = 0;
 #pragma unroll
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     p.w = pk.seg.w[sg] + (int64_t)e * pk.estride;
     p.n = pk.seg.n[sg];
     p.ldy = pk.seg.ldy[sg];
-    p.t = min(Cfg<QT, MI>::BMW, pk.counts[e] - r0);
+    p.t = pk.tiles[3 * ti + 2];  // the tile's rows
     p.list = pk.list + base;  // the tile's pairs
     if (pk.gather) {          // gate / up: X rows are the pairs' tokens, y the compact rows
       p.y = pk.seg.y[sg] + (int64_t)base * pk.seg.ldy[sg];

@@ -89,13 +89,16 @@ def test_wide_weights_exact(orc, qtype):
     weights.cache_clear()
 
 
-@pytest.mark.parametrize("qtype", [Q6_K, Q4_K], ids=["Q6_K", "Q4_K"])
-def test_plain_wide_dispatch(orc, qtype):
+@pytest.mark.parametrize("qtype,t", [(Q6_K, 4096), (Q4_K, 4096), (Q5_K, 4024), (Q2_K, 3950)],
+                         ids=["Q6_K", "Q4_K", "Q5_K-last-tile-184-rows", "Q2_K-last-tile-110-rows"])
+def test_plain_wide_dispatch(orc, qtype, t):
     """A plain projection large enough for whole rounds of 256 x 256 tiles
     (T = 4096, n = 8192: 512 tiles), with an odd number of blocks per row
-    (k = 1280: rows start 2 bytes into a dword for Q6_K on odd rows)."""
+    (k = 1280: rows start 2 bytes into a dword for Q6_K on odd rows); with a
+    ragged last token tile, that tile runs over 6 M blocks (129-192 rows)
+    or 4 (at most 128)."""
     import torch
-    t, n, k = 4096, 8192, 1280
+    n, k = 8192, 1280
     raw = weights(qtype, n, k, 9950 + qtype)
     x = act_f16(t, k, 9951)
     y = qp.prefill_gemm(qtype, to_dev(raw), n, k, to_dev(x).view(torch.float16))
