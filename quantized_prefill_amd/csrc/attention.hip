@@ -30,6 +30,8 @@
 // cache values rounded to binary16, scores and the softmax are f32
 // (exp2 of scale*log2(e)-scaled scores), P is rounded to binary16 for the
 // second product, O accumulates in f32 and is divided by the f32 row sum.
+#include <cfloat>
+
 #include "qp_device.h"
 #include "qp_internal.h"
 
@@ -153,6 +155,10 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
   const bool wave_live = q0w < p.t;
 
   // this wave's queries as the B operand of K . Q^T: query r, dims 16c + 8hh ..
+  // A negative scale negates Q (exact) so that the scores are scaled by
+  // csc = |scale| log2(e) > 0 (or 0) in the log2 domain.
+  const float csc = __builtin_fabsf(p.c);
+  const float qsign = p.c < 0.f ? -1.f : 1.f;
   half8 qf[8];
   {
     const int qi = q0w + r;
@@ -161,8 +167,8 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
     for (int c = 0; c < 8; ++c) {
       float4v a = {0, 0, 0, 0}, bq = {0, 0, 0, 0};
       if (qi < p.t) {
-        a = *(const float4v*)(qrow + 16 * c);
-        bq = *(const float4v*)(qrow + 16 * c + 4);
+        a = *(const float4v*)(qrow + 16 * c) * qsign;
+        bq = *(const float4v*)(qrow + 16 * c + 4) * qsign;
       }
       const u32x4 h = {pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]), pack_f16x2(bq[0], bq[1]),
                        pack_f16x2(bq[2], bq[3])};
@@ -251,20 +257,24 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[c], s[kt], 0, 0, 0);
         }
       }
-      // scale into the log2 domain, mask keys after the query, block maximum
-      const bool diag = key0 + kBK - 1 > qpos_lo;
+      // keys after the query to -inf (only blocks on the diagonal have any;
+      // the test is wave-uniform), then the block maximum of the raw scores:
+      // with csc > 0 the scaled maximum is csc times it, the same f32 value
+      // as the largest of the rounded products
+      if (key0 + kBK - 1 > qpos_lo) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int a = 0; a < 16; ++a)
+            if (key0 + 32 * kt + 8 * (a >> 2) + 4 * hh + (a & 3) > qpos) s[kt][a] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          float v = s[kt][a] * p.c;
-          if (diag && key0 + 32 * kt + 8 * (a >> 2) + 4 * hh + (a & 3) > qpos) v = -INFINITY;
-          s[kt][a] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[kt][a]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : mx * csc);
       // a row with no visible key yet (m_new = -inf) subtracts 0 instead, so
       // that exp2 sees -inf, never -inf - -inf
       const float m_sub = m_new == -INFINITY ? 0.f : m_new;
@@ -277,17 +287,32 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
           for (int a = 0; a < 16; ++a) o[dt][a] *= alpha;
       }
       m_run = m_new;
+      // p = 2^(csc s - m).  With |m| <= 1024 for every query of the wave, one
+      // fma: it differs from the rounded product minus m by at most half an
+      // ulp of m (2^-14), far below P's binary16 rounding.  Otherwise the
+      // rounded product first, so that the maximum's own p is exactly 1
+      // however large the scores.
+      const bool fused = __all(__builtin_fabsf(m_sub) <= 1024.f);
+      float pv[32];
+      if (fused) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) pv[e] = __builtin_fmaf(s[e >> 4][e & 15], csc, -m_sub);
+      } else {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) pv[e] = s[e >> 4][e & 15] * csc - m_sub;
+      }
       half8 pb[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + e] - m_sub);
-          l_part += pv[e];
+          pv[8 * st + e] = __builtin_amdgcn_exp2f(pv[8 * st + e]);
+          l_part += pv[8 * st + e];
         }
-        const u32x4 h = {pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
-                         pack_f16x2(pv[6], pv[7])};
+        const float* q8 = pv + 8 * st;
+        const u32x4 h = {pack_f16x2(q8[0], q8[1]), pack_f16x2(q8[2], q8[3]), pack_f16x2(q8[4], q8[5]),
+                         pack_f16x2(q8[6], q8[7])};
         pb[st] = __builtin_bit_cast(half8, h);
       }
       // k index 8hh + e of step st is key 16 st + 8 (e >> 2) + 4 hh + (e & 3)
@@ -373,6 +398,10 @@ hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void
   p.group = (int)(n_head / n_kv);
   p.nqt = (int)((t + kBM - 1) / kBM);
   p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  // a nonzero scale whose log2-domain factor rounds to 0 in f32 keeps the
+  // smallest normal magnitude instead (the softmax is uniform either way to
+  // well within f32), so that a masked score (-inf) times it stays -inf
+  if (p.c == 0.f && scale != 0.f) p.c = scale > 0.f ? FLT_MIN : -FLT_MIN;
   const int64_t blocks = (int64_t)p.nqt * n_head;
   p.xcd = blocks % (8 * p.group) == 0 ? 1 : 0;
   // one round of workgroups (two per CU): halves; more: single halves
