@@ -26,12 +26,12 @@
 // accumulator registers (the key order inside a 16-key step is the
 // accumulator's row order; V^T is read in that order).
 //
-// Numerics: Q is rounded to binary16 (nearest even), K and V are the exact
-// cache values rounded to binary16, scores and the softmax are f32
-// (exp2 of scale*log2(e)-scaled scores), P is rounded to binary16 for the
-// second product, O accumulates in f32 and is divided by the f32 row sum.
-#include <cfloat>
-
+// Numerics: Q is rounded to binary16 (nearest even; negated for a negative
+// scale), K and V are the exact cache values rounded to binary16, scores and
+// the softmax are f32 (exp2 of scale*log2(e)-scaled scores, the scaling and
+// the running maximum's subtraction one fma while the maxima are within
+// 1024), P is rounded to binary16 for the second product, O accumulates in
+// f32 and is divided by the f32 row sum.
 #include "qp_device.h"
 #include "qp_internal.h"
 
@@ -397,11 +397,10 @@ hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void
   p.n_kv = (int)n_kv;
   p.group = (int)(n_head / n_kv);
   p.nqt = (int)((t + kBM - 1) / kBM);
-  p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  // a nonzero scale whose log2-domain factor rounds to 0 in f32 keeps the
-  // smallest normal magnitude instead (the softmax is uniform either way to
-  // well within f32), so that a masked score (-inf) times it stays -inf
-  if (p.c == 0.f && scale != 0.f) p.c = scale > 0.f ? FLT_MIN : -FLT_MIN;
+  // log2(e) > 1, so a nonzero f32 scale never rounds to a zero factor (a
+  // subnormal one is kept: the kernels run with f32 denormals), and a masked
+  // score (-inf) times it stays -inf
+  p.c = (float)((double)scale * 1.4426950408889634);
   const int64_t blocks = (int64_t)p.nqt * n_head;
   p.xcd = blocks % (8 * p.group) == 0 ? 1 : 0;
   // one round of workgroups (two per CU): halves; more: single halves

@@ -81,6 +81,20 @@ def test_attention_sharp_scores(orc):
     assert_close(y, ref, "attention sharp")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 1e-44], ids=["negative", "subnormal"])
+def test_attention_unusual_scales(orc, scale):
+    """A negative scale (the kernel negates Q, exact in binary16) and a
+    subnormal one (the softmax is uniform over the visible keys, and masked
+    keys still get none of it)."""
+    t, n_head, n_kv = 200, 4, 2
+    q = queries(t, n_head, 12650)
+    kc = synth.kv_cache(F16W, t, n_kv, HD, 12651)
+    vc = synth.kv_cache(F16W, t, n_kv, HD, 12652)
+    y = run_attention(F16W, q, kc, vc, 0, n_head, n_kv, scale=scale)
+    ref = orc.attention(F16W, q, kc, vc, 0, n_head, n_kv, HD, scale=scale)
+    assert_close(y, ref, f"attention scale {scale}")
+
+
 def test_attention_deterministic():
     t, n_head, n_kv = 333, 8, 2
     q = queries(t, n_head, 12700)
