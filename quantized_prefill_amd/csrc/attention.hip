@@ -274,19 +274,24 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[kt][a]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : mx * csc);
-      // a row with no visible key yet (m_new = -inf) subtracts 0 instead, so
-      // that exp2 sees -inf, never -inf - -inf
-      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
-      l_part *= alpha;
-      if (__any(m_new != m_run)) {  // the maximum moved for some query of the wave
+      const float m_blk = mx == -INFINITY ? -INFINITY : mx * csc;
+      // The running maximum moves only in a block where some query of the
+      // wave sees a scaled score more than 8 above it (always at its first
+      // visible key): in the others p is at most 2^8, which binary16 holds at
+      // full precision, and O and the row sums need no rescale.
+      if (__any(m_blk > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, m_blk);
+        // a row with no visible key yet keeps -inf and subtracts 0 instead,
+        // so that exp2 sees -inf, never -inf - -inf
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_part *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int a = 0; a < 16; ++a) o[dt][a] *= alpha;
+        m_run = m_new;
       }
-      m_run = m_new;
+      const float m_sub = m_run == -INFINITY ? 0.f : m_run;
       // p = 2^(csc s - m).  With |m| <= 1024 for every query of the wave, one
       // fma: it differs from the rounded product minus m by at most half an
       // ulp of m (2^-14), far below P's binary16 rounding.  Otherwise the
