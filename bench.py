@@ -40,7 +40,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_wide_q6k_gate_up_qwe
 # kernel with weights decoded in registers, for Q6_K weights, running the
 # gate and up projections of the 8B layer at T = 2048 in one launch (768
 # tiles): the layer's largest share of flops.
-DOMINANT = "gemm_wide_kernel<14, 5, 8> (Q6_K gate and up in one launch, f16 X, 256 x 256 tiles)"
+DOMINANT = "gemm_wide_kernel<14, 5, 8, 1> (Q6_K gate and up in one launch, f16 X, 256 x 256 tiles)"
 DOMINANT_PROJS = ("gate", "up")
 KERNEL_SOURCES = ("gemm_wide.hip", "gemm_common.h", "qp_device.h", "qp_internal.h")
 
