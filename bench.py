@@ -235,6 +235,35 @@ def time_fn(torch, fn, iters):
     return s.elapsed_time(e) / iters  # ms
 
 
+def raw_gemm(torch, qp, qtype, w, n, k, x, y):
+    """qp_prefill_gemm_ws with its arguments prepared once (the binding's
+    cached workspace): a row of launches of ten microseconds then times the
+    library's launches, not the binding's per-call argument checks."""
+    t = x.shape[0]
+    xd = qp.F16 if x.dtype == torch.float16 else qp.F32
+    ws = qp.gemm_workspace(n, k, t, x.device)
+    args = (qtype, w.data_ptr(), n, k, x.data_ptr(), xd, t, x.stride(0), y.data_ptr(), y.stride(0),
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+            torch.cuda.current_stream().cuda_stream)
+    fn = qp.lib().qp_prefill_gemm_ws
+
+    def call():
+        if fn(*args) != 0:
+            raise RuntimeError("qp_prefill_gemm_ws failed")
+    return call
+
+
+def raw_dequant_f32(torch, qp, qtype, w, rows, cols, out):
+    """qp_dequant_f32 with its arguments prepared once (as raw_gemm)."""
+    args = (qtype, w.data_ptr(), rows, cols, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    fn = qp.lib().qp_dequant_f32
+
+    def call():
+        if fn(*args) != 0:
+            raise RuntimeError("qp_dequant_f32 failed")
+    return call
+
+
 ROW_GROUPS = ("q8_0", "q4_k_1p7b", "q5_k_8b", "qknorm", "moe", "attention")
 
 
@@ -272,9 +301,9 @@ def _rows_q8_0(torch, synth, qp, iters, dev):
     w = d(synth.quant_weights(synth.Q8_0, 1024, 1024, synth.seed_for(0, 0)))
     x = d(synth.activations_f32(64, 1024, synth.seed_for(0, 1)))
     y = torch.empty((64, 1024), device=dev)
-    ms = time_fn(torch, lambda: qp.prefill_gemm(synth.Q8_0, w, 1024, 1024, x, out=y), iters)
+    ms = time_fn(torch, raw_gemm(torch, qp, synth.Q8_0, w, 1024, 1024, x, y), iters)
     o32 = torch.empty((1024, 1024), device=dev)
-    msd = time_fn(torch, lambda: qp.dequant_f32(synth.Q8_0, w, 1024, 1024, out=o32), iters)
+    msd = time_fn(torch, raw_dequant_f32(torch, qp, synth.Q8_0, w, 1024, 1024, o32), iters)
     rows["q8_0_1024_t64"] = dict(gemm_tflops=2 * 64 * 1024 * 1024 / ms / 1e9, gemm_us=ms * 1e3,
                                  dequant_f32_gbps=(1024 * 1088 + 1024 * 1024 * 4) / msd / 1e6)
     return rows
@@ -292,10 +321,10 @@ def _rows_q4_k_1p7b(torch, synth, qp, iters, dev):
         w = d(synth.quant_weights(synth.Q4_K, n, k, synth.seed_for(1, i)))
         x = d(synth.activations_f16(512, k, synth.seed_for(1, 500 + k // 256))).view(torch.float16)
         y = torch.empty((512, n), device=dev)
-        tms += time_fn(torch, lambda: qp.prefill_gemm(synth.Q4_K, w, n, k, x, out=y), iters)
+        tms += time_fn(torch, raw_gemm(torch, qp, synth.Q4_K, w, n, k, x, y), iters)
         flops += 2.0 * 512 * n * k
         o32 = torch.empty((n, k), device=dev)
-        dms += time_fn(torch, lambda: qp.dequant_f32(synth.Q4_K, w, n, k, out=o32), iters)
+        dms += time_fn(torch, raw_dequant_f32(torch, qp, synth.Q4_K, w, n, k, o32), iters)
         dbytes += n * synth.row_bytes(synth.Q4_K, k) + 4.0 * n * k
     rows["q4_k_qwen3_1p7b_t512"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
                                         dequant_f32_gbps=dbytes / dms / 1e6)
@@ -316,10 +345,10 @@ def _rows_q5_k_8b(torch, synth, qp, iters, dev):
             x8[k] = d(synth.activations_f16(2048, k, synth.seed_for(2, 500 + k // 256))).view(torch.float16)
         w = d(synth.quant_weights(synth.Q5_K, n, k, synth.seed_for(2, 10 * synth.Q5_K + i)))
         y = torch.empty((2048, n), device=dev)
-        tms += time_fn(torch, lambda: qp.prefill_gemm(synth.Q5_K, w, n, k, x8[k], out=y), iters)
+        tms += time_fn(torch, raw_gemm(torch, qp, synth.Q5_K, w, n, k, x8[k], y), iters)
         flops += 2.0 * 2048 * n * k
         o32 = torch.empty((n, k), device=dev)
-        dms += time_fn(torch, lambda: qp.dequant_f32(synth.Q5_K, w, n, k, out=o32), iters)
+        dms += time_fn(torch, raw_dequant_f32(torch, qp, synth.Q5_K, w, n, k, o32), iters)
         dbytes += n * synth.row_bytes(synth.Q5_K, k) + 4.0 * n * k
         del w, y, o32
     rows["q5_k_qwen3_8b_t2048"] = dict(gemm_tflops=flops / tms / 1e9, gemm_us=tms * 1e3,
