@@ -417,6 +417,34 @@ qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const vo
                               int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
                               float scale, float* out, int64_t ldo, hipStream_t stream);
 
+/*
+ * Bytes of the workspace qp_prompt_attention_ws takes for a Q8_0 or Q4_0
+ * cache of kv_len tokens: the binary16 rows of both caches (0 for any other
+ * kv_type or head_dim, kv_len <= 0 or n_kv_head outside 1..1024).  Same
+ * passage as qp_prompt_attention.
+ */
+size_t qp_prompt_attention_workspace_bytes(int kv_type, int64_t kv_len, int64_t n_kv_head, int64_t head_dim);
+
+/*
+ * qp_prompt_attention with a workspace (same passage).  For a Q8_0 or Q4_0
+ * cache the kv_len * n_kv_head rows of both caches are first decoded into
+ * binary16 rows in the workspace (the values the attention itself stages from
+ * them, bit for bit: one pass over the caches instead of one per query tile
+ * and head), then the attention runs over those rows; the output is bitwise
+ * that of qp_prompt_attention.
+ *   workspace (device, owned by the caller, 16-byte aligned): at least
+ *               qp_prompt_attention_workspace_bytes(kv_type, n_past + t,
+ *               n_kv_head, head_dim) bytes; NULL: exactly qp_prompt_attention.
+ *               A binary16 cache ignores it.  Calls sharing a workspace must
+ *               not run concurrently.
+ * Errors: as qp_prompt_attention; QP_ERR_WORKSPACE_TOO_SMALL for a non-NULL
+ * workspace below the query, QP_ERR_INVALID_PARAMETER for a misaligned one.
+ */
+qp_status qp_prompt_attention_ws(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                                 int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
+                                 float scale, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* Static English name of a status ("QP_OK", ...): the error kinds of the
  * aprender issue's "Cause" (an unsupported type is an InvalidParameter-style
  * error and the call fails closed). */

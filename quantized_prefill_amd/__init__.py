@@ -45,6 +45,9 @@ SIGNATURES = {
     "qp_rope": (_INT, [_VP, _I64, _I64, _I64, _I64, _I64, C.c_double, _VP]),
     "qp_kv_cache_write": (_INT, [_INT, _VP, _I64, _I64, _I64, _I64, _VP, _I64, _VP]),
     "qp_prompt_attention": (_INT, [_INT, _VP, _I64, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _F32C, _VP, _I64, _VP]),
+    "qp_prompt_attention_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
+    "qp_prompt_attention_ws": (_INT, [_INT, _VP, _I64, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _F32C, _VP, _I64, _VP,
+                                      _SZ, _VP]),
     "qp_status_string": (C.c_char_p, [_INT]),
     "qp_last_error_detail": (C.c_char_p, []),
 }
@@ -182,6 +185,7 @@ _BLOCK_TYPES = (F16W, Q8_0, Q2_K, Q4_K, Q5_K, Q6_K)
 # caching allocator only after the work already queued on its stream.
 _GEMM_WORKSPACE = {}
 _QKV_WORKSPACE = {}
+_ATTN_WORKSPACE = {}
 
 
 def _workspace_key(device, stream: int):
@@ -440,11 +444,24 @@ def kv_cache_write(kv_type: int, src, n_kv_head: int, head_dim: int, cache, row0
     return cache
 
 
+def attention_workspace(kv_type: int, kv_len: int, n_kv_head: int, head_dim: int, device, stream=None):
+    """Workspace for prompt_attention over a Q8_0 or Q4_0 cache of kv_len
+    tokens (None for a binary16 cache), kept per device and stream and grown
+    as needed."""
+    nbytes = lib().qp_prompt_attention_workspace_bytes(kv_type, kv_len, n_kv_head, head_dim)
+    if nbytes == 0:
+        return None
+    return _cached_workspace(_ATTN_WORKSPACE, nbytes, device, stream)
+
+
 def prompt_attention(kv_type: int, q, k_cache, v_cache, n_past: int, n_head: int, n_kv_head: int,
-                     head_dim: int = 128, scale: float | None = None, out=None):
+                     head_dim: int = 128, scale: float | None = None, out=None, workspace=None):
     """Causal prompt attention of a chunk of q.shape[0] queries over a KV cache of
     n_past + q.shape[0] tokens (flat byte tensors of binary16, Q8_0 or Q4_0 rows).
-    scale None takes the library's default, 1 / sqrt(head_dim)."""
+    scale None takes the library's default, 1 / sqrt(head_dim).  workspace: a
+    uint8 GPU tensor, None for the cached one (attention_workspace: a quantized
+    cache is decoded to binary16 rows once per call), or False for none (the
+    kernel decodes as it stages; the output is the same bit for bit)."""
     torch = _torch()
     t = q.shape[0]
     if scale is None:
@@ -459,7 +476,15 @@ def prompt_attention(kv_type: int, q, k_cache, v_cache, n_past: int, n_head: int
         kv_bytes = (n_past + t) * n_kv_head * row_bytes(kv_type, head_dim) if row_bytes(kv_type, head_dim) > 0 else 0
         _need_bytes(k_cache, kv_bytes, "k_cache")
         _need_bytes(v_cache, kv_bytes, "v_cache")
-    check(lib().qp_prompt_attention(kv_type, _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
-                                    _dev(v_cache, "v_cache"), n_past, t, n_head, n_kv_head, head_dim, float(scale),
-                                    _dev(out, "out"), out.stride(0), _stream()))
+    ptrs = (_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"))
+    ws = None
+    if t > 0 and workspace is not False:
+        ws = attention_workspace(kv_type, n_past + t, n_kv_head, head_dim, q.device) if workspace is None else workspace
+        if ws is not None:
+            _need_bytes(ws, lib().qp_prompt_attention_workspace_bytes(kv_type, n_past + t, n_kv_head, head_dim),
+                        "workspace")
+    check(lib().qp_prompt_attention_ws(kv_type, ptrs[0], q.stride(0), ptrs[1], ptrs[2], n_past, t, n_head, n_kv_head,
+                                       head_dim, float(scale), ptrs[3], out.stride(0),
+                                       _dev(ws, "workspace") if ws is not None else None,
+                                       ws.numel() if ws is not None else 0, _stream()))
     return out

@@ -316,9 +316,18 @@ qp_status qp_kv_cache_write(int kv_type, const float* src, int64_t lds, int64_t 
                   "kv write launch");
 }
 
-qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
-                              int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
-                              float scale, float* out, int64_t ldo, hipStream_t stream) {
+size_t qp_prompt_attention_workspace_bytes(int kv_type, int64_t kv_len, int64_t n_kv_head, int64_t head_dim) {
+  if ((kv_type != QP_Q8_0 && kv_type != QP_Q4_0) || head_dim != 128 || kv_len <= 0 || kv_len >= ((int64_t)1 << 31) ||
+      n_kv_head < 1 || n_kv_head > 1024)
+    return 0;
+  const int64_t one = kv_len * n_kv_head * head_dim * 2;  // binary16 rows of one cache
+  return (size_t)(2 * ((one + 255) / 256 * 256));
+}
+
+static qp_status attention_impl(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                                int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
+                                float scale, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   if (kv_type != QP_F16W && kv_type != QP_Q8_0 && kv_type != QP_Q4_0)
     return fail(QP_ERR_UNSUPPORTED_TYPE, "no prompt attention over a KV cache of ggml type %d", kv_type);
   if (head_dim != 128) return fail(QP_ERR_INVALID_PARAMETER, "head_dim %lld (only 128)", (long long)head_dim);
@@ -339,9 +348,39 @@ qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const vo
   const size_t cache_align = kv_type == QP_F16W ? 16 : 2;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, cache_align) || !aligned(v_cache, cache_align))
     return fail(QP_ERR_INVALID_PARAMETER, "misaligned pointer");
+  if (workspace != nullptr && kv_type != QP_F16W) {
+    // decode both caches once into binary16 rows, then attend over those
+    const int64_t kv_len = n_past + t;
+    const size_t need = qp_prompt_attention_workspace_bytes(kv_type, kv_len, n_kv_head, head_dim);
+    if (workspace_bytes < need)
+      return fail(QP_ERR_WORKSPACE_TOO_SMALL, "attention workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned(workspace, 16)) return fail(QP_ERR_INVALID_PARAMETER, "misaligned workspace");
+    uint8_t* kf = (uint8_t*)workspace;
+    uint8_t* vf = kf + need / 2;
+    hipError_t e = qp::launch_kv_decode_f16(kv_type, k_cache, kv_len * n_kv_head, kf, stream);
+    if (e == hipSuccess) e = qp::launch_kv_decode_f16(kv_type, v_cache, kv_len * n_kv_head, vf, stream);
+    if (e == hipSuccess)
+      e = qp::launch_attention(QP_F16W, q, ldq, kf, vf, n_past, t, n_head, n_kv_head, scale, out, ldo, stream);
+    return from_hip(e, "attention launch");
+  }
   return from_hip(qp::launch_attention(kv_type, q, ldq, k_cache, v_cache, n_past, t, n_head, n_kv_head, scale, out,
                                        ldo, stream),
                   "attention launch");
+}
+
+qp_status qp_prompt_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                              int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
+                              float scale, float* out, int64_t ldo, hipStream_t stream) {
+  return attention_impl(kv_type, q, ldq, k_cache, v_cache, n_past, t, n_head, n_kv_head, head_dim, scale, out, ldo,
+                        nullptr, 0, stream);
+}
+
+qp_status qp_prompt_attention_ws(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                                 int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,
+                                 float scale, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return attention_impl(kv_type, q, ldq, k_cache, v_cache, n_past, t, n_head, n_kv_head, head_dim, scale, out, ldo,
+                        workspace, workspace_bytes, stream);
 }
 
 const char* qp_status_string(qp_status s) {

@@ -212,3 +212,24 @@ def test_rope_and_kv_write_rejections():
     assert w(qp.F16W, FAKE, 1024, 8, 8, 128, FAKE + 2, 0, None) == 1  # binary16 cache needs 4 bytes
     assert w(qp.Q4_0, None, 1024, 0, 8, 128, None, 0, None) == 0  # t == 0
 
+
+
+def test_attention_workspace_query_and_rejections():
+    """qp_prompt_attention_workspace_bytes: two binary16 copies of the cache
+    for Q8_0 and Q4_0, 0 otherwise; qp_prompt_attention_ws rejects a short or
+    misaligned workspace before any launch."""
+    L = qp.lib()
+    q = L.qp_prompt_attention_workspace_bytes
+    assert q(qp.Q8_0, 2048, 8, 128) == 2 * 2048 * 8 * 128 * 2
+    assert q(qp.Q4_0, 1, 1, 128) == 2 * 256
+    assert q(qp.F16W, 2048, 8, 128) == 0
+    assert q(qp.Q8_0, 2048, 8, 64) == 0
+    assert q(qp.Q8_0, 0, 8, 128) == 0
+    assert q(qp.Q8_0, 16, 0, 128) == 0
+    A = L.qp_prompt_attention_ws
+    need = q(qp.Q8_0, 8, 8, 128)
+    args = [qp.Q8_0, FAKE, 4096, FAKE, FAKE, 0, 8, 32, 8, 128, 0.0, FAKE, 4096]
+    assert A(*args, FAKE, need - 1, None) == 3   # QP_ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in L.qp_last_error_detail()
+    assert A(*args, FAKE + 8, need, None) == 1   # not 16-byte aligned
+    assert A(*(args[:6] + [0] + args[7:]), None, 0, None) == 0   # empty chunk: nothing to do

@@ -19,14 +19,15 @@ def queries(t: int, n_head: int, seed: int, ldq: int | None = None) -> np.ndarra
     return q
 
 
-def run_attention(kvtype, q, kc, vc, n_past, n_head, n_kv, scale=None, ldo=None):
+def run_attention(kvtype, q, kc, vc, n_past, n_head, n_kv, scale=None, ldo=None, workspace=None):
     import torch
     qd = to_dev(q)
     t = q.shape[0]
     out = None
     if ldo is not None:
         out = torch.full((t, ldo), float("nan"), dtype=torch.float32, device="cuda")
-    y = qp.prompt_attention(kvtype, qd, to_dev(kc), to_dev(vc), n_past, n_head, n_kv, HD, scale, out=out)
+    y = qp.prompt_attention(kvtype, qd, to_dev(kc), to_dev(vc), n_past, n_head, n_kv, HD, scale, out=out,
+                            workspace=workspace)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -93,6 +94,24 @@ def test_attention_unusual_scales(orc, scale):
     y = run_attention(F16W, q, kc, vc, 0, n_head, n_kv, scale=scale)
     ref = orc.attention(F16W, q, kc, vc, 0, n_head, n_kv, HD, scale=scale)
     assert_close(y, ref, f"attention scale {scale}")
+
+
+@pytest.mark.parametrize("kvtype", [Q8_0, Q4_0], ids=["Q8_0", "Q4_0"])
+@pytest.mark.parametrize("t,n_past,n_head,n_kv", [(200, 77, 8, 4), (2048, 0, 32, 8), (2200, 0, 32, 8)],
+                         ids=["prefix", "one-round-halves", "single-halves"])
+def test_attention_decoded_cache_bitwise(orc, kvtype, t, n_past, n_head, n_kv):
+    """The workspace call decodes the quantized caches to binary16 rows first
+    and attends over those; its output equals the call that decodes while
+    staging, bit for bit (the binding's default is the workspace call, which
+    every other test here checks against the oracle)."""
+    seed = 13000 + t + n_past
+    q = queries(t, n_head, seed)
+    kc = synth.kv_cache(kvtype, n_past + t, n_kv, HD, seed + 1)
+    vc = synth.kv_cache(kvtype, n_past + t, n_kv, HD, seed + 2)
+    say(f"attention decoded cache {synth.NAMES[kvtype]} t={t} past={n_past}")
+    a = run_attention(kvtype, q, kc, vc, n_past, n_head, n_kv)
+    b = run_attention(kvtype, q, kc, vc, n_past, n_head, n_kv, workspace=False)
+    assert np.array_equal(a, b), "decoded-cache attention differs from the in-kernel decode"
 
 
 def test_attention_deterministic():
