@@ -3,16 +3,16 @@
 // ("QK-norm models take the FP16 batched prefill", section "What changes":
 // chunked batched prefill in FP16; the QK norm is per head).
 //
-// One wave per SIMD.  A workgroup of 4 waves owns a tile of BMW tokens x
-// BNW output features; wave w owns all BMW tokens of features
-// 32*NJ*w .. 32*NJ*w + 32*NJ - 1, i.e. MI x NJ MFMA tiles of 32 x 32
-// (v_mfma_f32_32x32x16_f16, f32 accumulators).  Each wave decodes the
-// weights of its own features straight into the MFMA B-operand registers, so
-// a weight is decoded once per tile and never goes through LDS as binary16.
-// Measured on MI355X: one wave per SIMD issuing independent MFMAs keeps the
-// matrix unit 97% busy with 2 independent VALU ops between MFMAs and 94%
-// with 4, so the decode arithmetic (2.5-3 VALU per weight, about 3 per MFMA
-// at 256 tokens) issues beside the MFMAs of the same wave.
+// Two waves per SIMD.  A workgroup of 8 waves owns a tile of BMW = 32 MI
+// tokens x BNW = 256 output features; wave w owns all BMW tokens of features
+// 32 w .. 32 w + 31, i.e. MI MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_f16,
+// f32 accumulators).  Each wave decodes the weights of its own features
+// straight into the MFMA B-operand registers, so a weight is decoded once
+// per tile and never goes through LDS as binary16, and one 16-byte LDS read
+// of the activations feeds each MFMA.  The decode arithmetic (2.5-3 VALU per
+// weight, about 4-5 VALU per MFMA at 256 tokens) issues beside the other
+// wave's MFMAs on the same SIMD.  With K slices (KS = 2 or 4, below) the 8
+// waves form KS groups over the parts of K, each owning 256 / KS features.
 //
 // K order.  K advances in chunks of 64 weights (4 MFMA k-steps of 16).
 // Inside a chunk, k-step s takes, for lanes 0-31 (g = 0) and 32-63 (g = 1),
