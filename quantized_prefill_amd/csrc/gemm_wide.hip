@@ -57,6 +57,8 @@ template <int QT> struct Stage;
 // the half (3), d (1).
 template <> struct Stage<kQ6_K> {
   static constexpr int NDW = 30, RSD = 31, TS = 210;
+  static constexpr bool P16 = false;
+  static constexpr int NP = 0;
   static __device__ __forceinline__ uint32_t off(int d, int h) {
     return d < 17 ? 64 * h + 4 * d : d < 26 ? 128 + 32 * h + 4 * (d - 17) : d < 29 ? 192 + 8 * h + 4 * (d - 26) : 208;
   }
@@ -65,23 +67,34 @@ template <> struct Stage<kQ6_K> {
 // qs[32h, +32) (8), d and dmin (1).
 template <> struct Stage<kQ2_K> {
   static constexpr int NDW = 11, RSD = 11, TS = 84;
+  static constexpr bool P16 = false;
+  static constexpr int NP = 0;
   static __device__ __forceinline__ uint32_t off(int d, int h) {
     return d < 2 ? 8 * h + 4 * d : d < 10 ? 16 + 32 * h + 4 * (d - 2) : 80;
   }
 };
 // Q4_K half h (16-byte aligned blocks): d, dmin and the 12 scale bytes (4
-// dwords), qs[64h, +64) (16).
+// dwords), qs[64h, +64) (16).  P16: staged as NP = 5 pieces of 16 bytes,
+// rows NDW dwords apart (an odd number of pieces, so the 16 rows of a
+// 16-byte read land in 16 distinct bank groups); off16(j, h) is the byte
+// offset of piece j within the block.
 template <> struct Stage<kQ4_K> {
-  static constexpr int NDW = 20, RSD = 21, TS = 144;
+  static constexpr int NDW = 20, RSD = 20, TS = 144;
+  static constexpr bool P16 = true;
+  static constexpr int NP = 5;
   static __device__ __forceinline__ uint32_t off(int d, int h) { return d < 4 ? 4 * d : 16 + 64 * h + 4 * (d - 4); }
+  static __device__ __forceinline__ uint32_t off16(int j, int h) { return j == 0 ? 0u : 16u + 64u * h + 16u * (j - 1); }
 };
 // Q5_K half h: header (4 dwords), qh[32] (8: every weight of the block has
 // its fifth bit there), qs[64h, +64) (16).
 template <> struct Stage<kQ5_K> {
-  static constexpr int NDW = 28, RSD = 29, TS = 176;
+  static constexpr int NDW = 28, RSD = 28, TS = 176;
+  static constexpr bool P16 = true;
+  static constexpr int NP = 7;
   static __device__ __forceinline__ uint32_t off(int d, int h) {
     return d < 12 ? 4 * d : 48 + 64 * h + 4 * (d - 12);
   }
+  static __device__ __forceinline__ uint32_t off16(int j, int h) { return j < 3 ? 16u * j : 48u + 64u * h + 16u * (j - 3); }
 };
 
 // One decode unit: 16 weights (run r of chunk O of a step) of one row, the
@@ -303,12 +316,15 @@ struct Cfg {
   static constexpr int RSD = Stage<QT>::RSD;
   static constexpr int R = 64 / RSD;                       // rows per staging instruction
   static constexpr int NG = (BNW + R - 1) / R;             // groups of R rows per tile
-  static constexpr int NI = (NG + NWS - 1) / NWS;          // staging instructions per wave and step
+  static constexpr int NI16 = Stage<QT>::NP * BNW / 64;   // P16 types: 16-byte staging loads per tile and step
+  static constexpr int NI = Stage<QT>::P16 ? (NI16 + NWS - 1) / NWS : (NG + NWS - 1) / NWS;  // per wave and step
   static constexpr int XTILE = BMW * 64;                   // halfs per activation chunk
   static constexpr int RAWB = BNW * RSD + 64;              // dwords per staging buffer (64 of padding)
   static constexpr int XB = 3;
   static constexpr int XL = BMW * 8 / 64 / NWS;            // activation loads per wave and chunk (16 B per lane)
   static_assert((NG - 1) * R * RSD + 64 <= RAWB, "the padding takes the last group's spare lanes");
+  static_assert(!Stage<QT>::P16 || (NI16 * 64 == Stage<QT>::NP * BNW && RSD == 4 * Stage<QT>::NP),
+                "16-byte staging: whole loads per tile, rows of NP pieces");
   static_assert(KS * (XB * XTILE * 2 + 2 * RAWB * 4) <= kLds, "LDS budget");
   static_assert(XL * NWS * 64 == BMW * 8, "whole activation loads per wave");
   static_assert((KS - 1) * NWS * MI * 16 * 64 <= XB * XTILE / 2 * KS, "the slice sums fit the activation buffers");
@@ -425,6 +441,20 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   uint32_t vo00, vo_a, vo_h, vl00, vl_a, vl_h;
   lane_off(sgr, vo00, vo_a, vo_h);
   lane_off(sgr_last, vl00, vl_a, vl_h);
+  // P16 types: load q of wave w is load gi = NWS q + w of the tile (past the
+  // last: the last again); lane L copies piece P = 64 gi + L of the staged
+  // rows, piece P % NP of row P / NP, to LDS dword 4 P (row pitch 4 NP)
+  uint32_t v16a[S::P16 ? NI : 1], v16b[S::P16 ? NI : 1];  // step halves 0 and 1
+  if constexpr (S::P16) {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int gi = min(NWS * q + w, C::NI16 - 1);
+      const int pc = 64 * gi + lane;
+      const int row = pc / S::NP, j = pc - row * S::NP;
+      v16a[q] = (uint32_t)(row * rb) + S::off16(j, 0);
+      v16b[q] = (uint32_t)(row * rb) + S::off16(j, 1);
+    }
+  }
   // part [Q0, Q1) of the loads of step st (clamped to the last step) into buffer buf
   auto stage_part = [&](int st, int buf, auto q0c, auto q1c) __attribute__((always_inline)) {
     constexpr int Q0 = decltype(q0c)::value, Q1 = decltype(q1c)::value;
@@ -432,7 +462,21 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
     const int u = (st >> 1) + ub0, h = st & 1;
     const uint32_t boff = (uint32_t)u * S::TS;
     uint32_t* dst = sm.raw[ks][buf];
-    if constexpr (FULL) {
+    if constexpr (S::P16) {
+      // whole 16-byte pieces; rows past the tensor (not FULL) read zeros
+      // past wrsrc_part's record count, as below
+#pragma unroll
+      for (int q = Q0; q < Q1; ++q) {
+        const int gi = min(NWS * q + w, C::NI16 - 1);
+        const uint32_t v = h ? v16b[q] : v16a[q];
+        if constexpr (FULL)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (__attribute__((address_space(3))) void*)(dst + 256 * gi), 16,
+                                                   (int)v, (int)boff, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc_part, (__attribute__((address_space(3))) void*)(dst + 256 * gi),
+                                                   16, (int)(v + boff), 0, 0, 0);
+      }
+    } else if constexpr (FULL) {
       const uint32_t ab = (boff >> 1) & 1u;
       const uint32_t v0 = vo00 + ab * vo_a + (uint32_t)h * vo_h;
       const uint32_t vl = vl00 + ab * vl_a + (uint32_t)h * vl_h;
