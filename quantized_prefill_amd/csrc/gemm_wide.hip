@@ -550,13 +550,15 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
     using I1 = std::integral_constant<int, 1>;
 
     // ---- prologue: steps 0 and 1 staged, activation chunks 0 .. 2; chunk 0's
-    // slots 0..2 decoded (slot 3 in the loop's first k-step)
+    // slots 0..2 decoded (slot 3 in the loop's first k-step).  Only step 0
+    // and chunk 0 are waited for here (issued first); step 1 and chunk 1 land
+    // by chunk 0's barrier, whose wait leaves only chunk 2 in flight.
     stage_part(0, 0, P0{}, P4{});
-    stage_part(1, 1, P0{}, P4{});
     load_x(0);
+    stage_part(1, 1, P0{}, P4{});
     load_x(1);
     load_x(2);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm<NI + 2 * XL>();
     lds_barrier();
     {
       const char* ap = a_ptr(0, 0);
