@@ -43,8 +43,9 @@ constexpr int kWaves = 4;            // per half
 constexpr int kBM = 32 * kWaves;     // queries per workgroup
 constexpr int kBK = 64;              // keys per staged block
 constexpr int kKP = kD + 8;          // K row pitch in halves: 16-lane reads hit distinct banks
-constexpr int kVP = kBK + 4;         // V^T row pitch in halves: 34 dwords, 32 rows on distinct bank pairs
-constexpr int kStage = kBK * kKP + kD * kVP;  // halves per stage
+constexpr int kVP = kD + 32;         // V row pitch in halves: 80 dwords, so the 4 key rows of a 32-lane
+                                     // transposed read fall in 4 disjoint 16-bank groups
+constexpr int kStage = kBK * kKP + kBK * kVP;  // halves per stage
 
 struct AttnArgs {
   const float* q;
@@ -182,10 +183,9 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
   const uint8_t* kbase = p.kc + (int64_t)g * C::kRowBytes;
   const uint8_t* vbase = p.vc + (int64_t)g * C::kRowBytes;
 
-  // staging.  K chunk j of this thread: key (tid + 256 j) >> 4, dims
-  // 8 * (tid & 15) ..  (16 lanes read one row).  V chunk j: key
-  // 2 * (tid & 31) + (j & 1), dims 8 * ((tid >> 5) + 8 * (j >> 1)) .. : the
-  // two keys of a pair go to V^T as one 32-bit word per dim.
+  // staging.  K and V chunk j of this thread: key (tid + 256 j) >> 4, dims
+  // 8 * (tid & 15) ..  (16 lanes read one row); both stored as rows, V^T's
+  // operands come from V's rows by transposed reads.
   C kch[4], vch[4];
   auto load_block = [&](int kb) {
 #pragma unroll
@@ -195,28 +195,20 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
         kch[j].load(kbase + key * row_stride, tid & 15);
       else
         kch[j].zero();
-      const int vkey = kb * kBK + 2 * (tid & 31) + (j & 1);
-      if (vkey < p.kv_len)
-        vch[j].load(vbase + vkey * row_stride, (tid >> 5) + 8 * (j >> 1));
+      if (key < p.kv_len)
+        vch[j].load(vbase + key * row_stride, tid & 15);
       else
         vch[j].zero();
     }
   };
   auto store_block = [&](int buf) {
     _Float16* ks = lds + buf * kStage;
-    _Float16* vt = ks + kBK * kKP;
+    _Float16* vs = ks + kBK * kKP;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4*)(ks + ((tid + 256 * j) >> 4) * kKP + 8 * (tid & 15)) = kch[j].halves();
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const u32x4 a = vch[2 * pr].halves(), b = vch[2 * pr + 1].halves();
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-      uint32_t* col = (uint32_t*)(vt + 8 * ((tid >> 5) + 8 * pr) * kVP + 2 * (tid & 31));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        col[(2 * e) * (kVP / 2)] = (av[e] & 0xFFFFu) | (bv[e] << 16);
-        col[(2 * e + 1) * (kVP / 2)] = (av[e] >> 16) | (bv[e] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int row = (tid + 256 * j) >> 4;
+      *(u32x4*)(ks + row * kKP + 8 * (tid & 15)) = kch[j].halves();
+      *(u32x4*)(vs + row * kVP + 8 * (tid & 15)) = vch[j].halves();
     }
   };
 
@@ -245,7 +237,7 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
     const int key0 = kb * kBK;
     if (kb < nkb && wave_live && key0 <= qpos_lo + 31) {
       const _Float16* ks = lds + (i & 1) * kStage;
-      const _Float16* vt = ks + kBK * kKP;
+      const _Float16* vs = ks + kBK * kKP;
       float16v s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -320,15 +312,22 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
                          pack_f16x2(q8[6], q8[7])};
         pb[st] = __builtin_bit_cast(half8, h);
       }
-      // k index 8hh + e of step st is key 16 st + 8 (e >> 2) + 4 hh + (e & 3)
+      // k index 8hh + e of step st is key 16 st + 8 (e >> 2) + 4 hh + (e & 3).
+      // The A operand (dim l % 32, those 8 keys) by two transposed reads of V
+      // rows: in each 16-lane group, lane m addresses row K0 + m / 4, dims
+      // D + 4 (m % 4) .. + 3, and lane j receives rows K0 .. K0 + 3 of dim
+      // D + j (D = 32 dt + 16 ((l >> 4) & 1), K0 = 16 st + 4 hh and + 8).
+      const _Float16* vl = vs + (4 * hh + ((lane & 15) >> 2)) * kVP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const _Float16* vr = vt + (32 * dt + r) * kVP + 16 * st + 4 * hh;
-          const half4 lo = *(const half4*)vr;
-          const half4 hi = *(const half4*)(vr + 8);
-          const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          typedef short s4 __attribute__((ext_vector_type(4)));
+          const _Float16* vr = vl + 16 * st * kVP + 32 * dt;
+          const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)vr);
+          const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vr + 8 * kVP));
+          const half4 l4 = __builtin_bit_cast(half4, lo), h4 = __builtin_bit_cast(half4, hi);
+          const half8 va = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[st], o[dt], 0, 0, 0);
         }
     }
