@@ -438,7 +438,8 @@ size_t qp_prompt_attention_workspace_bytes(int kv_type, int64_t kv_len, int64_t 
  *               A binary16 cache ignores it.  Calls sharing a workspace must
  *               not run concurrently.
  * Errors: as qp_prompt_attention; QP_ERR_WORKSPACE_TOO_SMALL for a non-NULL
- * workspace below the query, QP_ERR_INVALID_PARAMETER for a misaligned one.
+ * workspace below the query, QP_ERR_INVALID_PARAMETER for a misaligned one
+ * or a quantized cache of more than 2^27 - 8 rows (kv_len * n_kv_head).
  */
 qp_status qp_prompt_attention_ws(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
                                  int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv_head, int64_t head_dim,

@@ -355,10 +355,12 @@ static qp_status attention_impl(int kv_type, const float* q, int64_t ldq, const 
     if (workspace_bytes < need)
       return fail(QP_ERR_WORKSPACE_TOO_SMALL, "attention workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(QP_ERR_INVALID_PARAMETER, "misaligned workspace");
+    if (2 * kv_len * n_kv_head * (head_dim / 8) > ((int64_t)1 << 32) - 256)  // one thread per 8 values, K and V
+      return fail(QP_ERR_INVALID_PARAMETER, "a cache of %lld rows is too large for one decode launch",
+                  (long long)(kv_len * n_kv_head));
     uint8_t* kf = (uint8_t*)workspace;
     uint8_t* vf = kf + need / 2;
-    hipError_t e = qp::launch_kv_decode_f16(kv_type, k_cache, kv_len * n_kv_head, kf, stream);
-    if (e == hipSuccess) e = qp::launch_kv_decode_f16(kv_type, v_cache, kv_len * n_kv_head, vf, stream);
+    hipError_t e = qp::launch_kv_decode_f16(kv_type, k_cache, v_cache, kv_len * n_kv_head, kf, vf, stream);
     if (e == hipSuccess)
       e = qp::launch_attention(QP_F16W, q, ldq, kf, vf, n_past, t, n_head, n_kv_head, scale, out, ldo, stream);
     return from_hip(e, "attention launch");

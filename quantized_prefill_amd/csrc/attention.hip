@@ -373,19 +373,23 @@ __global__ __launch_bounds__(64 * kWaves * NH) __attribute__((amdgpu_waves_per_e
                                                        o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv};
 }
 
-// A quantized cache's rows as binary16 rows (the values the attention
-// kernel's own staging makes of them, bit for bit): one thread per 8
-// values, rows of kD values.
+// Two quantized caches' rows (K, then V) as binary16 rows (the values the
+// attention kernel's own staging makes of them, bit for bit): one thread
+// per 8 values, rows of kD values.
 template <int KV>
-__global__ __launch_bounds__(256) void kv_decode_f16_kernel(const uint8_t* __restrict__ src, int64_t rows,
-                                                            u32x4* __restrict__ dst) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk of 8 values
-  if (i >= rows * (kD / 8)) return;
+__global__ __launch_bounds__(256) void kv_decode_f16_kernel(const uint8_t* __restrict__ src0,
+                                                            const uint8_t* __restrict__ src1, int64_t rows,
+                                                            u32x4* __restrict__ dst0, u32x4* __restrict__ dst1) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk of 8 values
+  const int64_t per = rows * (kD / 8);
+  const bool second = i >= per;
+  if (second) i -= per;
+  if (i >= per) return;
   const int64_t row = i / (kD / 8);
   const int dc = (int)(i - row * (kD / 8));
   Chunk<KV> c;
-  c.load(src + row * Chunk<KV>::kRowBytes, dc);
-  dst[i] = c.halves();
+  c.load((second ? src1 : src0) + row * Chunk<KV>::kRowBytes, dc);
+  (second ? dst1 : dst0)[i] = c.halves();
 }
 
 }  // namespace
@@ -399,14 +403,17 @@ int64_t attention_row_bytes(int kv_type) {
   }
 }
 
-hipError_t launch_kv_decode_f16(int kv_type, const void* src, int64_t rows, void* dst, hipStream_t s) {
-  const int64_t chunks = rows * (kD / 8);
+hipError_t launch_kv_decode_f16(int kv_type, const void* k_src, const void* v_src, int64_t rows, void* k_dst,
+                                void* v_dst, hipStream_t s) {
+  const int64_t chunks = 2 * rows * (kD / 8);
   if (chunks == 0) return hipSuccess;
   const dim3 grid((uint32_t)((chunks + 255) / 256));
   if (kv_type == kQ8_0)
-    hipLaunchKernelGGL(kv_decode_f16_kernel<kQ8_0>, grid, dim3(256), 0, s, (const uint8_t*)src, rows, (u32x4*)dst);
+    hipLaunchKernelGGL(kv_decode_f16_kernel<kQ8_0>, grid, dim3(256), 0, s, (const uint8_t*)k_src,
+                       (const uint8_t*)v_src, rows, (u32x4*)k_dst, (u32x4*)v_dst);
   else if (kv_type == kQ4_0)
-    hipLaunchKernelGGL(kv_decode_f16_kernel<kQ4_0>, grid, dim3(256), 0, s, (const uint8_t*)src, rows, (u32x4*)dst);
+    hipLaunchKernelGGL(kv_decode_f16_kernel<kQ4_0>, grid, dim3(256), 0, s, (const uint8_t*)k_src,
+                       (const uint8_t*)v_src, rows, (u32x4*)k_dst, (u32x4*)v_dst);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

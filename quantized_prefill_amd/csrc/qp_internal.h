@@ -71,9 +71,10 @@ hipError_t launch_kv_write(int kv_type, const float* src, int64_t lds, int64_t t
 
 // Causal prompt attention over a binary16 or Q8_0 KV cache, head_dim 128.
 int64_t attention_row_bytes(int kv_type);
-// A Q8_0 or Q4_0 cache's rows (head_dim 128) as binary16 rows, the values
-// the attention kernel stages from them.
-hipError_t launch_kv_decode_f16(int kv_type, const void* src, int64_t rows, void* dst, hipStream_t s);
+// The rows of a Q8_0 or Q4_0 K and V cache (head_dim 128) as binary16 rows,
+// the values the attention kernel stages from them; one launch.
+hipError_t launch_kv_decode_f16(int kv_type, const void* k_src, const void* v_src, int64_t rows, void* k_dst,
+                                void* v_dst, hipStream_t s);
 hipError_t launch_attention(int kv_type, const float* q, int64_t ldq, const void* k_cache, const void* v_cache,
                             int64_t n_past, int64_t t, int64_t n_head, int64_t n_kv, float scale, float* out,
                             int64_t ldo, hipStream_t s);
