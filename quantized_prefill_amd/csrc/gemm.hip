@@ -29,6 +29,7 @@
 // column l%32), k = 8*(l/32) + e; result register a of lane l holds
 // D[8*(a/4) + 4*(l/32) + a%4][l%32].
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 #include <vector>
 
@@ -1059,27 +1060,44 @@ __global__ __launch_bounds__(256) void moe_silu_kernel(const float* __restrict__
 // out[t, :] = sum over slots s (in order) of weights[t, s] * inverse scale *
 // the down pass's row of pair t * top_k + s; pairs with an id outside
 // [0, n_experts) add nothing.  The factor is the product the 128-row
-// kernel's down epilogue applies, in the same order.  One thread per float4
-// of out: a token's slot rows are consecutive rows of dbuf.
+// kernel's down epilogue applies, in the same order.  blockIdx.x is the
+// token (its slot ids, maxima and weights are then uniform loads), thread i
+// of blockIdx.y the float4 256 blockIdx.y + i of its row; the slots' rows are
+// loaded 8 at a time before any is summed, so that 8 loads per thread are
+// in flight.
 __global__ __launch_bounds__(256) void moe_combine_rows_kernel(const float* __restrict__ dbuf,
                                                                const int32_t* __restrict__ ids,
                                                                const uint32_t* __restrict__ pairmax,
-                                                               const float* __restrict__ weights, int t, int top_k,
-                                                               int ne, int hidden, float* __restrict__ out) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nq = (int64_t)t * hidden / 4;
-  if (q >= nq) return;
-  const int tok = (int)(q / (hidden / 4));
-  const int c4 = (int)(q - (int64_t)tok * (hidden / 4));
+                                                               const float* __restrict__ weights, int top_k, int ne,
+                                                               int hidden, float* __restrict__ out) {
+  const int tok = blockIdx.x;
+  const int c4 = blockIdx.y * 256 + threadIdx.x;
+  if (4 * c4 >= hidden) return;
+  const int64_t pair0 = (int64_t)tok * top_k;
+  const float* src = dbuf + pair0 * hidden + 4 * c4;
   float4v acc = (float4v){0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < top_k; ++s) {
-    const int64_t pair = (int64_t)tok * top_k + s;
-    const int id = ids[pair];
-    if (id < 0 || id >= ne) continue;
-    const float f = row_scale_from_max(pairmax[pair], true) * weights[pair];
-    const float4v v = *(const float4v*)(dbuf + pair * hidden + 4 * c4);
-    acc += v * f;
-  }
+  // slots s0 .. s0 + 7 (past top_k: the last slot again, not summed)
+  auto group = [&](int s0, auto whole) __attribute__((always_inline)) {
+    int id[8];
+    uint32_t mx[8];
+    float wt[8];
+    float4v v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = decltype(whole)::value ? s0 + j : min(s0 + j, top_k - 1);
+      id[j] = ids[pair0 + s];
+      mx[j] = pairmax[pair0 + s];
+      wt[j] = weights[pair0 + s];
+      v[j] = *(const float4v*)(src + (int64_t)s * hidden);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((decltype(whole)::value || s0 + j < top_k) && id[j] >= 0 && id[j] < ne)
+        acc += v[j] * (row_scale_from_max(mx[j], true) * wt[j]);
+  };
+  int s0 = 0;
+  for (; s0 + 8 <= top_k; s0 += 8) group(s0, std::true_type{});
+  if (s0 < top_k) group(s0, std::false_type{});
   *(float4v*)(out + (int64_t)tok * hidden + 4 * c4) = acc;
 }
 
@@ -1221,9 +1239,9 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
     d.seg.ldy[0] = hidden;
     for (int i = 1; i <= kMaxSeg; ++i) d.seg.tile0[i] = (int)hcols;
     if ((err = launch_gemm_wide(qtype, kGrouped, 8, d, s)) != hipSuccess) return err;
-    const int64_t nq = t * hidden / 4;
-    hipLaunchKernelGGL(moe_combine_rows_kernel, dim3((uint32_t)((nq + 255) / 256)), dim3(256), 0, s, dbuf, ids, rowmax,
-                       weights, (int)t, (int)top_k, (int)n_experts, (int)hidden, out);
+    if (t == 0) return hipSuccess;
+    hipLaunchKernelGGL(moe_combine_rows_kernel, dim3((uint32_t)t, (uint32_t)((hidden / 4 + 255) / 256)), dim3(256), 0, s,
+                       dbuf, ids, rowmax, weights, (int)top_k, (int)n_experts, (int)hidden, out);
     return hipGetLastError();
   }
 
