@@ -1009,15 +1009,16 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
 
 // Between the two passes of the 256-row kernel: per compact row, h =
 // SiLU(g) * u = g / (1 + exp(-g)) * u (the same f32 products as the 128-row
-// kernel's epilogue), the row's largest |h| (bits into pairmax at the row's
-// pair), and h times
+// kernel's epilogue; SILU false: h itself from g, formed by the gate/up
+// pass), the row's largest |h| (bits into pairmax at the row's pair), and h
+// times
 // the power of two that brings that maximum into [2^14, 2^15), rounded to
 // binary16 (the down pass's A rows).  One wave per row; lane l holds columns
 // 4 (l + 64 j) .. + 3, read and written 16 / 8 bytes at a time (inter is a
 // multiple of 256, so of 4).
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
-template <int NJ>
+template <int NJ, bool SILU>
 __global__ __launch_bounds__(256) void moe_silu_kernel(const float* __restrict__ g, const float* __restrict__ u,
                                                        const int* __restrict__ nrows, const int* __restrict__ list,
                                                        int inter, uint32_t* __restrict__ pairmax,
@@ -1026,19 +1027,23 @@ __global__ __launch_bounds__(256) void moe_silu_kernel(const float* __restrict__
   const int lane = threadIdx.x & 63;
   if (row >= *nrows) return;
   const float* gr = g + (int64_t)row * inter;
-  const float* ur = u + (int64_t)row * inter;
+  const float* ur = SILU ? u + (int64_t)row * inter : nullptr;
   float4v h[NJ];
   float mx = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = 4 * (lane + 64 * j);
     if (c < inter) {
-      const float4v gv = *(const float4v*)(gr + c), uv = *(const float4v*)(ur + c);
+      const float4v gv = *(const float4v*)(gr + c);
+      if constexpr (SILU) {
+        const float4v uv = *(const float4v*)(ur + c);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[j][e] = gv[e] / (1.f + __expf(-gv[e])) * uv[e];
-        mx = __builtin_fmaxf(mx, __builtin_fabsf(h[j][e]));
+        for (int e = 0; e < 4; ++e) h[j][e] = gv[e] / (1.f + __expf(-gv[e])) * uv[e];
+      } else {
+        h[j] = gv;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(h[j][e]));
     }
   }
 #pragma unroll
@@ -1206,18 +1211,38 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
       p.seg.ldy[i] = inter;
     }
     for (int i = 2; i <= kMaxSeg; ++i) p.seg.tile0[i] = (int)(2 * icols);
-    if ((err = launch_gemm_wide(qtype, kGrouped, 8, p, s)) != hipSuccess) return err;
+    // Q4_K / Q5_K with inter % 128 == 0: tiles of 128 gate and the same 128
+    // up rows form h = SiLU(g) u themselves (gbuf), and the pass after
+    // only scales h; otherwise g and u as two arrays and SiLU in that pass
+    const bool fused = wide_supported(qtype, kGroupedGU) && inter % 128 == 0;
+    if (fused) {
+      GemmParams f = p;
+      f.w = (const uint8_t*)w_gate;
+      f.w2 = (const uint8_t*)w_up;
+      f.n = (int)inter;
+      f.y = gbuf;
+      f.ldy = inter;
+      if ((err = launch_gemm_wide(qtype, kGroupedGU, 8, f, s)) != hipSuccess) return err;
+    } else if ((err = launch_gemm_wide(qtype, kGrouped, 8, p, s)) != hipSuccess) {
+      return err;
+    }
     {
       const dim3 g((uint32_t)((npairs + 3) / 4));
-      if (inter <= 1024)
-        hipLaunchKernelGGL(moe_silu_kernel<4>, g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, rowmax,
-                           h16);
-      else if (inter <= 2048)
-        hipLaunchKernelGGL(moe_silu_kernel<8>, g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, rowmax,
-                           h16);
-      else
-        hipLaunchKernelGGL(moe_silu_kernel<16>, g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, rowmax,
-                           h16);
+#define QP_SILU(NJ)                                                                                                 \
+  if (fused)                                                                                                        \
+    hipLaunchKernelGGL((moe_silu_kernel<NJ, false>), g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter, \
+                       rowmax, h16);                                                                                \
+  else                                                                                                              \
+    hipLaunchKernelGGL((moe_silu_kernel<NJ, true>), g, dim3(256), 0, s, gbuf, ubuf, ntiles + 1, list, (int)inter,  \
+                       rowmax, h16);
+      if (inter <= 1024) {
+        QP_SILU(4)
+      } else if (inter <= 2048) {
+        QP_SILU(8)
+      } else {
+        QP_SILU(16)
+      }
+#undef QP_SILU
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     // down: A = the binary16 h rows of each tile (compact rows, contiguous),

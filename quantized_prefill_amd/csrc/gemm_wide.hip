@@ -398,7 +398,7 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
     const int row = w * (BMW / NWS) + 8 * q + (lane >> 3);
     const int piece = (lane & 7) ^ ((row >> 1) & 7);
     int xr = min(row, m_rows - 1);
-    if constexpr (MODE == kGrouped) {
+    if constexpr (MODE == kGrouped || MODE == kGroupedGU) {
       if (p.gather) xr = p.list[xr] / p.top_k;  // the token of compact row xr
     }
     xoff[q] = (uint32_t)(2 * (xr * p.ldx + 8 * piece));
@@ -429,6 +429,12 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)wtile, (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsrc_part =
       __builtin_amdgcn_make_buffer_rsrc((void*)wtile, (short)0, FULL ? -1 : (int)((int64_t)(p.n - n0) * rb), 0x00020000);
+  // kGroupedGU: staged rows 0..127 are gate rows n0.., 128..255 the same up
+  // rows; a 16-byte load lies wholly in one half (128 NP pieces = 2 NP loads)
+  static_assert(MODE != kGroupedGU || (S::P16 && FULL && KS == 1 && C::NI16 % 2 == 0), "gate/up tiles: 16-byte staging");
+  const __amdgpu_buffer_rsrc_t wrsrc_up =
+      MODE == kGroupedGU ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.w2 + (int64_t)n0 * rb), (short)0, -1, 0x00020000)
+                         : wrsrc;
   // FULL: the dword-aligned start of the lane's run splits into a per-lane
   // part and a per-instruction part (rows 2 apart start at the same offset
   // within a dword, and R is even wherever rb % 4 != 0), for block offsets 0
@@ -451,8 +457,9 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
       const int gi = min(NWS * q + w, C::NI16 - 1);
       const int pc = 64 * gi + lane;
       const int row = pc / S::NP, j = pc - row * S::NP;
-      v16a[q] = (uint32_t)(row * rb) + S::off16(j, 0);
-      v16b[q] = (uint32_t)(row * rb) + S::off16(j, 1);
+      const int wr = MODE == kGroupedGU ? (row & 127) : row;  // the row within its tensor's tile rows
+      v16a[q] = (uint32_t)(wr * rb) + S::off16(j, 0);
+      v16b[q] = (uint32_t)(wr * rb) + S::off16(j, 1);
     }
   }
   // part [Q0, Q1) of the loads of step st (clamped to the last step) into buffer buf
@@ -469,7 +476,11 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
       for (int q = Q0; q < Q1; ++q) {
         const int gi = min(NWS * q + w, C::NI16 - 1);
         const uint32_t v = h ? v16b[q] : v16a[q];
-        if constexpr (FULL)
+        if constexpr (MODE == kGroupedGU)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(2 * gi < C::NI16 ? wrsrc : wrsrc_up,
+                                                   (__attribute__((address_space(3))) void*)(dst + 256 * gi), 16, (int)v,
+                                                   (int)boff, 0, 0);
+        else if constexpr (FULL)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (__attribute__((address_space(3))) void*)(dst + 256 * gi), 16,
                                                    (int)v, (int)boff, 0, 0);
         else
@@ -508,8 +519,9 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   using P3 = std::integral_constant<int, 3 * NI / 4>;
   using P4 = std::integral_constant<int, NI>;
 
-  // ---- decode side: the lane's row is tile row 32 w + l % 32
-  const int nrow = 32 * w + (lane & 31);
+  // ---- decode side: the lane's row is tile row 32 w + l % 32 (kGroupedGU:
+  // lanes l % 32 < 16 gate row 16 w + l % 16, the others the same up row)
+  const int nrow = MODE == kGroupedGU ? ((lane & 16) << 3) + 16 * w + (lane & 15) : 32 * w + (lane & 31);
   const uint32_t rdelta = (uint32_t)((FULL ? nrow : min(nrow, p.n - 1 - n0)) & 1) * rb3;  // 2: row starts 2 bytes into a dword
   // staged bytes of unit (O, r) of step st (clamped)
   auto read_unit = [&](int st, auto oc, auto rc, uint32_t (&u)[D::NU]) __attribute__((always_inline)) {
@@ -685,6 +697,40 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
 
   // ---- epilogue: 16-byte stores through a per-wave LDS transpose
   float* scr = (float*)sm.x + 32 * 40 * w;
+  if constexpr (MODE == kGroupedGU) {
+    // column l % 32 of a block is gate feature n0 + 16 w + l % 16 for l % 32
+    // < 16, else the same up feature, over the same tokens: lanes l and
+    // l ^ 16 trade one value per pair of accumulators, the lane with the gate
+    // value forms h = SiLU(g) u = g u / (1 + 2^(-g log2 e)) for the even one,
+    // its partner for the odd one (row + 1).  Stores through a buffer whose
+    // record count ends at the tile's last row: rows past it are dropped.
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const bool up = (ln & 16) != 0;
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.y, (short)0, (int)((int64_t)m_rows * p.ldy * 4), 0x00020000);
+    const uint32_t voff = (uint32_t)(((4 * (ln >> 5) + (up ? 1 : 0)) * p.ldy + n0 + 16 * w + (ln & 15)) * 4);
+    const uint32_t rstep = (uint32_t)(p.ldy * 4);
+    // a bit mask (opaque to the optimizer, which would otherwise turn the
+    // choice between two accumulators into a run-time register index)
+    uint32_t upm = up ? ~0u : 0u;
+    asm volatile("" : "+v"(upm));
+    auto pick = [&](float x_up, float x_gate) __attribute__((always_inline)) {
+      return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x_up) & upm) |
+                                           (__builtin_bit_cast(uint32_t, x_gate) & ~upm));
+    };
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; a += 2) {
+        const float recv = __shfl_xor(pick(acc[i][a], acc[i][a + 1]), 16, 64);
+        const float gv = pick(recv, acc[i][a]);
+        const float uv = pick(acc[i][a + 1], recv);
+        const float h = gv * uv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(gv * -1.44269504088896341f));
+        const uint32_t row = (uint32_t)(32 * i + 8 * (a >> 2) + (a & 3));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, h), yr, (int)(voff + row * rstep), 0, 0);
+      }
+    return;
+  }
   float16v accs[MI][1];
 #pragma unroll
   for (int i = 0; i < MI; ++i) accs[i][0] = acc[i];
@@ -747,13 +793,28 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     m0 = 0;
   }
   const int n0 = tile_x * Cfg<QT, MI, KS>::BNW;
-  if (n0 + Cfg<QT, MI, KS>::BNW <= p.n)
+  if constexpr (MODE == kGroupedGU) {
+    // routed gate/up with SiLU: as kGrouped above, the column tile being 128
+    // features of h (gate and up rows of one expert)
+    const int ti = blockIdx.y;
+    if (ti >= *pk.ntiles) return;
+    const int e = pk.tiles[3 * ti], r0 = pk.tiles[3 * ti + 1];
+    const int base = pk.offsets[e] + r0;
+    p.w = pk.w + (int64_t)e * pk.estride;
+    p.w2 = pk.w2 + (int64_t)e * pk.estride;
+    p.t = pk.tiles[3 * ti + 2];
+    p.list = pk.list + base;
+    p.y = pk.y + (int64_t)base * pk.ldy;
+    wide_tile<QT, MODE, MI, true, KS>(p, sm, tile_x * 128, 0);
+  } else if (n0 + Cfg<QT, MI, KS>::BNW <= p.n) {
     wide_tile<QT, MODE, MI, true, KS>(p, sm, n0, m0);
-  else
+  } else {
     wide_tile<QT, MODE, MI, false, KS>(p, sm, n0, m0);
+  }
 }
 
 bool wide_supported(int qtype, int mode) {
+  if (mode == kGroupedGU) return qtype == kQ4_K || qtype == kQ5_K;
   return (qtype == kQ6_K || qtype == kQ2_K || qtype == kQ4_K || qtype == kQ5_K) &&
          (mode == kPlainF16 || mode == kMulti || mode == kGrouped);
 }
@@ -764,13 +825,22 @@ template <int QT, int MODE, int MI>
 static void launch_wide_t(const GemmParams& p, uint32_t col_tiles, hipStream_t s) {
   constexpr int BMW = 32 * MI;
   // kGrouped: p.t carries the size of the tile table (its largest possible length)
-  const dim3 grid(col_tiles, MODE == kGrouped ? (uint32_t)p.t : (uint32_t)((p.t + BMW - 1) / BMW));
+  const dim3 grid(col_tiles, MODE == kGrouped || MODE == kGroupedGU ? (uint32_t)p.t : (uint32_t)((p.t + BMW - 1) / BMW));
   hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), grid, dim3(NTW), 0, s, p);
 }
 
 // Tiles of 32 * mi tokens x 256 features (mi = 8 or 4); kMulti: p.seg
 // holds the segments and col_tiles their total.
 hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s) {
+  if (mode == kGroupedGU) {
+    // p.n: h columns (a multiple of 128), 128 per column tile
+    if (mi != 8 || p.n % 128 != 0) return hipErrorInvalidValue;
+    const uint32_t gcols = (uint32_t)(p.n / 128);
+    if (qtype == kQ4_K) launch_wide_t<kQ4_K, kGroupedGU, 8>(p, gcols, s);
+    else if (qtype == kQ5_K) launch_wide_t<kQ5_K, kGroupedGU, 8>(p, gcols, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (mode != kPlainF16 && mode != kMulti && mode != kGrouped) return hipErrorInvalidValue;
   if (mode == kGrouped && mi != 8) return hipErrorInvalidValue;
   const uint32_t cols = mode != kPlainF16 ? (uint32_t)p.seg.tile0[p.seg.nseg] : (uint32_t)((p.n + 255) / 256);
