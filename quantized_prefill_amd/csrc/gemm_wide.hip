@@ -665,8 +665,20 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   } else {
     main_loop(std::integral_constant<int, MI>{});
   }
+  // routed down pass: the tile's output rows (pairs list[r]) go through LDS,
+  // loaded once here instead of one dependent load per store below
+  int out_row = 0;
+  if constexpr (MODE == kGrouped) {
+    if (!p.gather && tid < BMW) out_row = p.list[min(tid, m_rows - 1)];
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
   lds_barrier();
+  if constexpr (MODE == kGrouped) {
+    if (!p.gather) {  // the staging buffers are free now
+      if (tid < BMW) ((int*)sm.raw[0][0])[tid] = out_row;
+      lds_barrier();
+    }
+  }
   if constexpr (KS > 1) {
     // the other slices' sums into the first's, in slice order (one dword
     // per lane and value), then all past a barrier before the stores reuse
@@ -738,7 +750,7 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
     if (!p.gather) {  // routed down pass: row r of the tile is pair list[r]'s row of y
       store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
                              [&](int r) __attribute__((always_inline)) {
-                               return p.y + (int64_t)p.list[min(r, m_rows - 1)] * p.ldy;  // rows past the tile: not stored
+                               return p.y + (int64_t)((const int*)sm.raw[0][0])[r] * p.ldy;  // rows past the tile: not stored
                              });
       return;
     }
