@@ -913,8 +913,9 @@ __global__ __launch_bounds__(1024) void moe_escan_kernel(const int* __restrict__
 __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__ counts, int ne,
                                                          int* __restrict__ offsets, int* __restrict__ tiles,
                                                          int* __restrict__ ntiles, int* __restrict__ tiles2,
-                                                         int* __restrict__ ntiles2, const int* __restrict__ cbad,
-                                                         int nchunks, uint32_t* __restrict__ header) {
+                                                         int* __restrict__ ntiles2, int max_tiles2,
+                                                         const int* __restrict__ cbad, int nchunks,
+                                                         uint32_t* __restrict__ header) {
   __shared__ int wsum[16];
   {
     int nb = 0;
@@ -926,7 +927,8 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
   const int e = threadIdx.x;
   const int c = e < ne ? counts[e] : 0;
   const int nt = (c + BM - 1) / BM;
-  // Tiles of the 256-row kernel as (expert, first row, rows).  The kernel
+  // Tiles of the 256-row kernel as (expert, first row, rows, first compact
+  // row of the tile: the expert's offset + first row).  The kernel
   // runs a tile of at most 128 rows over 4 M blocks and one of at most 192
   // over 6, so a list of 256 f + r rows with 0 < r <= 64 ends in tiles of
   // 192 and 64 + r rows rather than 256 and r (the weights are decoded once
@@ -952,9 +954,10 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
       tiles[2 * (t0 + k) + 1] = k * BM;
     }
     auto put = [&](int u, int r0, int rows) {
-      tiles2[3 * u] = e;
-      tiles2[3 * u + 1] = r0;
-      tiles2[3 * u + 2] = rows;
+      tiles2[4 * u] = e;
+      tiles2[4 * u + 1] = r0;
+      tiles2[4 * u + 2] = rows;
+      tiles2[4 * u + 3] = cin - c + r0;
     };
     const int u8 = tin8 - n8;
     for (int k = 0; k < n8; ++k) put(u8 + k, 256 * k, min(256, c - 256 * k));
@@ -966,6 +969,9 @@ __global__ __launch_bounds__(1024) void moe_oscan_kernel(const int* __restrict__
     ntiles[1] = rows_tot;  // compact rows in all lists
     *ntiles2 = tot8 + tot6 + tot4;
   }
+  // the rest of the 256-row table: tiles of no rows, which the kernel's
+  // workgroups leave at once (so that they need not read the count first)
+  for (int u = tot8 + tot6 + tot4 + threadIdx.x; u < max_tiles2; u += 1024) tiles2[4 * u + 2] = 0;
 }
 
 // Stable scatter: pair i of chunk j with expert e goes to compact row
@@ -1125,7 +1131,7 @@ bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t h
   ws.ntiles = o;  o += align256(sizeof(int) * 4);
   ws.tiles = o;   o += align256(sizeof(int) * 2 * ws.max_tiles);
   ws.ntiles2 = o; o += align256(sizeof(int) * 4);
-  ws.tiles2 = o;  o += align256(sizeof(int) * 3 * ws.max_tiles2);
+  ws.tiles2 = o;  o += align256(sizeof(int) * 4 * ws.max_tiles2);
   ws.list = o;    o += align256(sizeof(int) * pairs);
   ws.rowmax = o;  o += align256(sizeof(uint32_t) * pairs);
   ws.hbuf = o;    o += align256(sizeof(float) * pairs * inter);    // h (128-row kernel) or g (256-row kernel)
@@ -1171,7 +1177,7 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
                     t * hidden * 2 < ((int64_t)1 << 31) &&  // gathered X rows: 32-bit byte offsets from x
                     inter <= 4096;                          // the SiLU pass holds a row in registers
   hipLaunchKernelGGL(moe_oscan_kernel, dim3(1), dim3(1024), 0, s, counts, (int)n_experts, offsets, tiles, ntiles,
-                     tiles2, ntiles2, cbad, nch, header);
+                     tiles2, ntiles2, (int)ws.max_tiles2, cbad, nch, header);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (nch > 0) {
     hipLaunchKernelGGL(moe_scatter_kernel, dim3((uint32_t)nch), dim3(kMoeChunk), 0, s, ids, npairs, (int)n_experts,

@@ -54,7 +54,7 @@ struct GemmParams {
   int hd;
   float eps;
   // routed experts
-  const int* tiles;      // [max_tiles][2]: expert, first row of its list
+  const int* tiles;      // [max_tiles][2]: expert, first row of its list (256-row kernel: [4], see moe_oscan_kernel)
   const int* ntiles;
   const int* offsets;    // first compact row of each expert
   const int* counts;     // rows of each expert

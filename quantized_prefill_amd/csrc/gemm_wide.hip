@@ -784,9 +784,9 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     // largest possible table; workgroups past its end leave at once), the
     // column tile picks the segment (gate / up, or the down projection)
     const int ti = blockIdx.y;
-    if (ti >= *pk.ntiles) return;
-    const int e = pk.tiles[3 * ti], r0 = pk.tiles[3 * ti + 1];
-    const int base = pk.offsets[e] + r0;  // first compact row of the tile
+    const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
+    if (te[2] == 0) return;  // past the table's tiles
+    const int e = (int)te[0], base = (int)te[3];  // expert, first compact row of the tile
     int sg = 0;
 #pragma unroll
     for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
@@ -794,7 +794,7 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     p.w = pk.seg.w[sg] + (int64_t)e * pk.estride;
     p.n = pk.seg.n[sg];
     p.ldy = pk.seg.ldy[sg];
-    p.t = pk.tiles[3 * ti + 2];  // the tile's rows
+    p.t = (int)te[2];  // the tile's rows
     p.list = pk.list + base;  // the tile's pairs
     if (pk.gather) {          // gate / up: X rows are the pairs' tokens, y the compact rows
       p.y = pk.seg.y[sg] + (int64_t)base * pk.seg.ldy[sg];
@@ -809,12 +809,12 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     // routed gate/up with SiLU: as kGrouped above, the column tile being 128
     // features of h (gate and up rows of one expert)
     const int ti = blockIdx.y;
-    if (ti >= *pk.ntiles) return;
-    const int e = pk.tiles[3 * ti], r0 = pk.tiles[3 * ti + 1];
-    const int base = pk.offsets[e] + r0;
+    const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
+    if (te[2] == 0) return;  // past the table's tiles
+    const int e = (int)te[0], base = (int)te[3];
     p.w = pk.w + (int64_t)e * pk.estride;
     p.w2 = pk.w2 + (int64_t)e * pk.estride;
-    p.t = pk.tiles[3 * ti + 2];
+    p.t = (int)te[2];
     p.list = pk.list + base;
     p.y = pk.y + (int64_t)base * pk.ldy;
     wide_tile<QT, MODE, MI, true, KS>(p, sm, tile_x * 128, 0);
