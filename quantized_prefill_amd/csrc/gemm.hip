@@ -1127,7 +1127,7 @@ bool moe_workspace_layout(int64_t t, int64_t top_k, int64_t n_experts, int64_t h
   ws.cpref = o;   o += align256(sizeof(int) * n_experts * ws.nchunks);
   ws.counts = o;  o += align256(sizeof(int) * n_experts);
   ws.offsets = o; o += align256(sizeof(int) * n_experts);
-  ws.max_tiles2 = n_experts + (pairs + 255) / 256;
+  ws.max_tiles2 = (n_experts + (pairs + 255) / 256 + 7) / 8 * 8;  // whole groups of 8 (one per XCD)
   ws.ntiles = o;  o += align256(sizeof(int) * 4);
   ws.tiles = o;   o += align256(sizeof(int) * 2 * ws.max_tiles);
   ws.ntiles2 = o; o += align256(sizeof(int) * 4);

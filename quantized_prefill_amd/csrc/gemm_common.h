@@ -73,6 +73,7 @@ struct GemmParams {
   // kGroupedGU: the same tiles over 128 gate rows (w) and the same 128 up
   // rows (w2) of an expert; y gets SiLU(g) u as f32 rows of n columns
   int gather;
+  int tcols;  // routed modes: column tiles (set by the launcher)
 };
 
 // Power of two bringing a row's largest |h| into [2^14, 2^15): binary16 then

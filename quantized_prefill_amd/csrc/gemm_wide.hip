@@ -761,11 +761,23 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
 
 // Grid: (column tiles, token tiles).  kMulti: projections over one X, each
 // a segment of whole column tiles (its own weights, rows and output).
+// Routed modes: a 1D grid of pk.tcols x (table length, a multiple of 8)
+// workgroups.  Workgroups go to the 8 XCDs in turn (b % 8), so workgroup b
+// takes table tile b % 8 + 8 ((b / 8) / tcols) and column tile (b / 8) %
+// tcols: an XCD runs whole table tiles, all their column tiles one after the
+// other, and the tile's activation rows are fetched into its L2 once rather
+// than by every XCD.
 template <int QT, int MODE, int MI, int KS = 1>
 __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
   __shared__ __attribute__((aligned(16))) Smem<QT, MI, KS> sm;
   GemmParams p = pk;
   int tile_x = blockIdx.x;
+  int ti = 0;
+  if constexpr (MODE == kGrouped || MODE == kGroupedGU) {
+    const uint32_t kx = blockIdx.x >> 3;
+    ti = (int)((blockIdx.x & 7) + 8 * (kx / (uint32_t)pk.tcols));
+    tile_x = (int)(kx % (uint32_t)pk.tcols);
+  }
   if constexpr (MODE == kMulti) {
     int sg = 0;
 #pragma unroll
@@ -780,10 +792,9 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
   }
   int m0 = blockIdx.y * Cfg<QT, MI>::BMW;
   if constexpr (MODE == kGrouped) {
-    // routed experts: blockIdx.y is a tile of the table (the grid covers the
-    // largest possible table; workgroups past its end leave at once), the
-    // column tile picks the segment (gate / up, or the down projection)
-    const int ti = blockIdx.y;
+    // routed experts: ti is a tile of the table (the grid covers the largest
+    // possible table; workgroups past its end leave at once), the column
+    // tile picks the segment (gate / up, or the down projection)
     const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
     if (te[2] == 0) return;  // past the table's tiles
     const int e = (int)te[0], base = (int)te[3];  // expert, first compact row of the tile
@@ -808,7 +819,6 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
   if constexpr (MODE == kGroupedGU) {
     // routed gate/up with SiLU: as kGrouped above, the column tile being 128
     // features of h (gate and up rows of one expert)
-    const int ti = blockIdx.y;
     const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
     if (te[2] == 0) return;  // past the table's tiles
     const int e = (int)te[0], base = (int)te[3];
@@ -836,14 +846,22 @@ int wide_cols() { return 32 * NW; }
 template <int QT, int MODE, int MI>
 static void launch_wide_t(const GemmParams& p, uint32_t col_tiles, hipStream_t s) {
   constexpr int BMW = 32 * MI;
-  // kGrouped: p.t carries the size of the tile table (its largest possible length)
-  const dim3 grid(col_tiles, MODE == kGrouped || MODE == kGroupedGU ? (uint32_t)p.t : (uint32_t)((p.t + BMW - 1) / BMW));
-  hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), grid, dim3(NTW), 0, s, p);
+  if constexpr (MODE == kGrouped || MODE == kGroupedGU) {
+    // p.t carries the size of the tile table (its largest possible length, a
+    // multiple of 8)
+    GemmParams q = p;
+    q.tcols = (int)col_tiles;
+    hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), dim3(col_tiles * (uint32_t)p.t), dim3(NTW), 0, s, q);
+  } else {
+    const dim3 grid(col_tiles, (uint32_t)((p.t + BMW - 1) / BMW));
+    hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), grid, dim3(NTW), 0, s, p);
+  }
 }
 
 // Tiles of 32 * mi tokens x 256 features (mi = 8 or 4); kMulti: p.seg
 // holds the segments and col_tiles their total.
 hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s) {
+  if ((mode == kGrouped || mode == kGroupedGU) && p.t % 8 != 0) return hipErrorInvalidValue;  // table length
   if (mode == kGroupedGU) {
     // p.n: h columns (a multiple of 128), 128 per column tile
     if (mi != 8 || p.n % 128 != 0) return hipErrorInvalidValue;
