@@ -1040,7 +1040,7 @@ __global__ __launch_bounds__(256) void moe_silu_kernel(const float* __restrict__
   for (int j = 0; j < NJ; ++j) {
     const int c = 4 * (lane + 64 * j);
     if (c < inter) {
-      const float4v gv = *(const float4v*)(gr + c);
+      const float4v gv = SILU ? *(const float4v*)(gr + c) : __builtin_nontemporal_load((const float4v*)(gr + c));  // h: read once
       if constexpr (SILU) {
         const float4v uv = *(const float4v*)(ur + c);
 #pragma unroll
@@ -1075,7 +1075,7 @@ __global__ __launch_bounds__(256) void moe_silu_kernel(const float* __restrict__
 // token (its slot ids, maxima and weights are then uniform loads), thread i
 // of blockIdx.y the float4 256 blockIdx.y + i of its row; the slots' rows are
 // loaded 8 at a time before any is summed, so that 8 loads per thread are
-// in flight.
+// in flight, as non-temporal loads (each row is read once).
 __global__ __launch_bounds__(256) void moe_combine_rows_kernel(const float* __restrict__ dbuf,
                                                                const int32_t* __restrict__ ids,
                                                                const uint32_t* __restrict__ pairmax,
@@ -1099,7 +1099,7 @@ __global__ __launch_bounds__(256) void moe_combine_rows_kernel(const float* __re
       id[j] = ids[pair0 + s];
       mx[j] = pairmax[pair0 + s];
       wt[j] = weights[pair0 + s];
-      v[j] = *(const float4v*)(src + (int64_t)s * hidden);
+      v[j] = __builtin_nontemporal_load((const float4v*)(src + (int64_t)s * hidden));  // read once
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
