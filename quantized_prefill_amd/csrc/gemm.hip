@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void add_partial_kernel(const float* __restric
   float* yr = y + (int64_t)r * ldy;
   const float* pr = part + (int64_t)r * n;
   if (c + 4 <= n && ldy % 4 == 0 && n % 4 == 0) {
-    const float4v a = *(const float4v*)(yr + c), b = *(const float4v*)(pr + c);
+    const float4v a = *(const float4v*)(yr + c), b = __builtin_nontemporal_load((const float4v*)(pr + c));  // part: read once
     *(float4v*)(yr + c) = a + b;
   } else {
     for (int e = c; e < n && e < c + 4; ++e) yr[e] = yr[e] + pr[e];
@@ -596,8 +596,9 @@ __global__ __launch_bounds__(256) void split_combine_kernel(SplitSum a, SplitSum
   if (ok) {
     const float4v* r0 = (const float4v*)(q.p0 + tok * q.n + c);
     const float4v* r1 = (const float4v*)(q.p1 + tok * q.n + c);
-    lo = r0[0] + r1[0];
-    hi = r0[1] + r1[1];
+    // the two partial sums are read once
+    lo = __builtin_nontemporal_load(r0) + __builtin_nontemporal_load(r1);
+    hi = __builtin_nontemporal_load(r0 + 1) + __builtin_nontemporal_load(r1 + 1);
   }
   float4v* dst = (float4v*)(q.y + tok * q.ldy + c);
   if (q.hd == 0) {
@@ -1198,7 +1199,6 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
     p.counts = counts;
     p.list = list;
     p.top_k = (int)top_k;
-    p.gather = 1;
     p.x = x;
     p.ldx = hidden;
     p.k = (int)hidden;
@@ -1255,7 +1255,7 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
     // the raw products into dbuf's rows in pair order (row r of a tile goes
     // to pair list[r]), which the combine reads per token
     GemmParams d = p;
-    d.gather = 0;  // d.list stays: the epilogue stores row r of a tile at pair list[base + r]
+    // d.list stays: the epilogue stores row r of a tile at pair list[base + r]
     d.x = h16;
     d.ldx = inter;
     d.k = (int)inter;
@@ -1269,7 +1269,7 @@ hipError_t launch_grouped_expert(int qtype, const void* w_gate, const void* w_up
     d.seg.y[0] = dbuf;
     d.seg.ldy[0] = hidden;
     for (int i = 1; i <= kMaxSeg; ++i) d.seg.tile0[i] = (int)hcols;
-    if ((err = launch_gemm_wide(qtype, kGrouped, 8, d, s)) != hipSuccess) return err;
+    if ((err = launch_gemm_wide(qtype, kGroupedDown, 8, d, s)) != hipSuccess) return err;
     if (t == 0) return hipSuccess;
     hipLaunchKernelGGL(moe_combine_rows_kernel, dim3((uint32_t)t, (uint32_t)((hidden / 4 + 255) / 256)), dim3(256), 0, s,
                        dbuf, ids, rowmax, weights, (int)top_k, (int)n_experts, (int)hidden, out);

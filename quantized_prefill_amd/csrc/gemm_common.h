@@ -14,7 +14,8 @@ namespace qp {
 
 constexpr int BM = kTileM, BN = kTileN, BK = 64, NT = 256, LDK = BK + 8;
 
-enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4, kMulti = 5, kGrouped = 6, kGroupedGU = 7 };
+enum Mode { kPlainF16 = 0, kPlainF32 = 1, kQkNorm = 2, kGateUp = 3, kDown = 4, kMulti = 5, kGrouped = 6, kGroupedGU = 7,
+           kGroupedDown = 8 };
 
 // Projections sharing one X fused into one launch of the tall kernel (mode
 // kMulti): segment s owns the output-column tiles [tile0[s], tile0[s + 1]),
@@ -67,12 +68,12 @@ struct GemmParams {
   GemmSegments seg;      // fused projections (kMulti)
   int64_t part_stride;   // 128-tile plain modes split over gridDim.z K parts: floats between partial outputs
   int vec_store;         // 128-tile kernel: output rows are 16-byte multiples (16-byte stores)
-  // routed experts on the 256 x 256-tile kernel (kGrouped): a tile table of
-  // 256-row tiles of the per-expert lists; gather: X rows are the tokens
-  // list[row] / top_k (gate/up), else the compact rows themselves (down).
-  // kGroupedGU: the same tiles over 128 gate rows (w) and the same 128 up
-  // rows (w2) of an expert; y gets SiLU(g) u as f32 rows of n columns
-  int gather;
+  // routed experts on the 256 x 256-tile kernel: a tile table of 256-row
+  // tiles of the per-expert lists.  kGrouped (gate / up segments) and
+  // kGroupedGU: X rows are the tokens list[row] / top_k; kGroupedGU stages
+  // 128 gate rows (w) and the same 128 up rows (w2) of an expert and writes
+  // SiLU(g) u as f32 rows of n columns.  kGroupedDown: X rows are the compact
+  // rows themselves, output row r goes to pair list[r].
   int tcols;  // routed modes: column tiles (set by the launcher)
 };
 

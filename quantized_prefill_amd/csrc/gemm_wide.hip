@@ -375,7 +375,11 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   using S = Stage<QT>;
   using D = Dec<QT>;
   constexpr int BMW = C::BMW, BNW = C::BNW, XB = C::XB, RSD = C::RSD, R = C::R, NI = C::NI, XL = C::XL;
-  const int tid = threadIdx.x;
+  // routed modes: opaque to the optimizer, so that in the loop over tiles
+  // values derived from the thread index are formed per tile, not held in
+  // registers across tiles
+  int tid = threadIdx.x;
+  if constexpr (MODE == kGrouped || MODE == kGroupedGU || MODE == kGroupedDown) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ks = wv / NWS;      // K slice of the wave
@@ -398,9 +402,7 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
     const int row = w * (BMW / NWS) + 8 * q + (lane >> 3);
     const int piece = (lane & 7) ^ ((row >> 1) & 7);
     int xr = min(row, m_rows - 1);
-    if constexpr (MODE == kGrouped || MODE == kGroupedGU) {
-      if (p.gather) xr = p.list[xr] / p.top_k;  // the token of compact row xr
-    }
+    if constexpr (MODE == kGrouped || MODE == kGroupedGU) xr = p.list[xr] / p.top_k;  // the token of compact row xr
     xoff[q] = (uint32_t)(2 * (xr * p.ldx + 8 * piece));
   }
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)xtile, (short)0, -1, 0x00020000);
@@ -668,16 +670,14 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   // routed down pass: the tile's output rows (pairs list[r]) go through LDS,
   // loaded once here instead of one dependent load per store below
   int out_row = 0;
-  if constexpr (MODE == kGrouped) {
-    if (!p.gather && tid < BMW) out_row = p.list[min(tid, m_rows - 1)];
+  if constexpr (MODE == kGroupedDown) {
+    if (tid < BMW) out_row = p.list[min(tid, m_rows - 1)];
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped re-loads past the end have landed
   lds_barrier();
-  if constexpr (MODE == kGrouped) {
-    if (!p.gather) {  // the staging buffers are free now
-      if (tid < BMW) ((int*)sm.raw[0][0])[tid] = out_row;
-      lds_barrier();
-    }
+  if constexpr (MODE == kGroupedDown) {  // the staging buffers are free now
+    if (tid < BMW) ((int*)sm.raw[0][0])[tid] = out_row;
+    lds_barrier();
   }
   if constexpr (KS > 1) {
     // the other slices' sums into the first's, in slice order (one dword
@@ -746,58 +746,48 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, Smem<QT, MI, KS>&
   float16v accs[MI][1];
 #pragma unroll
   for (int i = 0; i < MI; ++i) accs[i][0] = acc[i];
-  if constexpr (MODE == kGrouped) {
-    if (!p.gather) {  // routed down pass: row r of the tile is pair list[r]'s row of y
-      store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
-                             [&](int r) __attribute__((always_inline)) {
-                               return p.y + (int64_t)((const int*)sm.raw[0][0])[r] * p.ldy;  // rows past the tile: not stored
-                             });
-      return;
-    }
+  if constexpr (MODE == kGroupedDown) {
+    // routed down pass: row r of the tile is pair list[r]'s row of y
+    store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
+                           [&](int r) __attribute__((always_inline)) {
+                             return p.y + (int64_t)((const int*)sm.raw[0][0])[r] * p.ldy;  // rows past the tile: not stored
+                           });
+  } else {
+    store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
+                           [&](int r) __attribute__((always_inline)) { return p.y + (int64_t)(m0 + r) * p.ldy; });
   }
-  store_tiles_vec<MI, 1>(accs, m_rows, n0 + 32 * w, p.n, lane, scr,
-                         [&](int r) __attribute__((always_inline)) { return p.y + (int64_t)(m0 + r) * p.ldy; });
 }
 
-// Grid: (column tiles, token tiles).  kMulti: projections over one X, each
-// a segment of whole column tiles (its own weights, rows and output).
-// Routed modes: a 1D grid of pk.tcols x (table length, a multiple of 8)
-// workgroups.  Workgroups go to the 8 XCDs in turn (b % 8), so workgroup b
-// takes table tile b % 8 + 8 ((b / 8) / tcols) and column tile (b / 8) %
-// tcols: an XCD runs whole table tiles, all their column tiles one after the
-// other, and the tile's activation rows are fetched into its L2 once rather
-// than by every XCD.
-template <int QT, int MODE, int MI, int KS = 1>
-__global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
-  __shared__ __attribute__((aligned(16))) Smem<QT, MI, KS> sm;
+// Routed modes whose workgroups loop over tiles (one workgroup per CU): the
+// types whose loop fits the register budget without spills; the others run
+// one tile per workgroup.
+constexpr bool wide_persistent(int qt, int mode) {
+  return mode == kGroupedGU || qt == kQ4_K || qt == kQ2_K;
+}
+
+// Routed modes: linear tile b of pk.tcols x (table length, a multiple of 8)
+// is table tile b % 8 + 8 ((b / 8) / tcols), column tile (b / 8) % tcols.
+// Returns false for an entry past the table (no rows; nothing touched).
+template <int QT, int MODE, int MI, int KS>
+__device__ __forceinline__ bool routed_tile(const GemmParams& pk, Smem<QT, MI, KS>& sm, uint32_t b) {
+  const uint32_t kx = b >> 3;
+  const int ti = (int)((b & 7) + 8 * (kx / (uint32_t)pk.tcols));
+  int tile_x = (int)(kx % (uint32_t)pk.tcols);
+  const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
+  if (te[2] == 0) return false;  // past the table's tiles
+  const int e = (int)te[0], base = (int)te[3];  // expert, first compact row of the tile
   GemmParams p = pk;
-  int tile_x = blockIdx.x;
-  int ti = 0;
-  if constexpr (MODE == kGrouped || MODE == kGroupedGU) {
-    const uint32_t kx = blockIdx.x >> 3;
-    ti = (int)((blockIdx.x & 7) + 8 * (kx / (uint32_t)pk.tcols));
-    tile_x = (int)(kx % (uint32_t)pk.tcols);
-  }
-  if constexpr (MODE == kMulti) {
-    int sg = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
-    tile_x -= pk.seg.tile0[sg];
-    p.w = pk.seg.w[sg];
-    p.n = pk.seg.n[sg];
-    p.k = pk.seg.k[sg];  // a K part: its weights start at seg.w, its activations xoff into each row
-    p.x = (const _Float16*)pk.x + pk.seg.xoff[sg];
-    p.y = pk.seg.y[sg];
-    p.ldy = pk.seg.ldy[sg];
-  }
-  int m0 = blockIdx.y * Cfg<QT, MI>::BMW;
-  if constexpr (MODE == kGrouped) {
-    // routed experts: ti is a tile of the table (the grid covers the largest
-    // possible table; workgroups past its end leave at once), the column
-    // tile picks the segment (gate / up, or the down projection)
-    const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
-    if (te[2] == 0) return;  // past the table's tiles
-    const int e = (int)te[0], base = (int)te[3];  // expert, first compact row of the tile
+  p.t = (int)te[2];          // the tile's rows
+  p.list = pk.list + base;  // the tile's pairs
+  if constexpr (MODE == kGroupedGU) {
+    // gate/up with SiLU: the column tile is 128 features of h (gate and up
+    // rows of one expert)
+    p.w = pk.w + (int64_t)e * pk.estride;
+    p.w2 = pk.w2 + (int64_t)e * pk.estride;
+    p.y = pk.y + (int64_t)base * pk.ldy;
+    wide_tile<QT, MODE, MI, true, KS>(p, sm, tile_x * 128, 0);
+  } else {
+    // the column tile picks the segment (gate / up, or the down projection)
     int sg = 0;
 #pragma unroll
     for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
@@ -805,40 +795,64 @@ __global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
     p.w = pk.seg.w[sg] + (int64_t)e * pk.estride;
     p.n = pk.seg.n[sg];
     p.ldy = pk.seg.ldy[sg];
-    p.t = (int)te[2];  // the tile's rows
-    p.list = pk.list + base;  // the tile's pairs
-    if (pk.gather) {          // gate / up: X rows are the pairs' tokens, y the compact rows
+    if constexpr (MODE == kGrouped) {  // gate / up: X rows are the pairs' tokens, y the compact rows
       p.y = pk.seg.y[sg] + (int64_t)base * pk.seg.ldy[sg];
-    } else {                  // down: A the compact rows, y the pairs' rows
+    } else {                           // down: A the compact rows, y the pairs' rows
       p.x = (const _Float16*)pk.x + (int64_t)base * pk.ldx;
       p.y = pk.seg.y[sg];
     }
-    m0 = 0;
+    // every column tile is whole: the launcher takes segments of whole tiles only
+    wide_tile<QT, MODE, MI, true, KS>(p, sm, tile_x * Cfg<QT, MI, KS>::BNW, 0);
   }
-  const int n0 = tile_x * Cfg<QT, MI, KS>::BNW;
-  if constexpr (MODE == kGroupedGU) {
-    // routed gate/up with SiLU: as kGrouped above, the column tile being 128
-    // features of h (gate and up rows of one expert)
-    const u32x4 te = *(const u32x4*)(pk.tiles + 4 * ti);
-    if (te[2] == 0) return;  // past the table's tiles
-    const int e = (int)te[0], base = (int)te[3];
-    p.w = pk.w + (int64_t)e * pk.estride;
-    p.w2 = pk.w2 + (int64_t)e * pk.estride;
-    p.t = (int)te[2];
-    p.list = pk.list + base;
-    p.y = pk.y + (int64_t)base * pk.ldy;
-    wide_tile<QT, MODE, MI, true, KS>(p, sm, tile_x * 128, 0);
-  } else if (n0 + Cfg<QT, MI, KS>::BNW <= p.n) {
-    wide_tile<QT, MODE, MI, true, KS>(p, sm, n0, m0);
+  return true;
+}
+
+// Grid: (column tiles, token tiles).  kMulti: projections over one X, each
+// a segment of whole column tiles (its own weights, rows and output).
+// Routed modes: gridDim.x workgroups (a multiple of 8) run linear tiles g,
+// g + gridDim.x, ... in turn (see routed_tile).  Workgroups go to the 8 XCDs
+// in turn (g % 8), and so does every tile of a workgroup: an XCD runs whole
+// table tiles, all their column tiles one after the other, and the tile's
+// activation rows are fetched into its L2 once rather than by every XCD.
+template <int QT, int MODE, int MI, int KS = 1>
+__global__ __launch_bounds__(NTW) void gemm_wide_kernel(GemmParams pk) {
+  __shared__ __attribute__((aligned(16))) Smem<QT, MI, KS> sm;
+  if constexpr (MODE == kGrouped || MODE == kGroupedGU || MODE == kGroupedDown) {
+    if constexpr (wide_persistent(QT, MODE)) {
+      const uint32_t total = (uint32_t)pk.tcols * (uint32_t)pk.t;
+      for (uint32_t b = blockIdx.x; b < total; b += gridDim.x)
+        if (routed_tile<QT, MODE, MI, KS>(pk, sm, b)) __syncthreads();  // the epilogue's LDS, before the next staging
+    } else {
+      routed_tile<QT, MODE, MI, KS>(pk, sm, blockIdx.x);
+    }
   } else {
-    wide_tile<QT, MODE, MI, false, KS>(p, sm, n0, m0);
+    GemmParams p = pk;
+    int tile_x = blockIdx.x;
+    if constexpr (MODE == kMulti) {
+      int sg = 0;
+#pragma unroll
+      for (int i = 1; i < kMaxSeg; ++i) sg += (i < pk.seg.nseg && tile_x >= pk.seg.tile0[i]);
+      tile_x -= pk.seg.tile0[sg];
+      p.w = pk.seg.w[sg];
+      p.n = pk.seg.n[sg];
+      p.k = pk.seg.k[sg];  // a K part: its weights start at seg.w, its activations xoff into each row
+      p.x = (const _Float16*)pk.x + pk.seg.xoff[sg];
+      p.y = pk.seg.y[sg];
+      p.ldy = pk.seg.ldy[sg];
+    }
+    const int m0 = blockIdx.y * Cfg<QT, MI>::BMW;
+    const int n0 = tile_x * Cfg<QT, MI, KS>::BNW;
+    if (n0 + Cfg<QT, MI, KS>::BNW <= p.n)
+      wide_tile<QT, MODE, MI, true, KS>(p, sm, n0, m0);
+    else
+      wide_tile<QT, MODE, MI, false, KS>(p, sm, n0, m0);
   }
 }
 
 bool wide_supported(int qtype, int mode) {
   if (mode == kGroupedGU) return qtype == kQ4_K || qtype == kQ5_K;
   return (qtype == kQ6_K || qtype == kQ2_K || qtype == kQ4_K || qtype == kQ5_K) &&
-         (mode == kPlainF16 || mode == kMulti || mode == kGrouped);
+         (mode == kPlainF16 || mode == kMulti || mode == kGrouped || mode == kGroupedDown);
 }
 
 int wide_cols() { return 32 * NW; }
@@ -846,12 +860,20 @@ int wide_cols() { return 32 * NW; }
 template <int QT, int MODE, int MI>
 static void launch_wide_t(const GemmParams& p, uint32_t col_tiles, hipStream_t s) {
   constexpr int BMW = 32 * MI;
-  if constexpr (MODE == kGrouped || MODE == kGroupedGU) {
+  if constexpr (MODE == kGrouped || MODE == kGroupedGU || MODE == kGroupedDown) {
     // p.t carries the size of the tile table (its largest possible length, a
     // multiple of 8)
+    // persistent types: one workgroup per CU (a multiple of 8), or fewer for
+    // a smaller table; the others one workgroup per tile
     GemmParams q = p;
     q.tcols = (int)col_tiles;
-    hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), dim3(col_tiles * (uint32_t)p.t), dim3(NTW), 0, s, q);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+      cus = 256;
+    const uint32_t total = col_tiles * (uint32_t)p.t;
+    const uint32_t g = wide_persistent(QT, MODE) ? std::min(total, (uint32_t)(cus / 8 * 8)) : total;
+    hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), dim3(g), dim3(NTW), 0, s, q);
   } else {
     const dim3 grid(col_tiles, (uint32_t)((p.t + BMW - 1) / BMW));
     hipLaunchKernelGGL((gemm_wide_kernel<QT, MODE, MI>), grid, dim3(NTW), 0, s, p);
@@ -861,7 +883,11 @@ static void launch_wide_t(const GemmParams& p, uint32_t col_tiles, hipStream_t s
 // Tiles of 32 * mi tokens x 256 features (mi = 8 or 4); kMulti: p.seg
 // holds the segments and col_tiles their total.
 hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hipStream_t s) {
-  if ((mode == kGrouped || mode == kGroupedGU) && p.t % 8 != 0) return hipErrorInvalidValue;  // table length
+  const bool routed = mode == kGrouped || mode == kGroupedGU || mode == kGroupedDown;
+  if (routed && p.t % 8 != 0) return hipErrorInvalidValue;  // table length
+  if (mode == kGrouped || mode == kGroupedDown)
+    for (int i = 0; i < p.seg.nseg; ++i)
+      if (p.seg.n[i] % 256 != 0) return hipErrorInvalidValue;  // routed tiles are whole column tiles
   if (mode == kGroupedGU) {
     // p.n: h columns (a multiple of 128), 128 per column tile
     if (mi != 8 || p.n % 128 != 0) return hipErrorInvalidValue;
@@ -871,12 +897,14 @@ hipError_t launch_gemm_wide(int qtype, int mode, int mi, const GemmParams& p, hi
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  if (mode != kPlainF16 && mode != kMulti && mode != kGrouped) return hipErrorInvalidValue;
-  if (mode == kGrouped && mi != 8) return hipErrorInvalidValue;
+  if (mode != kPlainF16 && mode != kMulti && mode != kGrouped && mode != kGroupedDown) return hipErrorInvalidValue;
+  if ((mode == kGrouped || mode == kGroupedDown) && mi != 8) return hipErrorInvalidValue;
   const uint32_t cols = mode != kPlainF16 ? (uint32_t)p.seg.tile0[p.seg.nseg] : (uint32_t)((p.n + 255) / 256);
 #define QP_WIDE_T(QT)                                                                              \
   if (mode == kGrouped) {                                                                          \
     launch_wide_t<QT, kGrouped, 8>(p, cols, s);                                                    \
+  } else if (mode == kGroupedDown) {                                                               \
+    launch_wide_t<QT, kGroupedDown, 8>(p, cols, s);                                                \
   } else if (mode == kMulti) {                                                                     \
     if (mi == 8) launch_wide_t<QT, kMulti, 8>(p, cols, s); else launch_wide_t<QT, kMulti, 4>(p, cols, s); \
   } else {                                                                                         \
