@@ -55,8 +55,9 @@ struct GemmParams {
   int hd;
   float eps;
   // routed experts
-  const int* tiles;      // [max_tiles][2]: expert, first row of its list (256-row kernel: [4], see moe_oscan_kernel)
-  const int* ntiles;
+  const int* tiles;      // 128-row kernel: [max_tiles][2] = expert, first row of its list; 256-row kernel:
+                         // [max_tiles2][4] = expert, first row, rows, first compact row (0 rows past the tiles)
+  const int* ntiles;     // 128-row kernel: tiles in the table
   const int* offsets;    // first compact row of each expert
   const int* counts;     // rows of each expert
   const int* list;       // compact row -> pair index (token * top_k + slot)
