@@ -121,7 +121,7 @@ __device__ __forceinline__ void store_tiles_vec(float16v (&v)[MI][JB], int m_row
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        asm volatile("" ::: "memory");  // one float4 in flight: the registers are nearly all taken
+        if ((q & 1) == 0) asm volatile("" ::: "memory");  // two float4 in flight: the registers are nearly all taken
         const int rr = 8 * q + l8, cg = ln & 7;
         const float4v x = *(const float4v*)(scr + rr * PITCH + 4 * cg);
         const int row = 32 * i + rr;
